@@ -1,0 +1,342 @@
+"""Plain, slow CPU oracle for the AWQ activation-aware INT4 scale search and packing.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module: only the
+tests, the smoke check and the CPU-baseline leg of the benchmark call it.  It shares no
+code, constants table or helper with the HIP library; the only thing the two sides share
+is the seeded input generator, which holds none of the method's arithmetic.
+
+Sources (cited by page title and section):
+
+* [EXPLAINER] "AWQ：为什么 4-bit 权重量化要先观察 Activation" (charlestar.github.io):
+  §1 (error measured through the input, the per-channel statistic a_j),
+  §2 (the symmetric [-7, 7] teaching quantizer), §3 (equivalent scaling XW = (XS^-1)(SW),
+  the worked two-channel examples and the 20-candidate search, the per-element error bound),
+  §4 (the candidate family s = a^alpha, alpha in {0, 0.05, ..., 0.95}, clamp 1e-4 before the
+  sqrt(max*min) normalisation, the per-candidate module-output MSE, first minimum wins),
+  §7 (the asymmetric group pseudo-quantizer actually used for the artefact: round w/Delta,
+  add z, clamp to [0, 15], reconstruct Delta(q - z); group size divides K; K-axis grouping
+  of a PyTorch [N, K] weight), §8 (g128 + fp16 scale + fp16 zero = 4.25 bits/weight).
+* [DREAMVFIA] "AWQ salient weight / GGUF compilation" report (dreamvfia.cn), §二: the
+  statistic (1/B) sum_b |X_bk| and the scale-equivalence algebra.
+* [MODULES] "5. 核心模块：校准器、压缩算法、格式封装与 kernel 后端" (ai-infra.cypggs.com), §5.3:
+  INT4 codes are usually packed eight per int32.
+
+Readings where the pages are silent (each is listed in the design doc):
+
+* The asymmetric formulas themselves were lost from the explainer's §7; the text gives the
+  order of operations and says a positive floor prevents division by zero.  This oracle uses
+  Delta = max(max - min, 1e-5) / 15, z = clamp(rne(-min / Delta), 0, 15),
+  q = clamp(rne(v / Delta) + z, 0, 15).  The 1e-5 floor is our choice.
+* Working precision of the quantizer: IEEE fp32, each operation rounded once (numpy float32
+  has no fused multiply-add), correctly rounded division, ties-to-even rounding.  The
+  scale table is computed in fp64 and rounded once to fp32.  The loss is fp64.
+* The loss of a candidate is the mean over the M x N outputs of (X E)^2 with
+  E = W - S^-1 Q(S W): the module-output MSE of §4 for a single linear layer.
+* Packing: qweight int32 [N, K/8], nibble i of word j holds the code of k = 8j + i (least
+  significant nibble first); scales fp16 [N, K/g] hold Delta (round-to-nearest-even);
+  zeros fp16 [N, K/g] hold the integer z.
+
+Every function here is pinned by tests (worked examples printed on the pages, closed forms,
+invariants, brute force on tiny inputs).  Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+from math import isfinite, sqrt
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+N_GRID = 20          # [EXPLAINER §4] twenty ratios 0, 0.05, ..., 0.95 (1 excluded)
+SCALE_FLOOR = 1e-4   # [EXPLAINER §4] clamp applied after the power, before normalising
+RANGE_FLOOR = np.float32(1e-5)  # positive floor on max - min (our reading of §7)
+QMAX = 15            # [EXPLAINER §7] unsigned 4-bit codes 0..15
+GROUP = 128          # [EXPLAINER §8], quant config group 128 (g128)
+
+
+# ---------------------------------------------------------------------------------------
+# Step 1: the activation statistic  [EXPLAINER §1], [DREAMVFIA §二]
+# ---------------------------------------------------------------------------------------
+def activation_stat(X: np.ndarray) -> np.ndarray:
+    """a_j = mean over the M calibration rows of |X[m, j]|, in float64.
+
+    X holds the exact input values (fp32 or bf16 values embed exactly in float64)."""
+    X = np.asarray(X, dtype=np.float64)
+    if X.ndim != 2 or X.shape[0] == 0:
+        raise ValueError("X must be a non-empty [M, K] matrix")
+    if not np.all(np.isfinite(X)):
+        raise ValueError("activations must be finite")
+    return np.abs(X).sum(axis=0) / X.shape[0]
+
+
+# ---------------------------------------------------------------------------------------
+# Step 2: the scale candidates  [EXPLAINER §3 listing and §4]
+# ---------------------------------------------------------------------------------------
+def alpha_grid(n_grid: int = N_GRID) -> List[float]:
+    """alpha_i = i / n_grid for i = 0 .. n_grid-1 (the value 1 itself is not a candidate)."""
+    return [i / n_grid for i in range(n_grid)]
+
+
+def candidate_scales(a: Sequence[float], alpha: float) -> np.ndarray:
+    """s = r / sqrt(max(r) * min(r)) with r_j = max(a_j ** alpha, 1e-4), in float64.
+
+    The clamp comes before the normalisation, so a final s_j may be below 1e-4; at
+    alpha = 0 every r_j is 1 (0 ** 0 = 1) and s is all ones."""
+    a = np.asarray(a, dtype=np.float64)
+    if a.ndim != 1 or a.size == 0 or not np.all(np.isfinite(a)) or np.any(a < 0):
+        raise ValueError("the statistic must be a finite non-negative vector")
+    r = np.maximum(np.power(a, alpha), SCALE_FLOOR)
+    return r / sqrt(float(r.max()) * float(r.min()))
+
+
+def scale_table_f32(a32: np.ndarray, n_grid: int = N_GRID) -> Tuple[np.ndarray, np.ndarray]:
+    """The fp32 table used by the production contract: s[i] = fp32(candidate_scales(a, i/n))
+    and its reciprocal rs[i] = fp32(1 / s[i]) (both rounded once from float64)."""
+    a64 = np.asarray(a32, dtype=np.float32).astype(np.float64)
+    s = np.stack([candidate_scales(a64, al).astype(np.float32) for al in alpha_grid(n_grid)])
+    if not np.all(np.isfinite(s)) or np.any(s <= 0):
+        raise ValueError("a scale candidate is outside fp32 range")
+    rs = (1.0 / s.astype(np.float64)).astype(np.float32)
+    return s, rs
+
+
+def first_argmin(losses: Sequence[float]) -> int:
+    """Index of the first minimum (the earliest, i.e. smallest-alpha, candidate wins ties)."""
+    best = 0
+    for i, v in enumerate(losses):
+        if v < losses[best]:
+            best = i
+    return best
+
+
+# ---------------------------------------------------------------------------------------
+# Step 3: group-wise asymmetric INT4 pseudo-quantization  [EXPLAINER §7]
+# ---------------------------------------------------------------------------------------
+def asym_params(v: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per group (last axis) of fp32 values: Delta (fp32) and the integer zero point z."""
+    v = np.asarray(v, dtype=np.float32)
+    mx = v.max(axis=-1)
+    mn = v.min(axis=-1)
+    delta = np.maximum(mx - mn, RANGE_FLOOR) / np.float32(QMAX)
+    if not np.all(np.isfinite(delta)):
+        raise ValueError("group range outside fp32 range")
+    z = np.clip(np.rint(-mn / delta), 0, QMAX)
+    return delta.astype(np.float32), z.astype(np.int32)
+
+
+def asym_codes(v: np.ndarray, delta: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """q = clamp(rne(v / Delta) + z, 0, 15) with Delta, z broadcast over the group axis."""
+    v = np.asarray(v, dtype=np.float32)
+    t = v / delta[..., None]
+    q = np.clip(np.rint(t) + z[..., None].astype(np.float32), 0, QMAX)
+    return q.astype(np.uint8)
+
+
+def quantize(W32: np.ndarray, s32: np.ndarray, group: int = GROUP
+             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Quantize S W for a [N, K] weight whose rows are output channels.
+
+    v[n, k] = fp32(W[n, k] * s[k]); groups of ``group`` consecutive k per row n.
+    Returns codes uint8 [N, K], zero points int32 [N, K/g], steps fp32 [N, K/g]."""
+    W32 = np.asarray(W32, dtype=np.float32)
+    s32 = np.asarray(s32, dtype=np.float32)
+    N, K = W32.shape
+    if group <= 0 or K % group != 0:
+        raise ValueError("the group size must divide K")
+    if not np.all(np.isfinite(W32)):
+        raise ValueError("weights must be finite")
+    if s32.shape != (K,) or not np.all(np.isfinite(s32)) or np.any(s32 <= 0):
+        raise ValueError("scales must be finite and positive")
+    v = (W32 * s32[None, :]).reshape(N, K // group, group)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("scaled weight outside fp32 range")
+    delta, z = asym_params(v)
+    q = asym_codes(v, delta, z)
+    return q.reshape(N, K), z, delta
+
+
+def dequant_scaled(q: np.ndarray, z: np.ndarray, delta: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Reconstruction in the scaled domain, Delta (q - z), in float64 [N, K]."""
+    N, K = q.shape
+    qg = q.reshape(N, K // group, group).astype(np.float64)
+    out = delta.astype(np.float64)[..., None] * (qg - z.astype(np.float64)[..., None])
+    return out.reshape(N, K)
+
+
+def effective_weight(q, z, delta, s32, group: int = GROUP) -> np.ndarray:
+    """S^-1 Q(S W): the weight the candidate actually applies to the unchanged X (float64)."""
+    return dequant_scaled(q, z, delta, group) / np.asarray(s32, dtype=np.float64)[None, :]
+
+
+# ---------------------------------------------------------------------------------------
+# Step 4: candidate loss  [EXPLAINER §1, §3, §4]
+# ---------------------------------------------------------------------------------------
+def candidate_loss(X64: np.ndarray, W64: np.ndarray, What64: np.ndarray, chunk: int = 4096) -> float:
+    """mean over the M x N outputs of (X E^T)^2 with E = W - What, all in float64.
+
+    W and What are [N, K]; the output Y = X W^T is [M, N].  Chunked over N only to bound
+    memory; the sum of squares is accumulated in float64."""
+    M = X64.shape[0]
+    N = W64.shape[0]
+    sse = 0.0
+    for n0 in range(0, N, chunk):
+        E = W64[n0:n0 + chunk] - What64[n0:n0 + chunk]
+        Y = X64 @ E.T
+        sse += float(np.einsum("ij,ij->", Y, Y))
+    return sse / (M * N)
+
+
+def search(X: np.ndarray, W: np.ndarray, a32: np.ndarray, group: int = GROUP, n_grid: int = N_GRID,
+           chunk: int = 4096) -> Dict[str, object]:
+    """The full candidate search of [EXPLAINER §4] for one linear layer.
+
+    X: exact activations [M, K]; W: exact weights [N, K] (fp32-representable);
+    a32: the fp32 statistic fed to the scale table.  Every candidate is evaluated exactly
+    (fp64 loss) and the first minimum wins."""
+    X64 = np.asarray(X, dtype=np.float64)
+    W32 = np.asarray(W, dtype=np.float32)
+    if not np.array_equal(W32.astype(np.float64), np.asarray(W, dtype=np.float64)):
+        raise ValueError("weights must be fp32-representable")
+    if not np.all(np.isfinite(X64)):
+        raise ValueError("activations must be finite")
+    N, K = W32.shape
+    if X64.shape[1] != K:
+        raise ValueError("X and W disagree on K")
+    W64 = W32.astype(np.float64)
+    s_tab, rs_tab = scale_table_f32(a32, n_grid)
+    losses = np.zeros(n_grid, dtype=np.float64)
+    for i in range(n_grid):
+        sse = 0.0
+        for n0 in range(0, N, chunk):
+            q, z, d = quantize(W32[n0:n0 + chunk], s_tab[i], group)
+            What = effective_weight(q, z, d, s_tab[i], group)
+            E = W64[n0:n0 + chunk] - What
+            Y = X64 @ E.T
+            sse += float(np.einsum("ij,ij->", Y, Y))
+        losses[i] = sse / (X64.shape[0] * N)
+    best = first_argmin(list(losses))
+    return {"losses": losses, "best": best, "s_table": s_tab, "rs_table": rs_tab,
+            "s_best": s_tab[best].copy(), "alpha_best": alpha_grid(n_grid)[best]}
+
+
+def search_tiles(X: np.ndarray, W: np.ndarray, s32: np.ndarray, rows: Tuple[int, int],
+                 cols: Tuple[int, int], group: int = GROUP) -> float:
+    """Sum of squared output errors over the output block rows x cols for one candidate s
+    (a sampled piece of the loss, for checks at sizes where the full search is slow)."""
+    m0, m1 = rows
+    n0, n1 = cols
+    q, z, d = quantize(np.asarray(W, dtype=np.float32)[n0:n1], s32, group)
+    E = np.asarray(W, dtype=np.float64)[n0:n1] - effective_weight(q, z, d, s32, group)
+    Y = np.asarray(X, dtype=np.float64)[m0:m1] @ E.T
+    return float(np.einsum("ij,ij->", Y, Y))
+
+
+# ---------------------------------------------------------------------------------------
+# Step 5: packing the winning codes  [EXPLAINER §7, §8], [MODULES §5.3]
+# ---------------------------------------------------------------------------------------
+def pack_words(q: np.ndarray) -> np.ndarray:
+    """Eight 4-bit codes per int32: nibble i of word j <- code of k = 8j + i."""
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    if K % 8 != 0:
+        raise ValueError("K must be a multiple of 8")
+    if np.any(q > QMAX):
+        raise ValueError("codes must be 4-bit")
+    q8 = q.reshape(N, K // 8, 8)
+    word = np.zeros((N, K // 8), dtype=np.uint32)
+    for i in range(8):
+        word |= q8[:, :, i] << np.uint32(4 * i)
+    return word.view(np.int32)
+
+
+def unpack_words(words: np.ndarray) -> np.ndarray:
+    w = np.asarray(words, dtype=np.int32).view(np.uint32)
+    N, J = w.shape
+    out = np.zeros((N, J, 8), dtype=np.uint8)
+    for i in range(8):
+        out[:, :, i] = (w >> np.uint32(4 * i)) & np.uint32(0xF)
+    return out.reshape(N, J * 8)
+
+
+def pack(W: np.ndarray, s32: np.ndarray, group: int = GROUP) -> Dict[str, np.ndarray]:
+    """The artefact for one layer: qweight int32 [N, K/8], scales fp16 [N, K/g] (Delta,
+    round-to-nearest-even), zeros fp16 [N, K/g] (integer z), plus the codes themselves."""
+    q, z, d = quantize(W, s32, group)
+    scales = d.astype(np.float16)
+    if not np.all(np.isfinite(scales)):
+        raise ValueError("a group step overflows fp16")
+    return {"qweight": pack_words(q), "scales": scales, "zeros": z.astype(np.float16),
+            "codes": q, "z": z, "delta": d}
+
+
+def artefact_bits_per_weight(N: int, K: int, group: int = GROUP) -> float:
+    """Storage of the artefact per weight: 4-bit codes + one fp16 scale and one fp16 zero per
+    group ([EXPLAINER §8]; padding and unquantized modules are not counted)."""
+    payload_bits = N * K * 4 + (N * K // group) * (16 + 16)
+    return payload_bits / (N * K)
+
+
+# ---------------------------------------------------------------------------------------
+# Teaching mode: the symmetric [-7, 7] quantizer and scaled forward  [EXPLAINER §2, §3]
+# ---------------------------------------------------------------------------------------
+def teaching_qdq(values: Sequence[float]) -> Tuple[List[int], List[float], float]:
+    """Symmetric absmax quantizer of [EXPLAINER §2]: one step Delta = max|v| / 7 per group,
+    integer codes in [-7, 7] by nearest rounding with ties to even; an all-zero group uses
+    Delta = 1.  Only finite values are accepted."""
+    vals = [float(v) for v in values]
+    if not vals or any(not isfinite(v) for v in vals):
+        raise ValueError("a group needs finite values")
+    peak = max(abs(v) for v in vals)
+    step = 1.0 if peak == 0 else peak / 7.0
+    if not (isfinite(step) and step > 0):
+        raise ValueError("step outside the float range")
+    codes = []
+    for v in vals:
+        c = round(v / step)  # Python round: nearest, ties to even
+        codes.append(int(min(7, max(-7, c))))
+    restored = [step * c for c in codes]
+    if any(not isfinite(r) for r in restored):
+        raise ValueError("reconstruction is not finite")
+    return codes, restored, step
+
+
+def teaching_forward(x: Sequence[float], w: Sequence[float], scales: Sequence[float]
+                     ) -> Tuple[float, List[int], float]:
+    """One output of the scaled layer of [EXPLAINER §3]: y = sum_j (x_j / s_j) * Q(w_j s_j),
+    with all channels in one teaching group.  Rejects mismatched lengths, non-finite input,
+    non-positive scales and any transform or product that leaves the float range."""
+    if not (len(x) == len(w) == len(scales)) or len(x) == 0:
+        raise ValueError("x, w and scales need the same non-zero length")
+    if any(not isfinite(v) for v in list(x) + list(w)):
+        raise ValueError("inputs must be finite")
+    if any(not (isfinite(s) and s > 0) for s in scales):
+        raise ValueError("scales must be finite and positive")
+    xs = [xi / si for xi, si in zip(x, scales)]
+    ws = [wi * si for wi, si in zip(w, scales)]
+    for orig, new in ((x, xs), (w, ws)):
+        for o, n in zip(orig, new):
+            if not isfinite(n) or (o != 0 and n == 0):
+                raise ValueError("scaling left the float range")
+    codes, restored, step = teaching_qdq(ws)
+    terms = [a * b for a, b in zip(xs, restored)]
+    for a, b, t in zip(xs, restored, terms):
+        if not isfinite(t) or (a != 0 and b != 0 and t == 0):
+            raise ValueError("product left the float range")
+    y = sum(terms)
+    if not isfinite(y):
+        raise ValueError("output is not finite")
+    return y, codes, step
+
+
+def teaching_search(x: Sequence[float], w: Sequence[float], n_grid: int = N_GRID
+                    ) -> Tuple[List[Tuple[float, float, float]], int]:
+    """The candidate search of [EXPLAINER §3/§4] on one token with the teaching quantizer:
+    a = |x| (one calibration row), scales from ``candidate_scales``, loss (y - x.w)^2.
+    Returns the history [(loss, alpha, y)] and the index of the first minimum."""
+    target = sum(xi * wi for xi, wi in zip(x, w))
+    a = [abs(v) for v in x]
+    history = []
+    for alpha in alpha_grid(n_grid):
+        s = [float(v) for v in candidate_scales(a, alpha)]
+        y, _, _ = teaching_forward(x, w, s)
+        history.append(((y - target) ** 2, alpha, y))
+    return history, first_argmin([h[0] for h in history])
