@@ -1,0 +1,165 @@
+"""Benchmark of the AWQ hot path on one MI355X.
+
+One step = the whole path on one synthetic layer resident in HBM: activation statistic ->
+20-candidate scale search (scale table, group ranges, fused quantize + error GEMM + squared
+error, reduction and argmin) -> exact quantization and packing at the winning scales.
+
+Default workload: the attention-projection-shaped layer, X bf16 [4096 x 4096], W bf16
+[4096 x 4096] (N x K), group 128, 20 candidates.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config attn] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AWQ α-search layers/sec + effective TFLOP/s (% MFMA peak), K=N=4096, M=4096"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (AMD spec, 2.5 PF class)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def cpu_baseline(config: str, n_sample: int):
+    """The oracle as it stands, on a bounded column sample of the same layer (all M tokens,
+    all K channels, the first n_sample output channels), scaled to layer-searches/s."""
+    import numpy as np
+    from oracle import awq_oracle as o
+    from post_weight_quantization_mean_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    spec = synth.CONFIGS[config].layers[0]
+    cfg_id = synth.CONFIGS[config].cfg_id
+    X = synth.make_x(spec, 0, cfg_id, 0)
+    W = synth.make_w(spec, 0, cfg_id, 0, rows=n_sample)
+    X64, W32 = synth.to_f64(X), synth.to_f32(W)
+    t0 = time.perf_counter()
+    a32 = o.activation_stat(X64).astype(np.float32)
+    res = o.search(X64, W32, a32)
+    o.pack(W32, res["s_best"])
+    dt = time.perf_counter() - t0
+    frac = n_sample / spec.N
+    return {"value": frac / dt, "unit": "layer-searches/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{config} layer, all {spec.M} tokens and {spec.K} channels, first {n_sample} of "
+                      f"{spec.N} output channels (statistic over the full X); {dt:.2f} s measured, "
+                      f"scaled by N/{n_sample}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="attn")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path would shard along N with one 160-byte loss all-reduce)"}))
+        sys.exit(2)
+
+    import torch
+    from post_weight_quantization_mean_amd import awq, synth
+    if not os.path.exists(awq._LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    dev = torch.device("cuda:0")
+    spec, X, W = synth.make_layer(args.config)
+    M, K, N = spec.M, spec.K, spec.N
+    Xd, Wd = X.to(dev), W.to(dev)
+    del X, W
+    a = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_stats = torch.empty(awq.stats_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    ws_search = torch.empty(awq.search_workspace_bytes(M, K, N), dtype=torch.uint8, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    scales = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+    zeros = torch.empty_like(scales)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        awq.stats(Xd, out=a, workspace=ws_stats, flags=flags, check=False)
+        if ev:
+            ev[1].record()
+        res = awq.search(Xd, Wd, a, workspace=ws_search, flags=flags, check=False)
+        if ev:
+            ev[2].record()
+        awq.pack(Wd, res.s_best, flags=flags, out=(qweight, scales, zeros), check=False)
+        if ev:
+            ev[3].record()
+        return res
+
+    for _ in range(args.warmup):
+        res = step()
+    torch.cuda.synchronize()
+    awq.raise_for_flags(flags)
+
+    # All events are created up front and read after the loop: no host sync inside the
+    # timed region, every launch queued back to back on the one stream.
+    evs = [events() for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        res = step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    awq.raise_for_flags(flags)
+    per_step = [(e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])) for e in evs]
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    st_ms = statistics.mean(p[0] for p in per_step)
+    se_ms = statistics.mean(p[1] for p in per_step)
+    pk_ms = statistics.mean(p[2] for p in per_step)
+    flops = 20 * 2.0 * M * K * N
+    achieved = flops / (se_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms_per_step,
+        "unit": "layer-searches/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config}: X bf16 [{M} x {K}], W bf16 [{N} x {K}], group 128, "
+                               f"20 candidates, stats + search + pack", "M": M, "K": K, "N": N,
+                   "group": 128, "n_grid": 20},
+        "effective_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "pct_mfma_peak": 100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stage_ms": {"stats": st_ms, "search": se_ms, "pack": pk_ms},
+        "stats_gbs": 2.0 * M * K / (st_ms * 1e-3) / 1e9,
+        "pack_gbs": 2.53125 * K * N / (pk_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "awq_search (scale table + group ranges + fused quantize/MFMA/SSE + select)",
+                     "work_per_launch": f"20 x 2*M*K*N = {flops:.4g} flop"},
+        "best_alpha": res.best_index / 20.0,
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+/*
+ * awq.h -- C ABI of libawq: AWQ activation-aware INT4 weight quantization, the
+ * data-parallel hot path (statistic, 20-candidate scale search, pack) on one MI355X.
+ *
+ * Sources (cited by page title and section):
+ *   [EXPLAINER] "AWQ：为什么 4-bit 权重量化要先观察 Activation" (charlestar.github.io)
+ *   [DREAMVFIA] "AWQ salient weight / GGUF compilation" report (dreamvfia.cn)
+ *   [MODULES]   "5. 核心模块：校准器、压缩算法、格式封装与 kernel 后端" (ai-infra.cypggs.com)
+ *
+ * Conventions shared by every entry point
+ *   - Orientation: X is [M, K] (M calibration tokens, K input channels), row-major with
+ *     row stride ldx elements (ldx >= K).  W is a PyTorch Linear weight [N, K] (N output
+ *     channels), row-major with row stride ldw (ldw >= K).  Groups of `group` consecutive k
+ *     along a row of W are quantized together ([EXPLAINER §7]: the source groups along the
+ *     last, input, dimension of the [N, K] tensor).
+ *   - Every pointer argument is DEVICE memory owned by the caller; buffers must stay alive
+ *     until the work queued on `stream` has finished.  The library allocates no device
+ *     memory, keeps no mutable global state and is reentrant; every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL is the default stream).
+ *   - Argument errors are returned synchronously as an awq_status before anything is
+ *     queued; no kernel is launched in that case.
+ *   - Data errors can only be seen on the device: kernels OR AWQ_FLAG_* bits into *flags.
+ *     The caller clears *flags before the call.  When a bit is set after the stream work
+ *     finished, the outputs of that call are undefined.
+ *   - Fixed quantization contract ([EXPLAINER §7]; quant config zero_point = True,
+ *     w_bit = 4, q_group_size = 128 in [DREAMVFIA §四]): asymmetric 4-bit codes 0..15,
+ *     group = 128 along K.  K must be a multiple of 128.
+ */
+#ifndef AWQ_H
+#define AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AWQ_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define AWQ_API __attribute__((visibility("default")))
+#else
+#define AWQ_API
+#endif
+
+/* Status codes returned synchronously. */
+typedef enum {
+  AWQ_OK = 0,
+  AWQ_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, ld < K, n_grid outside [1, 64] */
+  AWQ_ERR_SHAPE = 2,       /* K not a multiple of the group size, 64-bit size overflow */
+  AWQ_ERR_UNSUPPORTED = 3, /* dtype other than F32/BF16, group other than 128 */
+  AWQ_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than the size function says */
+  AWQ_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+} awq_status;
+
+/* Element types of X and W. */
+typedef enum { AWQ_DTYPE_F32 = 0, AWQ_DTYPE_BF16 = 1 } awq_dtype;
+
+/* Data-error bits OR-ed into *flags by the kernels. */
+#define AWQ_FLAG_NONFINITE_X 0x1u    /* awq_stats: X holds NaN or Inf */
+#define AWQ_FLAG_NONFINITE_W 0x2u    /* awq_pack: W holds NaN or Inf, or W*s overflows fp32 */
+#define AWQ_FLAG_SCALE_RANGE 0x4u    /* a scale candidate is not finite and positive in fp32,
+                                        or the statistic a is negative or not finite */
+#define AWQ_FLAG_F16_RANGE 0x8u      /* awq_pack: a group step does not fit fp16 */
+#define AWQ_FLAG_NONFINITE_LOSS 0x10u /* awq_search: a candidate loss is not finite (NaN/Inf
+                                         in X or W reach every loss through the product) */
+
+typedef struct ihipStream_t* awq_stream_t; /* the same type as hipStream_t */
+
+/* ABI version of the loaded library (AWQ_ABI_VERSION). */
+AWQ_API int awq_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+AWQ_API const char* awq_status_string(int status);
+
+/* ---------------------------------------------------------------------------------------
+ * Step 1: activation statistic  ([EXPLAINER §1]; [DREAMVFIA §二] writes it (1/B) sum |X|)
+ *   a[j] = (1/M) * sum_m |X[m, j]|  for j < K
+ * Arithmetic: every term is accumulated in fp64 (exact for bf16 inputs in practice), a
+ * fixed-order reduction, one rounding to fp32 at the end; bitwise reproducible.
+ *   X       [M, K] of x_dtype, row stride ldx
+ *   a_out   fp32 [K]
+ *   ws      workspace of at least awq_stats_workspace_bytes(M, K) bytes (device)
+ *   flags   device uint32; AWQ_FLAG_NONFINITE_X if X holds NaN/Inf
+ * ------------------------------------------------------------------------------------- */
+AWQ_API size_t awq_stats_workspace_bytes(int64_t M, int64_t K);
+AWQ_API int awq_stats(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                      float* a_out, void* ws, size_t ws_bytes, uint32_t* flags,
+                      awq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Steps 2-4 and the argmin of step 5: the candidate scale search ([EXPLAINER §3, §4]).
+ *   For i < n_grid, alpha_i = i / n_grid (n_grid = 20 gives 0, 0.05, ..., 0.95):
+ *     r_j = max(a_j ^ alpha_i, 1e-4)          (fp64; 0^0 = 1)
+ *     s_j = fp32(r_j / sqrt(max_k r_k * min_k r_k)),  rs_j = fp32(1 / s_j)
+ *   For every group g of 128 k in row n of W:  v = W[n,k] * s_k (fp32),
+ *     Delta = max(max v - min v, 1e-5) / 15,  z = clamp(rne(-min v / Delta), 0, 15),
+ *     q = clamp(rne(v / Delta) + z, 0, 15),   E[n,k] = W[n,k] - Delta (q - z) / s_k
+ *   loss_i = sum_{m,n} (X E^T)[m,n]^2 / (M N)      ([EXPLAINER §4]: module-output MSE)
+ *   best = first index attaining min loss           (earliest candidate wins ties)
+ * The quantized weights never leave the chip: each tile is quantized in registers and fed
+ * to a bf16 matrix-core product whose squared output error is reduced in the same kernel.
+ * Inside the search the code uses v * (1/Delta); awq_pack always divides exactly.
+ *   X, W           as above (both F32 or BF16; F32 X is split into two bf16 terms)
+ *   a              fp32 [K]: the statistic (normally awq_stats' output)
+ *   group, n_grid  128 and 1..64 (20 in the method)
+ *   losses_out     fp64 [n_grid];  best_out int32 [1];  s_best_out fp32 [K] = s of the winner
+ *   s_table_out    fp32 [n_grid, K] or NULL: the whole scale table
+ *   ws             workspace of at least awq_search_workspace_bytes(...) bytes (device)
+ *   flags          AWQ_FLAG_SCALE_RANGE, AWQ_FLAG_NONFINITE_LOSS
+ * ------------------------------------------------------------------------------------- */
+AWQ_API size_t awq_search_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
+                                          int32_t n_grid);
+AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                       const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                       int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
+                       float* s_best_out, float* s_table_out, void* ws, size_t ws_bytes,
+                       uint32_t* flags, awq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Step 5: real quantization and packing of S W ([EXPLAINER §7, §8]; [MODULES §5.3]:
+ * INT4 codes eight per int32).  Exact fp32 contract: v = W*s, Delta = max(max-min,1e-5)/15
+ * and q use correctly rounded division and ties-to-even rounding, bit-identical to the
+ * definition above.
+ *   qweight  int32 [N, K/8]: nibble i (bits 4i..4i+3) of word j holds the code of k = 8j+i
+ *   scales   fp16 [N, K/128] (uint16 storage): Delta rounded to nearest even
+ *   zeros    fp16 [N, K/128] (uint16 storage): the integer zero point z (never -0)
+ * The dequantized weight is scales * (q - zeros) / s[k]; the caller folds 1/s into the
+ * producer of X ([EXPLAINER §6]).  4.25 bits per weight ([EXPLAINER §8]).
+ *   flags    AWQ_FLAG_NONFINITE_W, AWQ_FLAG_SCALE_RANGE, AWQ_FLAG_F16_RANGE
+ * ------------------------------------------------------------------------------------- */
+AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                     const float* s, int32_t group, int32_t* qweight, uint16_t* scales,
+                     uint16_t* zeros, uint32_t* flags, awq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_H */

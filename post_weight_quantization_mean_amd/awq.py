@@ -1,0 +1,200 @@
+"""Python binding of libawq (argument marshalling only; every step runs in the HIP kernels).
+
+Tensors are torch tensors on a ROCm device; the calls are queued on the device's current
+torch stream.  Shapes follow PyTorch: X is [M, K] activations, W is a Linear weight [N, K].
+Data errors that only the device can see come back as flag bits; with ``check=True`` (the
+default) the call synchronises and raises ``ValueError`` for them, like the explainer page's
+reference code rejects non-finite input ("AWQ：为什么 4-bit 权重量化要先观察 Activation", §3).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libawq.so")
+
+AWQ_DTYPE_F32 = 0
+AWQ_DTYPE_BF16 = 1
+FLAG_NONFINITE_X = 0x1
+FLAG_NONFINITE_W = 0x2
+FLAG_SCALE_RANGE = 0x4
+FLAG_F16_RANGE = 0x8
+FLAG_NONFINITE_LOSS = 0x10
+_FLAG_TEXT = {
+    FLAG_NONFINITE_X: "activations must be finite",
+    FLAG_NONFINITE_W: "weights (and weights times scales) must be finite",
+    FLAG_SCALE_RANGE: "scale candidates must be finite and positive",
+    FLAG_F16_RANGE: "a group step does not fit fp16",
+    FLAG_NONFINITE_LOSS: "a candidate loss is not finite (non-finite X or W)",
+}
+GROUP = 128
+N_GRID = 20
+
+_lib = None
+
+
+class AwqError(RuntimeError):
+    """A status other than AWQ_OK returned by the library."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_lib.awq_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libawq.so (raises if it has not been built: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing; build it with "
+                              "`python -m post_weight_quantization_mean_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.awq_abi_version.restype = ctypes.c_int
+        L.awq_status_string.restype = ctypes.c_char_p
+        L.awq_status_string.argtypes = [ctypes.c_int]
+        L.awq_stats_workspace_bytes.restype = sz
+        L.awq_stats_workspace_bytes.argtypes = [i64, i64]
+        L.awq_stats.restype = ctypes.c_int
+        L.awq_stats.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, sz, vp, vp]
+        L.awq_search_workspace_bytes.restype = sz
+        L.awq_search_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+        L.awq_search.restype = ctypes.c_int
+        L.awq_search.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, i64, i64, vp,
+                                 i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.awq_pack.restype = ctypes.c_int
+        L.awq_pack.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, vp, vp, vp]
+        if L.awq_abi_version() != 1:
+            raise ImportError("libawq ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return AWQ_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return AWQ_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _matrix(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along K")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise AwqError(status, what)
+
+
+def raise_for_flags(flags: torch.Tensor) -> None:
+    """Synchronise on ``flags`` and raise ValueError naming every data error it carries."""
+    f = int(flags.item())
+    if f:
+        msgs = [txt for bit, txt in _FLAG_TEXT.items() if f & bit]
+        raise ValueError("; ".join(msgs) + f" (flags 0x{f:x})")
+
+
+def stats_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().awq_stats_workspace_bytes(M, K))
+
+
+def search_workspace_bytes(M: int, K: int, N: int, group: int = GROUP, n_grid: int = N_GRID) -> int:
+    return int(lib().awq_search_workspace_bytes(M, K, N, group, n_grid))
+
+
+def stats(X: torch.Tensor, *, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+          flags: Optional[torch.Tensor] = None, check: bool = True) -> torch.Tensor:
+    """a[j] = mean_m |X[m, j]| as fp32 [K]."""
+    M, K, ldx = _matrix(X, "X")
+    dev = X.device
+    a = out if out is not None else torch.empty(K, dtype=torch.float32, device=dev)
+    need = stats_workspace_bytes(M, K)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    st = lib().awq_stats(X.data_ptr(), _dtype_code(X), M, K, ldx, a.data_ptr(), ws.data_ptr(),
+                         ws.numel(), fl.data_ptr(), _stream(dev))
+    _check(st, "awq_stats")
+    if check:
+        raise_for_flags(fl)
+    return a
+
+
+@dataclasses.dataclass
+class SearchResult:
+    losses: torch.Tensor       # fp64 [n_grid] (device)
+    best: torch.Tensor         # int32 [1] (device)
+    s_best: torch.Tensor       # fp32 [K] (device)
+    s_table: Optional[torch.Tensor]  # fp32 [n_grid, K] (device) when requested
+    flags: torch.Tensor        # int32 [1] (device)
+
+    @property
+    def best_index(self) -> int:
+        return int(self.best.item())
+
+
+def search(X: torch.Tensor, W: torch.Tensor, a: torch.Tensor, group_size: int = GROUP, n_grid: int = N_GRID,
+           *, return_table: bool = False, workspace: Optional[torch.Tensor] = None,
+           flags: Optional[torch.Tensor] = None, check: bool = True) -> SearchResult:
+    """The candidate scale search over alpha = i / n_grid for one layer (or several
+    projections sharing one input, concatenated along N)."""
+    M, K, ldx = _matrix(X, "X")
+    N, Kw, ldw = _matrix(W, "W")
+    if Kw != K:
+        raise ValueError("X and W disagree on K")
+    if a.shape != (K,) or a.dtype != torch.float32 or not a.is_cuda or not a.is_contiguous():
+        raise ValueError("a must be a contiguous fp32 device vector of length K")
+    dev = X.device
+    losses = torch.empty(n_grid, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    s_table = torch.empty((n_grid, K), dtype=torch.float32, device=dev) if return_table else None
+    need = search_workspace_bytes(M, K, N, group_size, n_grid)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    st = lib().awq_search(X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
+                          a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(),
+                          s_best.data_ptr(), s_table.data_ptr() if s_table is not None else None,
+                          ws.data_ptr(), ws.numel(), fl.data_ptr(), _stream(dev))
+    _check(st, "awq_search")
+    if check:
+        raise_for_flags(fl)
+    return SearchResult(losses, best, s_best, s_table, fl)
+
+
+def pack(W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, *, flags: Optional[torch.Tensor] = None,
+         out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+         check: bool = True) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Quantize S W exactly and pack: qweight int32 [N, K/8], scales fp16 [N, K/128] (Delta),
+    zeros fp16 [N, K/128] (integer zero points)."""
+    N, K, ldw = _matrix(W, "W")
+    if s.shape != (K,) or s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous():
+        raise ValueError("s must be a contiguous fp32 device vector of length K")
+    dev = W.device
+    if out is None:
+        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+        scales = torch.empty((N, K // group_size if group_size > 0 else 0), dtype=torch.float16, device=dev)
+        zeros = torch.empty_like(scales)
+    else:
+        qweight, scales, zeros = out
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    st = lib().awq_pack(W.data_ptr(), _dtype_code(W), N, K, ldw, s.data_ptr(), group_size, qweight.data_ptr(),
+                        scales.data_ptr(), zeros.data_ptr(), fl.data_ptr(), _stream(dev))
+    _check(st, "awq_pack")
+    if check:
+        raise_for_flags(fl)
+    return qweight, scales, zeros

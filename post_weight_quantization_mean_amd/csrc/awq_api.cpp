@@ -1,0 +1,177 @@
+// Host side of libawq: argument validation, workspace carving and kernel launches behind the
+// C ABI declared in include/awq.h.  Validation is plain host code that runs before any HIP
+// call, so every argument error is reported without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "awq.h"
+#include "awq_internal.h"
+
+namespace {
+
+using awq::kGroup;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int t) { return t == AWQ_DTYPE_F32 || t == AWQ_DTYPE_BF16; }
+int64_t dsize(int t) { return t == AWQ_DTYPE_F32 ? 4 : 2; }
+
+// a * b without overflow (both non-negative), else -1
+int64_t mul_ok(int64_t a, int64_t b) {
+  if (a < 0 || b < 0) return -1;
+  if (a != 0 && b > INT64_MAX / a) return -1;
+  return a * b;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common checks of one [rows, K] operand with row stride ld.
+int check_matrix(const void* p, int dtype, int64_t rows, int64_t K, int64_t ld) {
+  if (p == nullptr) return AWQ_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return AWQ_ERR_UNSUPPORTED;
+  if (rows <= 0 || K <= 0 || ld < K) return AWQ_ERR_INVALID_ARG;
+  if (K % kGroup != 0) return AWQ_ERR_SHAPE;
+  const int64_t bytes = mul_ok(mul_ok(rows, ld), dsize(dtype));
+  if (bytes < 0) return AWQ_ERR_SHAPE;
+  // 16-byte vector loads: the base and every row start must be 16-byte aligned
+  if (!aligned16(p) || (ld * dsize(dtype)) % 16 != 0) return AWQ_ERR_INVALID_ARG;
+  return AWQ_OK;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+struct SearchLayout {
+  size_t s_tab, rs_tab, params, partial, total;
+};
+
+bool search_layout(int64_t M, int64_t K, int64_t N, int n_grid, SearchLayout* out) {
+  const awq::SearchPlan plan = awq::search_plan(M, K, N, n_grid);
+  const int64_t tab = mul_ok(mul_ok(n_grid, K), 4);
+  const int64_t par = mul_ok(mul_ok(mul_ok(n_grid, N), K / kGroup), 8);
+  const int64_t part = mul_ok(mul_ok(n_grid, plan.tiles), 8);
+  if (tab < 0 || par < 0 || part < 0) return false;
+  SearchLayout L;
+  L.s_tab = 0;
+  L.rs_tab = L.s_tab + align_up((size_t)tab);
+  L.params = L.rs_tab + align_up((size_t)tab);
+  L.partial = L.params + align_up((size_t)par);
+  L.total = L.partial + align_up((size_t)part);
+  *out = L;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+AWQ_API int awq_abi_version(void) { return AWQ_ABI_VERSION; }
+
+AWQ_API const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_OK: return "ok";
+    case AWQ_ERR_INVALID_ARG: return "invalid argument (null pointer, size, stride or alignment)";
+    case AWQ_ERR_SHAPE: return "shape error (K not a multiple of the group size, or size overflow)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported dtype or group size";
+    case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case AWQ_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+AWQ_API size_t awq_stats_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  const awq::StatsPlan p = awq::stats_plan(M, K, false);
+  const awq::StatsPlan q = awq::stats_plan(M, K, true);
+  const int64_t splits = p.splits > q.splits ? p.splits : q.splits;
+  const int64_t bytes = mul_ok(mul_ok(splits, K), 8);
+  return bytes < 0 ? 0 : align_up((size_t)bytes);
+}
+
+AWQ_API int awq_stats(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, float* a_out,
+                      void* ws, size_t ws_bytes, uint32_t* flags, awq_stream_t stream) {
+  int st = check_matrix(X, x_dtype, M, K, ldx);
+  if (st != AWQ_OK) return st;
+  if (a_out == nullptr || flags == nullptr) return AWQ_ERR_INVALID_ARG;
+  const size_t need = awq_stats_workspace_bytes(M, K);
+  if (need == 0) return AWQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < need) return AWQ_ERR_WORKSPACE;
+  const bool f32 = x_dtype == AWQ_DTYPE_F32;
+  const awq::StatsPlan plan = awq::stats_plan(M, K, f32);
+  return map_hip(awq::launch_stats(X, f32, M, K, ldx, a_out, static_cast<double*>(ws), plan, flags,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+AWQ_API size_t awq_search_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
+                                          int32_t n_grid) {
+  if (M <= 0 || K <= 0 || N <= 0 || group != kGroup || K % kGroup != 0 || n_grid < 1 || n_grid > 64)
+    return 0;
+  SearchLayout L;
+  if (!search_layout(M, K, N, n_grid, &L)) return 0;
+  return L.total;
+}
+
+AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                       const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                       int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
+                       float* s_best_out, float* s_table_out, void* ws, size_t ws_bytes,
+                       uint32_t* flags, awq_stream_t stream) {
+  int st = check_matrix(X, x_dtype, M, K, ldx);
+  if (st != AWQ_OK) return st;
+  st = check_matrix(W, w_dtype, N, K, ldw);
+  if (st != AWQ_OK) return st;
+  if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
+  if (n_grid < 1 || n_grid > 64) return AWQ_ERR_INVALID_ARG;
+  if (a == nullptr || losses_out == nullptr || best_out == nullptr || s_best_out == nullptr ||
+      flags == nullptr)
+    return AWQ_ERR_INVALID_ARG;
+  // Block-relative buffer offsets are 32-bit: 512 rows of X and 128 rows of W must span
+  // less than 2^31 bytes.
+  if (mul_ok(mul_ok(awq::kSearchBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX ||
+      mul_ok(mul_ok(awq::kSearchBN, ldw), dsize(w_dtype)) >= (int64_t)INT32_MAX)
+    return AWQ_ERR_SHAPE;
+  SearchLayout L;
+  if (!search_layout(M, K, N, n_grid, &L)) return AWQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < L.total) return AWQ_ERR_WORKSPACE;
+  if (!aligned16(ws) || !aligned16(a)) return AWQ_ERR_INVALID_ARG;
+  if (s_table_out != nullptr && !aligned16(s_table_out)) return AWQ_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(ws);
+  float* s_tab = s_table_out != nullptr ? s_table_out : reinterpret_cast<float*>(base + L.s_tab);
+  float* rs_tab = reinterpret_cast<float*>(base + L.rs_tab);
+  float2* params = reinterpret_cast<float2*>(base + L.params);
+  double* partial = reinterpret_cast<double*>(base + L.partial);
+  const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const awq::SearchPlan plan = awq::search_plan(M, K, N, n_grid);
+
+  hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, flags, s);
+  if (e == hipSuccess)
+    e = awq::launch_group_range(W, wf32, N, K, ldw, s_tab, n_grid, params, flags, s);
+  if (e == hipSuccess)
+    e = awq::launch_search_fused(X, xf32, M, ldx, W, wf32, N, K, ldw, s_tab, rs_tab, params,
+                                 n_grid, plan, partial, s);
+  if (e == hipSuccess)
+    e = awq::launch_select(partial, plan.tiles, n_grid, M, N, K, s_tab, losses_out, best_out,
+                           s_best_out, flags, s);
+  return map_hip(e);
+}
+
+AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                     const float* s, int32_t group, int32_t* qweight, uint16_t* scales,
+                     uint16_t* zeros, uint32_t* flags, awq_stream_t stream) {
+  int st = check_matrix(W, w_dtype, N, K, ldw);
+  if (st != AWQ_OK) return st;
+  if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
+  if (s == nullptr || qweight == nullptr || scales == nullptr || zeros == nullptr ||
+      flags == nullptr)
+    return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(s)) return AWQ_ERR_INVALID_ARG;
+  if (mul_ok(N, K) < 0) return AWQ_ERR_SHAPE;
+  return map_hip(awq::launch_pack(W, w_dtype == AWQ_DTYPE_F32, N, K, ldw, s, qweight, scales,
+                                  zeros, flags, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

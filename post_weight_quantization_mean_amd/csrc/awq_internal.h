@@ -1,0 +1,59 @@
+// Internal declarations shared by the HIP translation units of libawq (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+constexpr int kGroup = 128;  // quantization group along K
+constexpr int kQMax = 15;    // unsigned 4-bit codes 0..15
+
+// Flag bits, identical to the AWQ_FLAG_* values of the public header.
+constexpr uint32_t kFlagNonfiniteX = 0x1u;
+constexpr uint32_t kFlagNonfiniteW = 0x2u;
+constexpr uint32_t kFlagScaleRange = 0x4u;
+constexpr uint32_t kFlagF16Range = 0x8u;
+constexpr uint32_t kFlagNonfiniteLoss = 0x10u;
+
+// ---- statistic -------------------------------------------------------------------------
+struct StatsPlan {
+  int col_blocks;  // blocks across K
+  int splits;      // row splits (partials per column)
+  int64_t rows_per_split;
+};
+StatsPlan stats_plan(int64_t M, int64_t K, bool f32);
+hipError_t launch_stats(const void* X, bool f32, int64_t M, int64_t K, int64_t ldx, float* a_out,
+                        double* partial, const StatsPlan& plan, uint32_t* flags, hipStream_t st);
+
+// ---- search ----------------------------------------------------------------------------
+constexpr int kSearchBM = 512;  // tokens per block tile
+constexpr int kSearchBN = 128;  // output channels per block tile
+
+struct SearchPlan {
+  int64_t mt, nt;    // tiles along M and N
+  int64_t tiles;     // mt * nt
+  int64_t blocks;    // launched blocks (multiple of 8)
+  int64_t groups;    // K / 128
+};
+SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid);
+
+hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
+                              uint32_t* flags, hipStream_t st);
+hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
+                              const float* s_tab, int n_grid, float2* params, uint32_t* flags,
+                              hipStream_t st);
+hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const void* W,
+                               bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s_tab,
+                               const float* rs_tab, const float2* params, int n_grid,
+                               const SearchPlan& plan, double* partial, hipStream_t st);
+hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
+                         int64_t K, const float* s_tab, double* losses, int32_t* best,
+                         float* s_best, uint32_t* flags, hipStream_t st);
+
+// ---- pack ------------------------------------------------------------------------------
+hipError_t launch_pack(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s,
+                       int32_t* qweight, uint16_t* scales, uint16_t* zeros, uint32_t* flags,
+                       hipStream_t st);
+
+}  // namespace awq

@@ -1,0 +1,128 @@
+// Step 1 of the hot path: the per-input-channel activation statistic
+//   a_j = (1/M) sum_m |X[m, j]|
+// ("AWQ：为什么 4-bit 权重量化要先观察 Activation", §1: the mean absolute activation per input
+// channel; the dreamvfia.cn AWQ report, §二, writes it (1/B) sum_b |X_bk|).
+//
+// HBM-bound column reduction.  Each lane owns 16 bytes of a row (8 bf16 or 4 fp32 columns),
+// so a wave reads 1 KiB contiguous per row; 8 waves of a block stream interleaved rows of
+// one row split.  Every |x| is accumulated in fp64: for bf16/fp32 inputs of ordinary range
+// the column sums are then exact and independent of summation order.  Partials per
+// (split, column) go to the workspace and a second kernel sums them in a fixed order,
+// divides by M and rounds once to fp32.  A NaN/Inf input makes its column sum non-finite,
+// which the finalize kernel turns into AWQ_FLAG_NONFINITE_X.
+#include "awq_internal.h"
+
+namespace awq {
+namespace {
+
+constexpr int kStatsWaves = 8;
+constexpr int kStatsThreads = kStatsWaves * 64;
+
+template <bool F32>
+__global__ __launch_bounds__(kStatsThreads) void stats_partial_kernel(
+    const void* __restrict__ X, int64_t M, int64_t K, int64_t ldx, int64_t rows_per_split,
+    double* __restrict__ partial) {
+  constexpr int VEC = F32 ? 4 : 8;   // columns per lane (16 bytes)
+  constexpr int BCOLS = 64 * VEC;    // columns per block
+  __shared__ double red[kStatsWaves][BCOLS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * BCOLS + lane * VEC;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t r1 = (r0 + rows_per_split < M) ? r0 + rows_per_split : M;
+
+  double acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
+
+  if (col < K) {
+    if constexpr (F32) {
+      const float* base = static_cast<const float*>(X) + col;
+#pragma unroll 4
+      for (int64_t r = r0 + wave; r < r1; r += kStatsWaves) {
+        const float4 v = *reinterpret_cast<const float4*>(base + r * ldx);
+        acc[0] += fabs((double)v.x);
+        acc[1] += fabs((double)v.y);
+        acc[2] += fabs((double)v.z);
+        acc[3] += fabs((double)v.w);
+      }
+    } else {
+      const uint16_t* base = static_cast<const uint16_t*>(X) + col;
+#pragma unroll 4
+      for (int64_t r = r0 + wave; r < r1; r += kStatsWaves) {
+        const uint4 v = *reinterpret_cast<const uint4*>(base + r * ldx);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 word.
+          // Clearing the sign bit gives |x| directly.
+          const float lo = __uint_as_float((u[i] << 16) & 0x7fffffffu);
+          const float hi = __uint_as_float(u[i] & 0x7fff0000u);
+          acc[2 * i] += (double)lo;
+          acc[2 * i + 1] += (double)hi;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) red[wave][lane * VEC + i] = acc[i];
+  __syncthreads();
+  // Fixed-order combine of the 8 waves, then one store per column.
+  for (int c = threadIdx.x; c < BCOLS; c += kStatsThreads) {
+    const int64_t gc = (int64_t)blockIdx.x * BCOLS + c;
+    if (gc < K) {
+      double s = 0.0;
+#pragma unroll
+      for (int w = 0; w < kStatsWaves; ++w) s += red[w][c];
+      partial[(int64_t)blockIdx.y * K + gc] = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void stats_finalize_kernel(const double* __restrict__ partial,
+                                                            int splits, int64_t M, int64_t K,
+                                                            float* __restrict__ a_out,
+                                                            uint32_t* __restrict__ flags) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= K) return;
+  double s = 0.0;
+  for (int p = 0; p < splits; ++p) s += partial[(int64_t)p * K + j];
+  if (!isfinite(s)) atomicOr(flags, kFlagNonfiniteX);
+  a_out[j] = (float)(s / (double)M);
+}
+
+}  // namespace
+
+StatsPlan stats_plan(int64_t M, int64_t K, bool f32) {
+  const int vec = f32 ? 4 : 8;
+  StatsPlan p;
+  p.col_blocks = (int)((K + 64 * vec - 1) / (64 * vec));
+  // Aim for ~1024 blocks of 8 waves; keep at least 64 rows (8 per wave) in a split so the
+  // fp64 partials stay a few percent of the bytes read.
+  const int64_t want = (1024 + p.col_blocks - 1) / p.col_blocks;
+  const int64_t max_splits = (M + 63) / 64;
+  int64_t splits = want < max_splits ? want : max_splits;
+  if (splits < 1) splits = 1;
+  p.rows_per_split = (M + splits - 1) / splits;
+  p.splits = (int)((M + p.rows_per_split - 1) / p.rows_per_split);
+  return p;
+}
+
+hipError_t launch_stats(const void* X, bool f32, int64_t M, int64_t K, int64_t ldx, float* a_out,
+                        double* partial, const StatsPlan& plan, uint32_t* flags, hipStream_t st) {
+  dim3 grid(plan.col_blocks, plan.splits);
+  if (f32)
+    stats_partial_kernel<true><<<grid, kStatsThreads, 0, st>>>(X, M, K, ldx, plan.rows_per_split,
+                                                               partial);
+  else
+    stats_partial_kernel<false><<<grid, kStatsThreads, 0, st>>>(X, M, K, ldx, plan.rows_per_split,
+                                                                partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  stats_finalize_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(partial, plan.splits, M, K,
+                                                                     a_out, flags);
+  return hipGetLastError();
+}
+
+}  // namespace awq

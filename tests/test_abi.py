@@ -1,0 +1,115 @@
+"""CPU tests of the C-ABI boundary: the library loads without a GPU, exports every entry point
+the header declares, and reports every argument error synchronously, before any HIP call
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from post_weight_quantization_mean_amd import awq
+    if not os.path.exists(awq._LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return awq.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"AWQ_API\s+[\w\s\*]+?\b(awq_\w+)\s*\(", text)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
+                          "awq_search_workspace_bytes", "awq_search", "awq_pack"}
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+def test_version_and_status_strings(L):
+    assert L.awq_abi_version() == 1
+    for st in range(6):
+        assert L.awq_status_string(st)
+    assert L.awq_status_string(99) == b"unknown status"
+
+
+OK, INVALID, SHAPE, UNSUP, WS, HIP = 0, 1, 2, 3, 4, 5
+BF16, F32 = 1, 0
+P = 1 << 20  # a fake, 16-byte aligned device address: never dereferenced on these paths
+
+
+def test_workspace_size_functions(L):
+    assert L.awq_stats_workspace_bytes(0, 256) == 0
+    assert L.awq_stats_workspace_bytes(4096, 4096) > 0
+    assert L.awq_search_workspace_bytes(4096, 4096, 4096, 128, 20) > 4096 * 20 * 8
+    assert L.awq_search_workspace_bytes(4096, 4096, 4096, 64, 20) == 0
+    assert L.awq_search_workspace_bytes(4096, 4000, 4096, 128, 20) == 0
+    assert L.awq_search_workspace_bytes(4096, 4096, 4096, 128, 0) == 0
+    assert L.awq_search_workspace_bytes(4096, 4096, 4096, 128, 65) == 0
+
+
+def stats(L, X=P, dt=BF16, M=64, K=256, ldx=256, a=P, ws=P, wsb=1 << 30, fl=P):
+    return L.awq_stats(X, dt, M, K, ldx, a, ws, wsb, fl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(a=None), INVALID), (dict(fl=None), INVALID),
+    (dict(M=0), INVALID), (dict(K=0), INVALID), (dict(ldx=128), INVALID),
+    (dict(K=200, ldx=200), SHAPE), (dict(dt=7), UNSUP), (dict(X=P + 8), INVALID),
+    (dict(ldx=260), INVALID),  # 520-byte rows break 16-byte alignment
+    (dict(ws=None), WS), (dict(wsb=16), WS), (dict(M=1 << 62, ldx=1 << 10, K=256), SHAPE),
+])
+def test_stats_argument_errors(L, kw, status):
+    assert stats(L, **kw) == status
+
+
+def search(L, X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, a=P, group=128, n_grid=20,
+           losses=P, best=P, sb=P, tab=None, ws=P, wsb=1 << 30, fl=P):
+    return L.awq_search(X, xt, M, K, ldx, W, wt, N, ldw, a, group, n_grid, losses, best, sb, tab, ws, wsb, fl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(W=None), INVALID), (dict(a=None), INVALID), (dict(losses=None), INVALID),
+    (dict(best=None), INVALID), (dict(sb=None), INVALID), (dict(fl=None), INVALID),
+    (dict(N=0), INVALID), (dict(ldw=128), INVALID), (dict(K=384, ldx=384, ldw=200), INVALID),
+    (dict(K=192, ldx=192, ldw=192), SHAPE), (dict(group=64), UNSUP), (dict(group=256), UNSUP),
+    (dict(n_grid=0), INVALID), (dict(n_grid=65), INVALID), (dict(xt=3), UNSUP), (dict(wt=-1), UNSUP),
+    (dict(ws=None), WS), (dict(wsb=1000), WS), (dict(a=P + 4), INVALID), (dict(tab=P + 4), INVALID),
+    (dict(ldx=1 << 21, K=256), SHAPE),  # 512 rows of X would span more than 2^31 bytes
+])
+def test_search_argument_errors(L, kw, status):
+    assert search(L, **kw) == status
+
+
+def pack(L, W=P, wt=BF16, N=128, K=256, ldw=256, s=P, group=128, q=P, sc=P, z=P, fl=P):
+    return L.awq_pack(W, wt, N, K, ldw, s, group, q, sc, z, fl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), INVALID), (dict(s=None), INVALID), (dict(q=None), INVALID), (dict(sc=None), INVALID),
+    (dict(z=None), INVALID), (dict(fl=None), INVALID), (dict(N=-1), INVALID), (dict(K=100, ldw=100), SHAPE),
+    (dict(group=32), UNSUP), (dict(wt=5), UNSUP), (dict(s=P + 2), INVALID),
+])
+def test_pack_argument_errors(L, kw, status):
+    assert pack(L, **kw) == status
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    from post_weight_quantization_mean_amd import awq
+    with pytest.raises(ValueError):
+        awq.stats(torch.zeros(4, 128))
+    with pytest.raises(TypeError):
+        awq._dtype_code(torch.zeros(2, dtype=torch.float16))
