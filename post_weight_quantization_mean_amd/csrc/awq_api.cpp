@@ -44,19 +44,20 @@ int check_matrix(const void* p, int dtype, int64_t rows, int64_t K, int64_t ld) 
 int map_hip(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
 
 struct SearchLayout {
-  size_t s_tab, rs_tab, params, partial, total;
+  size_t s_tab, rs_tab, sr_tab, params, partial, total;
 };
 
 bool search_layout(int64_t M, int64_t K, int64_t N, int n_grid, SearchLayout* out) {
   const awq::SearchPlan plan = awq::search_plan(M, K, N, n_grid);
   const int64_t tab = mul_ok(mul_ok(n_grid, K), 4);
-  const int64_t par = mul_ok(mul_ok(mul_ok(n_grid, N), K / kGroup), 8);
+  const int64_t par = mul_ok(mul_ok(mul_ok(n_grid, awq::padded_n(N)), K / kGroup), 8);
   const int64_t part = mul_ok(mul_ok(n_grid, plan.tiles), 8);
   if (tab < 0 || par < 0 || part < 0) return false;
   SearchLayout L;
   L.s_tab = 0;
   L.rs_tab = L.s_tab + align_up((size_t)tab);
-  L.params = L.rs_tab + align_up((size_t)tab);
+  L.sr_tab = L.rs_tab + align_up((size_t)tab);
+  L.params = L.sr_tab + align_up((size_t)tab * 2);
   L.partial = L.params + align_up((size_t)par);
   L.total = L.partial + align_up((size_t)part);
   *out = L;
@@ -141,18 +142,19 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
   char* base = static_cast<char*>(ws);
   float* s_tab = s_table_out != nullptr ? s_table_out : reinterpret_cast<float*>(base + L.s_tab);
   float* rs_tab = reinterpret_cast<float*>(base + L.rs_tab);
+  float2* sr_tab = reinterpret_cast<float2*>(base + L.sr_tab);
   float2* params = reinterpret_cast<float2*>(base + L.params);
   double* partial = reinterpret_cast<double*>(base + L.partial);
   const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const awq::SearchPlan plan = awq::search_plan(M, K, N, n_grid);
 
-  hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, flags, s);
+  hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
   if (e == hipSuccess)
     e = awq::launch_group_range(W, wf32, N, K, ldw, s_tab, n_grid, params, flags, s);
   if (e == hipSuccess)
-    e = awq::launch_search_fused(X, xf32, M, ldx, W, wf32, N, K, ldw, s_tab, rs_tab, params,
-                                 n_grid, plan, partial, s);
+    e = awq::launch_search_fused(X, xf32, M, ldx, W, wf32, N, K, ldw, s_tab, rs_tab, sr_tab,
+                                 params, n_grid, plan, partial, s);
   if (e == hipSuccess)
     e = awq::launch_select(partial, plan.tiles, n_grid, M, N, K, s_tab, losses_out, best_out,
                            s_best_out, flags, s);

@@ -30,6 +30,15 @@ hipError_t launch_stats(const void* X, bool f32, int64_t M, int64_t K, int64_t l
 constexpr int kSearchBM = 512;  // tokens per block tile
 constexpr int kSearchBN = 128;  // output channels per block tile
 
+// Group ranges (Delta, z) of every (candidate, group, output channel) live in the workspace
+// as float2 [n_grid][K/128][Npad] with Npad = N rounded up to 128.  Within each 128-channel
+// tile, channel r and channel r + 64 sit side by side (slot 2 (r % 64) + r / 64), so one
+// 16-byte load gives a thread the ranges of both rows it quantizes.
+__host__ __device__ inline int64_t padded_n(int64_t N) { return (N + 127) / 128 * 128; }
+__host__ __device__ inline int64_t range_slot(int64_t n) {
+  return (n / 128) * 128 + 2 * (n % 64) + (n % 128) / 64;
+}
+
 struct SearchPlan {
   int64_t mt, nt;    // tiles along M and N
   int64_t tiles;     // mt * nt
@@ -38,15 +47,16 @@ struct SearchPlan {
 };
 SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid);
 
+// s_tab, rs_tab: fp32 [n_grid, K]; sr_tab: the same pairs interleaved, float2 [n_grid, K]
 hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
-                              uint32_t* flags, hipStream_t st);
+                              float2* sr_tab, uint32_t* flags, hipStream_t st);
 hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
                               const float* s_tab, int n_grid, float2* params, uint32_t* flags,
                               hipStream_t st);
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const void* W,
                                bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s_tab,
-                               const float* rs_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st);
+                               const float* rs_tab, const float2* sr_tab, const float2* params,
+                               int n_grid, const SearchPlan& plan, double* partial, hipStream_t st);
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
                          float* s_best, uint32_t* flags, hipStream_t st);

@@ -18,6 +18,7 @@ __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float*
                                                                    int64_t K, int n_grid,
                                                                    float* __restrict__ s_tab,
                                                                    float* __restrict__ rs_tab,
+                                                                   float2* __restrict__ sr_tab,
                                                                    uint32_t* __restrict__ flags) {
   __shared__ double smax[kScaleThreads / 64];
   __shared__ double smin[kScaleThreads / 64];
@@ -55,6 +56,7 @@ __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float*
     if (!(s > 0.0f) || isinf(s) || isinf(rs)) bad = true;
     s_tab[(int64_t)i * K + j] = s;
     rs_tab[(int64_t)i * K + j] = rs;
+    sr_tab[(int64_t)i * K + j] = make_float2(s, rs);
   }
   if (bad) atomicOr(flags, kFlagScaleRange);
 }
@@ -70,11 +72,13 @@ __global__ __launch_bounds__(256) void group_range_kernel(const void* __restrict
                                                          int n_grid, float2* __restrict__ params,
                                                          uint32_t* __restrict__ flags) {
   const int64_t G = K / kGroup;
+  const int64_t NP = padded_n(N);
+  // 16 lanes per (group g, channel n); a block covers 16 consecutive channels of one group
   const int64_t grp = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const bool live = grp < N * G;
-  const int64_t n = live ? grp / G : 0;
-  const int64_t g = live ? grp % G : 0;
+  const int64_t g = live ? grp / N : 0;
+  const int64_t n = live ? grp % N : 0;
   const int64_t k0 = g * kGroup + sub * 8;
 
   float w[8];
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256) void group_range_kernel(const void* __restrict
       if (!isfinite(range)) bad = true;
       const float delta = fmaxf(range, 1e-5f) / 15.0f;
       const float z = fminf(fmaxf(rintf(-mn / delta), 0.0f), 15.0f);
-      params[((int64_t)al * N + n) * G + g] = make_float2(delta, z);
+      params[((int64_t)al * G + g) * NP + range_slot(n)] = make_float2(delta, z);
     }
   }
   if (live && bad) atomicOr(flags, kFlagNonfiniteW);
@@ -167,8 +171,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 }  // namespace
 
 hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
-                              uint32_t* flags, hipStream_t st) {
-  scale_table_kernel<<<n_grid, kScaleThreads, 0, st>>>(a, K, n_grid, s_tab, rs_tab, flags);
+                              float2* sr_tab, uint32_t* flags, hipStream_t st) {
+  scale_table_kernel<<<n_grid, kScaleThreads, 0, st>>>(a, K, n_grid, s_tab, rs_tab, sr_tab, flags);
   return hipGetLastError();
 }
 

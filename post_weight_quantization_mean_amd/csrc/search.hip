@@ -122,13 +122,14 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
   const float* srow = s_tab + (int64_t)al * K + wkp * WEL;
   const float* rsrow = rs_tab + (int64_t)al * K + wkp * WEL;
   // group ranges of this thread's W rows (rows past N read row N-1 and are masked)
-  const float2* prow[WP];
+  const int64_t NP = padded_n(N);
+  const float2* prow[WP];  // this thread's rows in the range table of candidate al
   bool wlive[WP];
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
-    const int64_t n = n0 + wrow0 + Gm::WROW_STEP * i;
+    const int64_t n = n0 + wrow0 + Gm::WROW_STEP * i;  // < NP (tiles never pass NP)
     wlive[i] = n < N;
-    prow[i] = params + ((int64_t)al * N + (wlive[i] ? n : N - 1)) * G;
+    prow[i] = params + (int64_t)al * G * NP + range_slot(n);
   }
 
   uint4 xr[XP];
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
     }
     const uint32_t g = k0b / kGroup;
 #pragma unroll
-    for (int i = 0; i < WP; ++i) pr[i] = prow[i][g];
+    for (int i = 0; i < WP; ++i) pr[i] = prow[i][g * NP];
   };
 
   auto store_chunk = [&](int buf) {
@@ -294,39 +295,57 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
 
 
 // ---- pipelined kernel for bf16 X and bf16 W (the production path) ----------------------
-// Same tile and arithmetic as above; the K loop is software-pipelined:
-//   * X chunks go global -> LDS directly (buffer_load ... lds), two chunks ahead, into four
-//     LDS stages; no VGPRs or ds_write instructions are spent on X;
-//   * W chunks (and their scales, reciprocals and group ranges) are loaded into registers
-//     two chunks ahead, alternating between two register sets;
-//   * iteration c runs the matrix instructions of chunk c while the VALU quantizes chunk
-//     c+1 into the other E stage, so the two overlap on each SIMD.
+// Same tile and arithmetic as above; the K loop is software-pipelined three chunks deep:
+//   * X chunks go global -> LDS directly (buffer_load ... lds) into four LDS stages; no
+//     VGPRs or ds_write instructions are spent on X;
+//   * wave w quantizes the 8-channel piece w of every chunk, for rows `lane` and `lane + 64`:
+//     its W words and group ranges come in through two and one 16-byte vector loads; the
+//     chunk's 32 (s, 1/s) pairs come in through one 4-byte-per-lane load of an interleaved
+//     table and reach SGPRs with v_readlane (scalar loads would share lgkmcnt with LDS and
+//     turn every fragment wait into a full drain);
+//   * step c issues the 32 matrix instructions of chunk c one by one, and behind each the
+//     VALU work of quantizing chunk c+1 (one element every other MFMA), the prefetch loads
+//     of chunk c+3 and the second-half fragment reads; sched_barrier pins that order so the
+//     matrix core, the VALU and the memory pipes run concurrently on each SIMD.
+// Measured on the 4096^3 layer, the vector-memory address path is the scarce resource, so
+// every wave issues 12 vector loads per chunk (8 X DMA, 2 W, 1 group range, 1 scale pair),
+// spread one per two matrix instructions.
 // LDS tiles are unpadded [rows][32 bf16] with the four 16-byte slots of a row permuted by
-// swz(row) = ((row >> 1) ^ (row >> 3)) & 3, which spreads the 32 rows of an MFMA fragment
-// read over all banks.  The loop is unrolled by 4 (4 X stages, 2 E stages, 2 register sets)
-// so every stage is a distinct LDS object and the compiler's wait counters stay exact.
-// Each wave waits for its own chunk-(c+1) DMA before the barrier that ends iteration c, so
-// after the barrier every wave may read rows that other waves fetched.
+// swz(row) = (row >> 2) & 3; with it the 32-row MFMA fragment reads (ds_read_b128) measure
+// zero bank-conflict cycles on gfx950, where unswizzled 64-byte rows cost 12 per read.
+// The loop is unrolled by 4 (4 X stages, 2 E stages, 4 register sets) so every stage is a
+// distinct LDS object and the compiler's wait counters stay exact.  Each wave waits for its
+// own chunk-(c+1) DMA before the barrier that ends step c, so after the barrier every wave
+// may read rows that other waves fetched.
 #define AWQ_LDS __attribute__((address_space(3)))
 
-constexpr int PKC = 32;           // input channels per chunk
-constexpr int PROW = PKC * 2;     // bytes per LDS row
-constexpr int XSTAGE = BM * PROW; // 32 KiB
-constexpr int ESTAGE = BN * PROW; // 8 KiB
+constexpr int PKC = 32;            // input channels per chunk
+constexpr int PROW = PKC * 2;      // bytes per LDS row
+constexpr int XSTAGE = BM * PROW;  // 32 KiB
+constexpr int ESTAGE = BN * PROW;  // 8 KiB
 
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 struct WSet {
-  uint4 w[2];
-  float4 s[2], rs[2];
-  float2 p[2];
+  uint4 w[2];   // 8 bf16 channels of rows lane and lane + 64
+  float4 p;     // (Delta, z) of row lane, then of row lane + 64, for this chunk's group
+  float sr;     // lane l holds s (l even) or 1/s (l odd) of channel l / 2 of the chunk
+};
+struct SVal {
+  float s[8];   // wave-uniform (SGPRs, via v_readlane): s of this wave's 8 channels
+  float rs[8];  // 1 / s
+};
+
+struct RowQ {
+  float delta, inv, lo, hi;
 };
 
 __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const uint16_t* __restrict__ W,
     int64_t N, int64_t K, int64_t ldw, const float* __restrict__ s_tab,
-    const float* __restrict__ rs_tab, const float2* __restrict__ params, int n_grid,
-    int64_t nt_count, int64_t tiles, int64_t per_xcd, double* __restrict__ partial) {
+    const float* __restrict__ rs_tab, const float2* __restrict__ sr_tab,
+    const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles,
+    int64_t per_xcd, double* __restrict__ partial) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs2[XSTAGE];
@@ -343,6 +362,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int64_t m0 = (tile / nt_count) * BM;
   const int64_t n0 = (tile % nt_count) * BN;
   const int64_t G = K / kGroup;
+  const int64_t NP = padded_n(N);
   const int nchunks = (int)(K / PKC);
 
   const int tid = threadIdx.x;
@@ -350,9 +370,9 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // X: DMA instruction i of this wave fills LDS rows (4 i + wave) * 16 + lane / 4, slot
-  // lane % 4, with global piece kp = slot ^ swz(row).
-  const int64_t xrows = M - m0, wrows = N - n0;
-  const int64_t xbytes = xrows * ldx * 2, wbytes = wrows * ldw * 2;
+  // lane % 4, with the global piece kp = slot ^ swz(row).  Buffer resources are rebased at
+  // this tile so rows past M (or N) read as zero; offsets stay below 2^31 (host-checked).
+  const int64_t xbytes = (M - m0) * ldx * 2, wbytes = (N - n0) * ldw * 2;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -364,76 +384,80 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     const int kp = (lane & 3) ^ swz(row);
     xoff[i] = (uint32_t)(row * ldx * 2 + kp * 16);
   }
-  // W: thread owns rows wrow0 and wrow0 + 64, piece wkp (8 channels)
-  const int wkp = tid & 3;
-  const int wrow0 = tid >> 2;
-  const uint32_t woff0 = (uint32_t)(wrow0 * ldw * 2 + wkp * 16);
-  const uint32_t woff1 = (uint32_t)((wrow0 + 64) * ldw * 2 + wkp * 16);
-  const int eslot0 = (wrow0 * PROW) + ((wkp ^ swz(wrow0)) * 16);
-  const int eslot1 = ((wrow0 + 64) * PROW) + ((wkp ^ swz(wrow0 + 64)) * 16);
-  const float* srow = s_tab + (int64_t)al * K + wkp * 8;
-  const float* rsrow = rs_tab + (int64_t)al * K + wkp * 8;
-  const bool live0 = n0 + wrow0 < N, live1 = n0 + wrow0 + 64 < N;
-  const float2* prow0 = params + ((int64_t)al * N + (live0 ? n0 + wrow0 : N - 1)) * G;
-  const float2* prow1 = params + ((int64_t)al * N + (live1 ? n0 + wrow0 + 64 : N - 1)) * G;
+  // W side: this wave's piece is channels 8 wave .. 8 wave + 7 of each chunk
+  const uint32_t woff0 = (uint32_t)(lane * ldw * 2 + wave * 16);
+  const uint32_t woff1 = (uint32_t)((lane + 64) * ldw * 2 + wave * 16);
+  const int eslot0 = lane * PROW + ((wave ^ swz(lane)) * 16);
+  const int eslot1 = (lane + 64) * PROW + ((wave ^ swz(lane + 64)) * 16);
+  const bool live0 = n0 + lane < N, live1 = n0 + lane + 64 < N;
+  const float* srbase = reinterpret_cast<const float*>(sr_tab) + (int64_t)al * K * 2 + lane;
+  // ranges of rows lane and lane + 64 are adjacent (range_slot); rows past N are masked
+  const float4* pbase = reinterpret_cast<const float4*>(params + (int64_t)al * G * NP + n0 + 2 * lane);
 
-  // fragment reads: lane reads row (.. + fr), slot (2 j + fh) ^ swz(fr)
+  // fragment reads: lane reads row (... + fr), slot (2 j + fh) ^ swz(fr)
   const int fr = lane & 31, fh = lane >> 5;
   const int fsw = swz(fr);
   const int foff0 = fr * PROW + (((0 + fh) ^ fsw) * 16);
   const int foff1 = fr * PROW + (((2 + fh) ^ fsw) * 16);
   const int xwave = wave * WAVE_ROWS * PROW;
 
-  auto dma_x = [&](uint8_t* stage, int c) {
-    const uint32_t kb = (uint32_t)c * (PKC * 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrsrc, (AWQ_LDS void*)(stage + (4 * i + wave) * 1024), 16, (int)(xoff[i] + kb), 0, 0, 0);
+  auto dma_x_one = [&](uint8_t* stage, int i, uint32_t kb) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(stage + (4 * i + wave) * 1024), 16,
+                                             (int)(xoff[i] + kb), 0, 0, 0);
   };
-  auto load_w = [&](WSet& S, int c) {
-    const uint32_t kb = (uint32_t)c * (PKC * 2);
+  auto load_w0 = [&](WSet& S, uint32_t kb) {
     S.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(woff0 + kb), 0, 0));
+  };
+  auto load_w1 = [&](WSet& S, uint32_t kb) {
     S.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(woff1 + kb), 0, 0));
-    const int k0 = c * PKC;
-    S.s[0] = *reinterpret_cast<const float4*>(srow + k0);
-    S.s[1] = *reinterpret_cast<const float4*>(srow + k0 + 4);
-    S.rs[0] = *reinterpret_cast<const float4*>(rsrow + k0);
-    S.rs[1] = *reinterpret_cast<const float4*>(rsrow + k0 + 4);
-    const int g = k0 / kGroup;
-    S.p[0] = prow0[g];
-    S.p[1] = prow1[g];
   };
-  auto qdq_store = [&](const WSet& S, uint8_t* estage) {
-    const float sv[8] = {S.s[0].x, S.s[0].y, S.s[0].z, S.s[0].w, S.s[1].x, S.s[1].y, S.s[1].z, S.s[1].w};
-    const float rv[8] = {S.rs[0].x, S.rs[0].y, S.rs[0].z, S.rs[0].w,
-                         S.rs[1].x, S.rs[1].y, S.rs[1].z, S.rs[1].w};
+  auto load_p = [&](WSet& S, int k0) { S.p = pbase[(int64_t)(k0 / kGroup) * (NP / 2)]; };
+  auto load_sr = [&](WSet& S, int k0) { S.sr = srbase[2 * k0]; };
+  auto get_s = [&](const WSet& S) {
+    SVal v;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool live = i == 0 ? live0 : live1;
-      const float delta = live ? S.p[i].x : 1.0f;  // rows past N: e = 0 exactly
-      const float z = live ? S.p[i].y : 0.0f;
-      const float inv = __builtin_amdgcn_rcpf(delta);
-      const float lo = -z, hi = 15.0f - z;
-      const uint32_t u[4] = {S.w[i].x, S.w[i].y, S.w[i].z, S.w[i].w};
-      uint32_t pk[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float e2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int j = 2 * q + h;
-          const float w = h == 0 ? bf16_lo(u[q]) : bf16_hi(u[q]);
-          const float v = w * sv[j];                                // S W
-          const float r = rintf(v * inv);                           // rne(v / Delta)
-          const float qz = __builtin_amdgcn_fmed3f(r, lo, hi);      // clamp(r + z, 0, 15) - z
-          e2[h] = fmaf(-(qz * delta), rv[j], w);                    // w - Delta (q - z) / s
-        }
-        pk[q] = pack_bf16x2(e2[0], e2[1]);
-      }
-      *reinterpret_cast<uint4*>(estage + (i == 0 ? eslot0 : eslot1)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    for (int j = 0; j < 8; ++j) {
+      v.s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.sr), 16 * wave + 2 * j));
+      v.rs[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.sr), 16 * wave + 2 * j + 1));
     }
+    return v;
   };
+  auto load_all = [&](WSet& S, uint8_t* stage, int c) {
+    const uint32_t kb = (uint32_t)c * (PKC * 2);
+    load_sr(S, c * PKC);
+    load_w0(S, kb);
+    load_w1(S, kb);
+    load_p(S, c * PKC);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_x_one(stage, i, kb);
+  };
+  auto row_setup = [&](const WSet& S, int i) {
+    const bool live = i == 0 ? live0 : live1;
+    RowQ q;
+    q.delta = live ? (i == 0 ? S.p.x : S.p.z) : 1.0f;  // rows past N: Delta 1, z 0, w 0: e = 0
+    const float z = live ? (i == 0 ? S.p.y : S.p.w) : 0.0f;
+    q.inv = __builtin_amdgcn_rcpf(q.delta);  // search only; the pack divides exactly
+    q.lo = -z;
+    q.hi = 15.0f - z;
+    return q;
+  };
+  // e = w - Delta (q - z) / s for channel j (0..7) of row i (0/1)
+  auto elem = [&](const WSet& S, const SVal& T, const RowQ& q, int i, int j) {
+    const uint4& w4 = S.w[i];
+    const uint32_t u = j < 2 ? w4.x : j < 4 ? w4.y : j < 6 ? w4.z : w4.w;
+    const float w = (j & 1) ? bf16_hi(u) : bf16_lo(u);
+    const float v = w * T.s[j];                               // S W
+    const float r = rintf(v * q.inv);                         // rne(v / Delta)
+    const float qz = __builtin_amdgcn_fmed3f(r, q.lo, q.hi);  // clamp(r + z, 0, 15) - z
+    return fmaf(-(qz * q.delta), T.rs[j], w);                 // w - Delta (q - z) / s
+  };
+  auto store_piece = [&](uint8_t* estage, int slot, const float* e8) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pk[h] = pack_bf16x2(e8[2 * h], e8[2 * h + 1]);
+    *reinterpret_cast<uint4*>(estage + slot) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  };
+  auto frag = [&](const uint8_t* base, int fo) { return *reinterpret_cast<const bf16x8*>(base + fo); };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -443,67 +467,108 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
 
-  auto mfma_chunk = [&](const uint8_t* xst, const uint8_t* est) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int fo = j == 0 ? foff0 : foff1;
-      bf16x8 bfr[4], afr[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bfr[c] = *reinterpret_cast<const bf16x8*>(est + c * 32 * PROW + fo);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) afr[r] = *reinterpret_cast<const bf16x8*>(xst + xwave + r * 32 * PROW + fo);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[r], bfr[c], acc[r][c], 0, 0, 0);
-    }
-  };
-
   // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
-  // lgkmcnt[11:8] | vmcnt[5:4] at [15:14]); n = 16 = loads issued per iteration.
-  constexpr int kLoadsPerIter = 8 + 2 + 4 + 2;
-  constexpr int kWaitVm = (kLoadsPerIter & 0xf) | (0x7 << 4) | (0xf << 8) | ((kLoadsPerIter >> 4) << 14);
+  // lgkmcnt[11:8] | vmcnt[5:4] at [15:14]); n = 24 = vector loads issued by two steps.
+  constexpr int kLoadsPerStep = 1 + 2 + 1 + 8;
+  constexpr int kPending = 2 * kLoadsPerStep;
+  constexpr int kWaitVm = (kPending & 0xf) | (0x7 << 4) | (0xf << 8) | ((kPending >> 4) << 14);
   constexpr int kWaitLgkm0 = 0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
-  WSet A, B;
-  // Prologue: W(0), X(0), W(1), X(1) in flight; chunk 0 quantized into E stage 0.  Every
-  // step then issues W(c+2) before X(c+2), so at the end of step c exactly the 16 loads of
-  // that step were issued after X(c+1): vmcnt(16) means this wave's X(c+1) has landed.
-  load_w(A, 0);
-  dma_x(xs0, 0);
-  load_w(B, 1);
-  dma_x(xs1, 1);
-  qdq_store(A, es0);
+  WSet S0, S1, S2, S3;  // three chunks ahead
+  // Prologue: chunks 0, 1 and 2 in flight (the X DMA last in each), chunk 0 quantized into
+  // E stage 0.  Every step c then issues the 12 vector loads of chunk c+3, X DMA last, so at
+  // the end of step c vmcnt(24) means this wave's X DMA of chunk c+1 has landed.
+  load_all(S0, xs0, 0);
+  load_all(S1, xs1, 1);
+  load_all(S2, xs2, 2);
+  {
+    float e[8];
+    const SVal T0 = get_s(S0);
+    const RowQ q0 = row_setup(S0, 0), q1 = row_setup(S0, 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S0, T0, q0, 0, j);
+    store_piece(es0, eslot0, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S0, T0, q1, 1, j);
+    store_piece(es0, eslot1, e);
+  }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(kWaitVm);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  // One pipeline step: matrix work of chunk c from (xc, ec); quantize chunk c+1 from `next`
-  // into en; prefetch chunk c+2 into `fill` and xn.  Past the end the prefetch repeats the
-  // last chunk into stages nobody reads again.
+  // One pipeline step, hand-scheduled in 32 groups, one per matrix instruction of chunk c.
+  // Group g: MFMA g; in odd groups one element of the quantization of chunk c+1; in groups
+  // 0-7 one second-half fragment read; in even groups 0-22 one prefetch load of chunk c+3
+  // (scales, W words, group ranges, then the 8 X DMA), so no group carries more than one
+  // vector-memory instruction behind its 32-cycle MFMA.
   auto step = [&](int c, const uint8_t* xc, uint8_t* xn, const uint8_t* ec, uint8_t* en,
                   const WSet& next, WSet& fill) {
-    const int cp = c + 2 < nchunks ? c + 2 : nchunks - 1;
-    load_w(fill, cp);
-    dma_x(xn, cp);
-    mfma_chunk(xc, ec);
-    qdq_store(next, en);
+    const int cp = c + 3 < nchunks ? c + 3 : nchunks - 1;  // past the end: harmless reload
+    const uint32_t kb = (uint32_t)cp * (PKC * 2);
+    const int k0 = cp * PKC;
+    const uint8_t* xw = xc + xwave;
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a0[t] = frag(xw + t * 32 * PROW, foff0);
+      b0[t] = frag(ec + t * 32 * PROW, foff0);
+    }
+    const SVal tv = get_s(next);
+    const RowQ q0 = row_setup(next, 0);
+    const RowQ q1 = row_setup(next, 1);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm);  // this wave's chunk c+1 DMA has landed
+    float e[16];
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      const int r = (g >> 2) & 3, cc = g & 3;
+      if (g < 16)
+        acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[r], b0[cc], acc[r][cc], 0, 0, 0);
+      else
+        acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[r], b1[cc], acc[r][cc], 0, 0, 0);
+      if (g & 1) {
+        const int el = g >> 1;
+        e[el] = el < 8 ? elem(next, tv, q0, 0, el) : elem(next, tv, q1, 1, el - 8);
+        asm volatile("" : "+v"(e[el]));  // keep the element in this group (no IR sinking)
+      }
+      if (g < 8) {
+        if (g & 1)
+          b1[g >> 1] = frag(ec + (g >> 1) * 32 * PROW, foff1);
+        else
+          a1[g >> 1] = frag(xw + (g >> 1) * 32 * PROW, foff1);
+      }
+      if (g == 0) {
+        load_sr(fill, k0);
+      } else if (g == 2) {
+        load_w0(fill, kb);
+      } else if (g == 4) {
+        load_w1(fill, kb);
+      } else if (g == 6) {
+        load_p(fill, k0);
+      } else if (g >= 8 && g <= 22 && (g & 1) == 0) {
+        dma_x_one(xn, (g - 8) >> 1, kb);
+      } else if (g == 17) {
+        store_piece(en, eslot0, e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    store_piece(en, eslot1, e + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm);  // this wave's chunk c+1 loads (X DMA too) landed
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // nchunks = K / 32 is a multiple of 4 (K is a multiple of 128)
+  // nchunks = K / 32 is a multiple of 4 (K is a multiple of 128).  Step c reads X stage
+  // c % 4 and E stage c % 2, quantizes register set (c+1) % 4 into E stage (c+1) % 2 and
+  // fills register set (c+3) % 4 and X stage (c+3) % 4 (last read in step c-1).
   for (int c = 0; c < nchunks; c += 4) {
-    step(c + 0, xs0, xs2, es0, es1, B, A);
-    step(c + 1, xs1, xs3, es1, es0, A, B);
-    step(c + 2, xs2, xs0, es0, es1, B, A);
-    step(c + 3, xs3, xs1, es1, es0, A, B);
+    step(c + 0, xs0, xs3, es0, es1, S1, S3);
+    step(c + 1, xs1, xs0, es1, es0, S2, S0);
+    step(c + 2, xs2, xs1, es0, es1, S3, S1);
+    step(c + 3, xs3, xs2, es1, es0, S0, S2);
   }
 
   double ss = 0.0;
@@ -538,8 +603,8 @@ SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
 
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const void* W,
                                bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s_tab,
-                               const float* rs_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st) {
+                               const float* rs_tab, const float2* sr_tab, const float2* params,
+                               int n_grid, const SearchPlan& plan, double* partial, hipStream_t st) {
   const int64_t per_xcd = plan.blocks / 8;
   const dim3 grid((unsigned)plan.blocks);
 #define AWQ_LAUNCH(XF, WF)                                                                      \
@@ -549,7 +614,7 @@ hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx,
   if (!xf32 && !wf32) {
     search_pipelined_kernel<<<grid, THREADS, 0, st>>>(
         static_cast<const uint16_t*>(X), M, ldx, static_cast<const uint16_t*>(W), N, K, ldw, s_tab,
-        rs_tab, params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
+        rs_tab, sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
     return hipGetLastError();
   }
   if (xf32 && wf32)
