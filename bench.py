@@ -26,9 +26,10 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (AMD spec, 2.5 PF cla
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
-def cpu_baseline(config: str, n_sample: int):
+def cpu_baseline(config: str, n_sample: int, min_seconds: float = 10.0, max_reps: int = 3):
     """The oracle as it stands, on a bounded column sample of the same layer (all M tokens,
-    all K channels, the first n_sample output channels), scaled to layer-searches/s."""
+    all K channels, the first n_sample output channels), scaled to layer-searches/s.  The
+    sample is repeated until at least min_seconds of CPU work (at most max_reps times)."""
     import numpy as np
     from oracle import awq_oracle as o
     from post_weight_quantization_mean_amd import synth
@@ -42,16 +43,55 @@ def cpu_baseline(config: str, n_sample: int):
     X = synth.make_x(spec, 0, cfg_id, 0)
     W = synth.make_w(spec, 0, cfg_id, 0, rows=n_sample)
     X64, W32 = synth.to_f64(X), synth.to_f32(W)
-    t0 = time.perf_counter()
-    a32 = o.activation_stat(X64).astype(np.float32)
-    res = o.search(X64, W32, a32)
-    o.pack(W32, res["s_best"])
-    dt = time.perf_counter() - t0
+    times = []
+    while not times or (sum(times) < min_seconds and len(times) < max_reps):
+        t0 = time.perf_counter()
+        a32 = o.activation_stat(X64).astype(np.float32)
+        res = o.search(X64, W32, a32)
+        o.pack(W32, res["s_best"])
+        times.append(time.perf_counter() - t0)
+    dt = statistics.mean(times)
     frac = n_sample / spec.N
     return {"value": frac / dt, "unit": "layer-searches/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{config} layer, all {spec.M} tokens and {spec.K} channels, first {n_sample} of "
-                      f"{spec.N} output channels (statistic over the full X); {dt:.2f} s measured, "
-                      f"scaled by N/{n_sample}"}
+                      f"{spec.N} output channels (statistic over the full X), stats + 20-candidate search "
+                      f"+ pack; {len(times)} run(s), mean {dt:.2f} s, scaled by N/{n_sample}"}
+
+
+def search_traffic(config: str):
+    """HBM bytes per launch of the fused search kernel, from the FETCH_SIZE / WRITE_SIZE counter
+    summary committed under profiles/, or None when that summary was taken on another version
+    of the kernel source (its sha256 is recorded there) or for another workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"search_fused_{config}_traffic.txt")
+    src = os.path.join(ROOT, "post_weight_quantization_mean_amd", "csrc", "search.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("search.hip sha256") != sha or "traffic bytes per launch" not in fields:
+        return None
+    return float(fields["traffic bytes per launch"])
+
+
+def copy_probe(mib: int, reps: int):
+    """A plain device-to-device copy of a known size, the calibration run for the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE per dispatch against 2 x mib MiB moved)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[-4:], src[-4:])
+    print(json.dumps({"copy_probe_mib": mib, "reps": reps, "bytes_read": n * 4, "bytes_written": n * 4}),
+          flush=True)
 
 
 def main():
@@ -61,12 +101,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="output channels of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the path would shard along N with one 160-byte loss all-reduce)"}))
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
 
     import torch
     from post_weight_quantization_mean_amd import awq, synth
@@ -87,21 +133,29 @@ def main():
     scales = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
     zeros = torch.empty_like(scales)
 
+    stream = torch.cuda.current_stream(dev)
+
     def events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        # [0..3]: stage boundaries on the call stream; [4], [5]: recorded by the library right
+        # before and after the fused search kernel, on the same stream
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in evs:
+            e.record(stream)  # creates the HIP event outside the timed region
+        return evs
 
     def step(ev=None):
         if ev:
-            ev[0].record()
+            ev[0].record(stream)
         awq.stats(Xd, out=a, workspace=ws_stats, flags=flags, check=False)
         if ev:
-            ev[1].record()
-        res = awq.search(Xd, Wd, a, workspace=ws_search, flags=flags, check=False)
+            ev[1].record(stream)
+        res = awq.search(Xd, Wd, a, workspace=ws_search, flags=flags, check=False,
+                         fused_events=(ev[4], ev[5]) if ev else None)
         if ev:
-            ev[2].record()
+            ev[2].record(stream)
         awq.pack(Wd, res.s_best, flags=flags, out=(qweight, scales, zeros), check=False)
         if ev:
-            ev[3].record()
+            ev[3].record(stream)
         return res
 
     for _ in range(args.warmup):
@@ -112,7 +166,6 @@ def main():
     # All events are created up front and read after the loop: no host sync inside the
     # timed region, every launch queued back to back on the one stream.
     evs = [events() for _ in range(args.steps)]
-    stream = torch.cuda.current_stream(dev)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -124,15 +177,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     awq.raise_for_flags(flags)
-    per_step = [(e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])) for e in evs]
+    per_step = [(e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]),
+                 e[4].elapsed_time(e[5])) for e in evs]
 
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     st_ms = statistics.mean(p[0] for p in per_step)
     se_ms = statistics.mean(p[1] for p in per_step)
     pk_ms = statistics.mean(p[2] for p in per_step)
+    fu_ms = statistics.mean(p[3] for p in per_step)
     flops = 20 * 2.0 * M * K * N
-    achieved = flops / (se_ms * 1e-3) / 1e12
+    achieved = flops / (fu_ms * 1e-3) / 1e12
+    traffic = search_traffic(args.config)
     out = {
         "metric": METRIC,
         "value": 1000.0 / ms_per_step,
@@ -146,13 +202,15 @@ def main():
                    "group": 128, "n_grid": 20},
         "effective_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "pct_mfma_peak": 100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "stage_ms": {"stats": st_ms, "search": se_ms, "pack": pk_ms},
+        "stage_ms": {"stats": st_ms, "search": se_ms, "search_fused_kernel": fu_ms, "pack": pk_ms},
         "stats_gbs": 2.0 * M * K / (st_ms * 1e-3) / 1e9,
         "pack_gbs": 2.53125 * K * N / (pk_ms * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "awq_search (scale table + group ranges + fused quantize/MFMA/SSE + select)",
-                     "work_per_launch": f"20 x 2*M*K*N = {flops:.4g} flop"},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "search_pipelined_kernel (fused quantize + bf16 MFMA error product + "
+                               "squared error, all 20 candidates in one launch)",
+                     "work_per_launch": f"20 x 2*M*K*N = {flops:.4g} flop",
+                     "ms_per_launch": fu_ms},
         "best_alpha": res.best_index / 20.0,
         "wall_s": wall,
     }

@@ -67,6 +67,7 @@ typedef enum { AWQ_DTYPE_F32 = 0, AWQ_DTYPE_BF16 = 1 } awq_dtype;
                                          in X or W reach every loss through the product) */
 
 typedef struct ihipStream_t* awq_stream_t; /* the same type as hipStream_t */
+typedef struct ihipEvent_t* awq_event_t;   /* the same type as hipEvent_t */
 
 /* ABI version of the loaded library (AWQ_ABI_VERSION). */
 AWQ_API int awq_abi_version(void);
@@ -117,6 +118,18 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
                        int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
                        float* s_best_out, float* s_table_out, void* ws, size_t ws_bytes,
                        uint32_t* flags, awq_stream_t stream);
+
+/* The same search with two caller-created events (hipEventCreate; either may be NULL)
+ * recorded on `stream` immediately before and after the fused quantize + product + squared
+ * error kernel, so that a caller can time that kernel alone with hipEventElapsedTime (the
+ * scale table, group-range and select launches fall outside the pair).  Arguments, results
+ * and errors as awq_search; a failed hipEventRecord returns AWQ_ERR_HIP. */
+AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                             int32_t group, int32_t n_grid, double* losses_out,
+                             int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
+                             size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
+                             awq_event_t fused_begin, awq_event_t fused_end);
 
 /* ---------------------------------------------------------------------------------------
  * Step 5: real quantization and packing of S W ([EXPLAINER §7, §8]; [MODULES §5.3]:

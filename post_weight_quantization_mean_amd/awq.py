@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.awq_search.restype = ctypes.c_int
         L.awq_search.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, i64, i64, vp,
                                  i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.awq_search_timed.restype = ctypes.c_int
+        L.awq_search_timed.argtypes = L.awq_search.argtypes + [vp, vp]
         L.awq_pack.restype = ctypes.c_int
         L.awq_pack.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, vp, vp, vp]
         if L.awq_abi_version() != 1:
@@ -149,9 +151,14 @@ class SearchResult:
 
 def search(X: torch.Tensor, W: torch.Tensor, a: torch.Tensor, group_size: int = GROUP, n_grid: int = N_GRID,
            *, return_table: bool = False, workspace: Optional[torch.Tensor] = None,
-           flags: Optional[torch.Tensor] = None, check: bool = True) -> SearchResult:
+           flags: Optional[torch.Tensor] = None, check: bool = True,
+           fused_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> SearchResult:
     """The candidate scale search over alpha = i / n_grid for one layer (or several
-    projections sharing one input, concatenated along N)."""
+    projections sharing one input, concatenated along N).
+
+    ``fused_events``: two timing events that the library records right before and after the
+    fused candidate kernel (awq_search_timed), so that ``e0.elapsed_time(e1)`` is that
+    kernel's time alone."""
     M, K, ldx = _matrix(X, "X")
     N, Kw, ldw = _matrix(W, "W")
     if Kw != K:
@@ -166,10 +173,19 @@ def search(X: torch.Tensor, W: torch.Tensor, a: torch.Tensor, group_size: int = 
     need = search_workspace_bytes(M, K, N, group_size, n_grid)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    st = lib().awq_search(X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
-                          a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(),
-                          s_best.data_ptr(), s_table.data_ptr() if s_table is not None else None,
-                          ws.data_ptr(), ws.numel(), fl.data_ptr(), _stream(dev))
+    args = (X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
+            a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(),
+            s_best.data_ptr(), s_table.data_ptr() if s_table is not None else None,
+            ws.data_ptr(), ws.numel(), fl.data_ptr(), _stream(dev))
+    if fused_events is None:
+        st = lib().awq_search(*args)
+    else:
+        evs = []
+        for e in fused_events:
+            if not e.cuda_event:  # torch creates the HIP event lazily, on its first record
+                e.record(torch.cuda.current_stream(dev))
+            evs.append(e.cuda_event)
+        st = lib().awq_search_timed(*args, *evs)
     _check(st, "awq_search")
     if check:
         raise_for_flags(fl)

@@ -114,11 +114,12 @@ AWQ_API size_t awq_search_workspace_bytes(int64_t M, int64_t K, int64_t N, int32
   return L.total;
 }
 
-AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                       const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
-                       int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
-                       float* s_best_out, float* s_table_out, void* ws, size_t ws_bytes,
-                       uint32_t* flags, awq_stream_t stream) {
+AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                             int32_t group, int32_t n_grid, double* losses_out,
+                             int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
+                             size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
+                             awq_event_t fused_begin, awq_event_t fused_end) {
   int st = check_matrix(X, x_dtype, M, K, ldx);
   if (st != AWQ_OK) return st;
   st = check_matrix(W, w_dtype, N, K, ldw);
@@ -152,13 +153,27 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
   hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
   if (e == hipSuccess)
     e = awq::launch_group_range(W, wf32, N, K, ldw, s_tab, n_grid, params, flags, s);
+  if (e == hipSuccess && fused_begin != nullptr)
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
   if (e == hipSuccess)
     e = awq::launch_search_fused(X, xf32, M, ldx, W, wf32, N, K, ldw, s_tab, rs_tab, sr_tab,
                                  params, n_grid, plan, partial, s);
+  if (e == hipSuccess && fused_end != nullptr)
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_end), s);
   if (e == hipSuccess)
     e = awq::launch_select(partial, plan.tiles, n_grid, M, N, K, s_tab, losses_out, best_out,
                            s_best_out, flags, s);
   return map_hip(e);
+}
+
+AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                       const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                       int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
+                       float* s_best_out, float* s_table_out, void* ws, size_t ws_bytes,
+                       uint32_t* flags, awq_stream_t stream) {
+  return awq_search_timed(X, x_dtype, M, K, ldx, W, w_dtype, N, ldw, a, group, n_grid,
+                          losses_out, best_out, s_best_out, s_table_out, ws, ws_bytes, flags,
+                          stream, nullptr, nullptr);
 }
 
 AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,

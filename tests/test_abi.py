@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
-                          "awq_search_workspace_bytes", "awq_search", "awq_pack"}
+                          "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack"}
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -91,6 +91,17 @@ def search(L, X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, 
 ])
 def test_search_argument_errors(L, kw, status):
     assert search(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(X=None), INVALID), (dict(group=64), UNSUP), (dict(wsb=1000), WS)])
+def test_search_timed_argument_errors(L, kw, status):
+    # the timed variant validates exactly like awq_search, before recording any event
+    a = dict(X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, a=P, group=128, n_grid=20,
+             losses=P, best=P, sb=P, tab=None, ws=P, wsb=1 << 30, fl=P)
+    a.update(kw)
+    assert L.awq_search_timed(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["W"], a["wt"], a["N"], a["ldw"],
+                              a["a"], a["group"], a["n_grid"], a["losses"], a["best"], a["sb"], a["tab"],
+                              a["ws"], a["wsb"], a["fl"], None, None, None) == status
 
 
 def pack(L, W=P, wt=BF16, N=128, K=256, ldw=256, s=P, group=128, q=P, sc=P, z=P, fl=P):

@@ -156,6 +156,25 @@ def test_search_is_deterministic(awq):
     assert torch.equal(r1.losses, r2.losses) and torch.equal(r1.s_best, r2.s_best)
 
 
+def test_search_timed_matches_search(awq):
+    """awq_search_timed returns exactly what awq_search returns, and its two events bracket a
+    positive time no longer than the whole call."""
+    banner("search_timed")
+    _, X, W = synth.custom_layer(1024, 512, 384, seed=6)
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    a = awq.stats(Xd)
+    r1 = awq.search(Xd, Wd, a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    r2 = awq.search(Xd, Wd, a, fused_events=(ev[1], ev[2]))
+    ev[3].record()
+    torch.cuda.synchronize()
+    assert torch.equal(r1.losses, r2.losses) and torch.equal(r1.best, r2.best)
+    assert torch.equal(r1.s_best, r2.s_best)
+    fused, whole = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < fused <= whole
+
+
 GOLDEN_LOSSES = os.path.join(GOLDEN, "oracle_losses.json")
 
 
