@@ -32,11 +32,13 @@ constexpr int kSearchBN = 128;  // output channels per block tile
 
 // Group ranges (Delta, z) of every (candidate, group, output channel) live in the workspace
 // as float2 [n_grid][K/128][Npad] with Npad = N rounded up to 128.  Within each 128-channel
-// tile, channel r and channel r + 64 sit side by side (slot 2 (r % 64) + r / 64), so one
-// 16-byte load gives a thread the ranges of both rows it quantizes.
+// tile, channel r = 32 w + 16 i + j (w < 4, i < 2, j < 16) sits at slot 32 w + 2 j + i, so
+// rows r and r + 16 are side by side and one 16-byte load gives a thread the ranges of both
+// rows it quantizes.
 __host__ __device__ inline int64_t padded_n(int64_t N) { return (N + 127) / 128 * 128; }
 __host__ __device__ inline int64_t range_slot(int64_t n) {
-  return (n / 128) * 128 + 2 * (n % 64) + (n % 128) / 64;
+  const int64_t r = n % 128;
+  return (n / 128) * 128 + (r / 32) * 32 + 2 * (r % 16) + (r % 32) / 16;
 }
 
 struct SearchPlan {

@@ -23,6 +23,8 @@
 // Block order is XCD-aware: the hardware places workgroup b on XCD b % 8, so logical index
 // L = (b % 8) * ceil(G/8) + b / 8 gives every XCD a contiguous run of L.  L runs candidate-
 // fastest, so the ~32 blocks resident on one XCD share the same X rows and W rows in its L2.
+#include <type_traits>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -295,45 +297,45 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
 
 
 // ---- pipelined kernel for bf16 X and bf16 W (the production path) ----------------------
-// Same tile and arithmetic as above; the K loop is software-pipelined three chunks deep:
-//   * X chunks go global -> LDS directly (buffer_load ... lds) into four LDS stages; no
-//     VGPRs or ds_write instructions are spent on X;
-//   * wave w quantizes the 8-channel piece w of every chunk, for rows `lane` and `lane + 64`:
-//     its W words and group ranges come in through two and one 16-byte vector loads; the
-//     chunk's 32 (s, 1/s) pairs come in through one 4-byte-per-lane load of an interleaved
-//     table and reach SGPRs with v_readlane (scalar loads would share lgkmcnt with LDS and
-//     turn every fragment wait into a full drain);
-//   * step c issues the 32 matrix instructions of chunk c one by one, and behind each the
-//     VALU work of quantizing chunk c+1 (one element every other MFMA), the prefetch loads
-//     of chunk c+3 and the second-half fragment reads; sched_barrier pins that order so the
-//     matrix core, the VALU and the memory pipes run concurrently on each SIMD.
-// Measured on the 4096^3 layer, the vector-memory address path is the scarce resource, so
-// every wave issues 12 vector loads per chunk (8 X DMA, 2 W, 1 group range, 1 scale pair),
-// spread one per two matrix instructions.
+// Same tile and arithmetic as above, software-pipelined so that every step is a run of 32
+// back-to-back matrix instructions with the other work of the step issued between them.
+// Step c (one chunk of 32 input channels) issues the MFMAs of chunk c and, between them:
+//   * the quantization of chunk c+2 into E stage (c+2) % 3: wave w quantizes E rows
+//     32w .. 32w+31, lane l rows 32w + l/4 and 32w + 16 + l/4, channels 8 (l%4) .. +7, from
+//     W words loaded two steps earlier, the group ranges of its two rows and the chunk's
+//     (s, 1/s) pairs, read from a per-group table in LDS;
+//   * the fragment reads of chunk c's second K-half, then of chunk c+1's first K-half, so the
+//     next step starts its matrix work without waiting on LDS;
+//   * the vector loads of chunk c+4's W words and the global -> LDS DMA (buffer_load ... lds)
+//     of chunk c+3's X rows; once per group (every 4th step) the next group's ranges and its
+//     (s, 1/s) table.
+// The vector-memory address path is the scarce resource of this kernel: an instruction costs
+// in proportion to the 128-byte lines it touches, and a line-sized 16-row x 64-byte pattern
+// moves about 3.5x the bytes per cycle of a 64-row x 16-byte gather.  So every load here is
+// rows of 64 contiguous bytes (four lanes per row), ranges and scale pairs are fetched once
+// per group, and no scale is loaded per element.
+// Each wave DMAs only the 128 X rows it multiplies, so X needs no barrier: a wave reads its
+// rows once its own vmcnt says they landed.  E is shared by the four waves; the one barrier
+// per step, after every wave stored its part of E for chunk c+2, makes E of chunk c+1 (stored
+// a step earlier) readable during step c.  X stages are four distinct LDS objects with a
+// static role per unrolled step (the compiler's wait counters for the DMA stay exact); the
+// three E stages are addressed at run time.
 // LDS tiles are unpadded [rows][32 bf16] with the four 16-byte slots of a row permuted by
 // swz(row) = (row >> 2) & 3; with it the 32-row MFMA fragment reads (ds_read_b128) measure
 // zero bank-conflict cycles on gfx950, where unswizzled 64-byte rows cost 12 per read.
-// The loop is unrolled by 4 (4 X stages, 2 E stages, 4 register sets) so every stage is a
-// distinct LDS object and the compiler's wait counters stay exact.  Each wave waits for its
-// own chunk-(c+1) DMA before the barrier that ends step c, so after the barrier every wave
-// may read rows that other waves fetched.
 #define AWQ_LDS __attribute__((address_space(3)))
 
 constexpr int PKC = 32;            // input channels per chunk
 constexpr int PROW = PKC * 2;      // bytes per LDS row
 constexpr int XSTAGE = BM * PROW;  // 32 KiB
 constexpr int ESTAGE = BN * PROW;  // 8 KiB
+constexpr int NES = 3;             // E stages
+constexpr int SRG = kGroup * 8;    // one group's (s, 1/s) pairs: 1 KiB
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 struct WSet {
-  uint4 w[2];   // 8 bf16 channels of rows lane and lane + 64
-  float4 p;     // (Delta, z) of row lane, then of row lane + 64, for this chunk's group
-  float sr;     // lane l holds s (l even) or 1/s (l odd) of channel l / 2 of the chunk
-};
-struct SVal {
-  float s[8];   // wave-uniform (SGPRs, via v_readlane): s of this wave's 8 channels
-  float rs[8];  // 1 / s
+  uint4 w[2];  // this lane's 8 bf16 channels of its rows r0 and r1
 };
 
 struct RowQ {
@@ -342,17 +344,17 @@ struct RowQ {
 
 __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const uint16_t* __restrict__ W,
-    int64_t N, int64_t K, int64_t ldw, const float* __restrict__ s_tab,
-    const float* __restrict__ rs_tab, const float2* __restrict__ sr_tab,
+    int64_t N, int64_t K, int64_t ldw, const float2* __restrict__ sr_tab,
     const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles,
     int64_t per_xcd, double* __restrict__ partial) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs2[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs3[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t es0[ESTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t es1[ESTAGE];
-  __shared__ double red[4];
+  __shared__ __attribute__((aligned(1024))) uint8_t es[NES * ESTAGE];
+  // per-wave copies of one group's scale pairs: even groups in srs0, odd groups in srs1
+  __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * SRG];
+  __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * SRG];
 
   const int64_t b = blockIdx.x;
   const int64_t L = (b & 7) * per_xcd + (b >> 3);
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int al = (int)(L - tile * n_grid);
   const int64_t m0 = (tile / nt_count) * BM;
   const int64_t n0 = (tile % nt_count) * BN;
-  const int64_t G = K / kGroup;
+  const int G = (int)(K / kGroup);
   const int64_t NP = padded_n(N);
   const int nchunks = (int)(K / PKC);
 
@@ -369,32 +371,39 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // X: DMA instruction i of this wave fills LDS rows (4 i + wave) * 16 + lane / 4, slot
-  // lane % 4, with the global piece kp = slot ^ swz(row).  Buffer resources are rebased at
-  // this tile so rows past M (or N) read as zero; offsets stay below 2^31 (host-checked).
+  // X: DMA instruction i of wave w fills LDS rows 128 w + 16 i + lane / 4 (the wave's own
+  // rows), slot lane % 4, with the global piece kp = slot ^ swz(row).  Buffer resources are
+  // rebased at this tile so rows past M (or N) read as zero; offsets stay below 2^31
+  // (host-checked).
   const int64_t xbytes = (M - m0) * ldx * 2, wbytes = (N - n0) * ldw * 2;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + n0 * ldw), (short)0, (int)(wbytes < 0x7fffffff ? wbytes : 0x7fffffff), 0x00020000);
+  // this candidate's (s, 1/s) pairs: K float2 = 8 K bytes (< 2^24: K <= ldx < 2^21 follows
+  // from the host check on 512 rows of X)
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sr_tab + (int64_t)al * K), (short)0, (int)(K * 8), 0x00020000);
   uint32_t xoff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = (4 * i + wave) * 16 + (lane >> 2);
+    const int row = wave * WAVE_ROWS + 16 * i + (lane >> 2);
     const int kp = (lane & 3) ^ swz(row);
     xoff[i] = (uint32_t)(row * ldx * 2 + kp * 16);
   }
-  // W side: this wave's piece is channels 8 wave .. 8 wave + 7 of each chunk
-  const uint32_t woff0 = (uint32_t)(lane * ldw * 2 + wave * 16);
-  const uint32_t woff1 = (uint32_t)((lane + 64) * ldw * 2 + wave * 16);
-  const int eslot0 = lane * PROW + ((wave ^ swz(lane)) * 16);
-  const int eslot1 = (lane + 64) * PROW + ((wave ^ swz(lane + 64)) * 16);
-  const bool live0 = n0 + lane < N, live1 = n0 + lane + 64 < N;
-  const float* srbase = reinterpret_cast<const float*>(sr_tab) + (int64_t)al * K * 2 + lane;
-  // ranges of rows lane and lane + 64 are adjacent (range_slot); rows past N are masked
-  const float4* pbase = reinterpret_cast<const float4*>(params + (int64_t)al * G * NP + n0 + 2 * lane);
+  // quantization: rows r0, r1 of the E tile, channel piece q4 of each chunk
+  const int q4 = lane & 3;
+  const int r0 = wave * 32 + (lane >> 2), r1 = r0 + 16;
+  const uint32_t woff0 = (uint32_t)(r0 * ldw * 2 + q4 * 16);
+  const uint32_t woff1 = (uint32_t)(r1 * ldw * 2 + q4 * 16);
+  const int eslot0 = r0 * PROW + ((q4 ^ swz(r0)) * 16);
+  const int eslot1 = r1 * PROW + ((q4 ^ swz(r1)) * 16);
+  const bool live0 = n0 + r0 < N, live1 = n0 + r1 < N;
+  // ranges of rows r0 and r1 are adjacent (range_slot); rows past N are masked
+  const float4* pbase = reinterpret_cast<const float4*>(params + (int64_t)al * G * NP + n0 + 32 * wave + 2 * (lane >> 2));
+  const int64_t pstride = NP / 2;  // float4 per group
 
-  // fragment reads: lane reads row (... + fr), slot (2 j + fh) ^ swz(fr)
+  // fragment reads: lane reads row (32 t + fr), slot (2 h + fh) ^ swz(fr) for K-half h
   const int fr = lane & 31, fh = lane >> 5;
   const int fsw = swz(fr);
   const int foff0 = fr * PROW + (((0 + fh) ^ fsw) * 16);
@@ -402,54 +411,49 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int xwave = wave * WAVE_ROWS * PROW;
 
   auto dma_x_one = [&](uint8_t* stage, int i, uint32_t kb) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(stage + (4 * i + wave) * 1024), 16,
-                                             (int)(xoff[i] + kb), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xrsrc, (AWQ_LDS void*)(stage + xwave + i * 1024), 16, (int)xoff[i], (int)kb, 0, 0);
   };
-  auto load_w0 = [&](WSet& S, uint32_t kb) {
-    S.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(woff0 + kb), 0, 0));
-  };
-  auto load_w1 = [&](WSet& S, uint32_t kb) {
-    S.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(woff1 + kb), 0, 0));
-  };
-  auto load_p = [&](WSet& S, int k0) { S.p = pbase[(int64_t)(k0 / kGroup) * (NP / 2)]; };
-  auto load_sr = [&](WSet& S, int k0) { S.sr = srbase[2 * k0]; };
-  auto get_s = [&](const WSet& S) {
-    SVal v;
+  auto load_x = [&](uint8_t* stage, int c) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v.s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.sr), 16 * wave + 2 * j));
-      v.rs[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.sr), 16 * wave + 2 * j + 1));
-    }
-    return v;
+    for (int i = 0; i < 8; ++i) dma_x_one(stage, i, (uint32_t)c * (PKC * 2));
   };
-  auto load_all = [&](WSet& S, uint8_t* stage, int c) {
-    const uint32_t kb = (uint32_t)c * (PKC * 2);
-    load_sr(S, c * PKC);
-    load_w0(S, kb);
-    load_w1(S, kb);
-    load_p(S, c * PKC);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma_x_one(stage, i, kb);
+  auto load_w = [&](WSet& S, int i, int c) {
+    S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           wrsrc, (int)(i == 0 ? woff0 : woff1), c * (PKC * 2), 0));
   };
-  auto row_setup = [&](const WSet& S, int i) {
+  auto load_p = [&](int g) { return pbase[(int64_t)g * pstride]; };
+  // each wave copies group g's 1 KiB of pairs into its own slot of table (g even: srs0), one
+  // 16-byte-per-lane DMA (a 4-byte DMA costs several times more per instruction)
+  auto dma_sr = [&](uint8_t* table, int g) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (AWQ_LDS void*)(table + SRG * wave), 16, 16 * lane,
+                                             g * SRG, 0, 0);
+  };
+  // (s, 1/s) of channels 8 q4 .. 8 q4 + 7 of chunk c: four float4 (s_2t, rs_2t, s_2t+1, rs_2t+1)
+  auto sr_addr = [&](const uint8_t* table, int c) {
+    return table + SRG * wave + (32 * (c & 3) + 8 * q4) * 8;
+  };
+  auto row_setup = [&](const float4& P, int i) {
     const bool live = i == 0 ? live0 : live1;
     RowQ q;
-    q.delta = live ? (i == 0 ? S.p.x : S.p.z) : 1.0f;  // rows past N: Delta 1, z 0, w 0: e = 0
-    const float z = live ? (i == 0 ? S.p.y : S.p.w) : 0.0f;
+    q.delta = live ? (i == 0 ? P.x : P.z) : 1.0f;  // rows past N: Delta 1, z 0, w 0: e = 0
+    const float z = live ? (i == 0 ? P.y : P.w) : 0.0f;
     q.inv = __builtin_amdgcn_rcpf(q.delta);  // search only; the pack divides exactly
     q.lo = -z;
     q.hi = 15.0f - z;
     return q;
   };
   // e = w - Delta (q - z) / s for channel j (0..7) of row i (0/1)
-  auto elem = [&](const WSet& S, const SVal& T, const RowQ& q, int i, int j) {
+  auto elem = [&](const WSet& S, const float4* sv, const RowQ& q, int i, int j) {
     const uint4& w4 = S.w[i];
     const uint32_t u = j < 2 ? w4.x : j < 4 ? w4.y : j < 6 ? w4.z : w4.w;
     const float w = (j & 1) ? bf16_hi(u) : bf16_lo(u);
-    const float v = w * T.s[j];                               // S W
+    const float s = (j & 1) ? sv[j >> 1].z : sv[j >> 1].x;
+    const float rs = (j & 1) ? sv[j >> 1].w : sv[j >> 1].y;
+    const float v = w * s;                                    // S W
     const float r = rintf(v * q.inv);                         // rne(v / Delta)
     const float qz = __builtin_amdgcn_fmed3f(r, q.lo, q.hi);  // clamp(r + z, 0, 15) - z
-    return fmaf(-(qz * q.delta), T.rs[j], w);                 // w - Delta (q - z) / s
+    return fmaf(-(qz * q.delta), rs, w);                      // w - Delta (q - z) / s
   };
   auto store_piece = [&](uint8_t* estage, int slot, const float* e8) {
     uint32_t pk[4];
@@ -457,7 +461,26 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     for (int h = 0; h < 4; ++h) pk[h] = pack_bf16x2(e8[2 * h], e8[2 * h + 1]);
     *reinterpret_cast<uint4*>(estage + slot) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   };
+  auto quantize_all = [&](const WSet& S, const float4& P, int c, uint8_t* estage) {  // prologue only
+    float4 sv[4];
+    const uint8_t* sa = sr_addr(srs0, c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
+    const RowQ q0 = row_setup(P, 0), q1 = row_setup(P, 1);
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, sv, q0, 0, j);
+    store_piece(estage, eslot0, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, sv, q1, 1, j);
+    store_piece(estage, eslot1, e);
+  };
   auto frag = [&](const uint8_t* base, int fo) { return *reinterpret_cast<const bf16x8*>(base + fo); };
+  auto vm_wait = [](auto n) {  // s_waitcnt vmcnt(n), other counters untouched
+    constexpr int v = decltype(n)::value;
+    __builtin_amdgcn_s_waitcnt((v & 0xf) | (0x7 << 4) | (0xf << 8) | ((v >> 4) << 14));
+  };
+  constexpr int kWaitLgkm0 = 0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -467,59 +490,95 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
 
-  // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
-  // lgkmcnt[11:8] | vmcnt[5:4] at [15:14]); n = 24 = vector loads issued by two steps.
-  constexpr int kLoadsPerStep = 1 + 2 + 1 + 8;
-  constexpr int kPending = 2 * kLoadsPerStep;
-  constexpr int kWaitVm = (kPending & 0xf) | (0x7 << 4) | (0xf << 8) | ((kPending >> 4) << 14);
-  constexpr int kWaitLgkm0 = 0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
-
-  WSet S0, S1, S2, S3;  // three chunks ahead
-  // Prologue: chunks 0, 1 and 2 in flight (the X DMA last in each), chunk 0 quantized into
-  // E stage 0.  Every step c then issues the 12 vector loads of chunk c+3, X DMA last, so at
-  // the end of step c vmcnt(24) means this wave's X DMA of chunk c+1 has landed.
-  load_all(S0, xs0, 0);
-  load_all(S1, xs1, 1);
-  load_all(S2, xs2, 2);
-  {
-    float e[8];
-    const SVal T0 = get_s(S0);
-    const RowQ q0 = row_setup(S0, 0), q1 = row_setup(S0, 1);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = elem(S0, T0, q0, 0, j);
-    store_piece(es0, eslot0, e);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = elem(S0, T0, q1, 1, j);
-    store_piece(es0, eslot1, e);
-  }
+  WSet S0, S1, S2, S3;  // W words of chunk c live in set c % 4
+  float4 PC, PN;        // ranges of the group being quantized, of the next group
+  // Prologue (once per block): group 0's scale table and ranges, W of chunks 0-3 and X of
+  // chunks 0-2, in the order the steady state expects for chunks 2, 3 and X 1, 2.
+  dma_sr(srs0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm);
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  PC = load_p(0);
+  load_w(S0, 0, 0);
+  load_w(S0, 1, 0);
+  load_w(S1, 0, 1);
+  load_w(S1, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(xs0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(S2, 0, 2);
+  load_w(S2, 1, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(xs1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(S3, 0, 3);
+  load_w(S3, 1, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(xs2, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  // the scale table DMA, the ranges and W of chunks 0, 1 landed (28 loads follow them)
+  vm_wait(std::integral_constant<int, 28>{});
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-
-  // One pipeline step, hand-scheduled in 32 groups, one per matrix instruction of chunk c.
-  // Group g: MFMA g; in odd groups one element of the quantization of chunk c+1; in groups
-  // 0-7 one second-half fragment read; in even groups 0-22 one prefetch load of chunk c+3
-  // (scales, W words, group ranges, then the 8 X DMA), so no group carries more than one
-  // vector-memory instruction behind its 32-cycle MFMA.
-  auto step = [&](int c, const uint8_t* xc, uint8_t* xn, const uint8_t* ec, uint8_t* en,
-                  const WSet& next, WSet& fill) {
-    const int cp = c + 3 < nchunks ? c + 3 : nchunks - 1;  // past the end: harmless reload
-    const uint32_t kb = (uint32_t)cp * (PKC * 2);
-    const int k0 = cp * PKC;
-    const uint8_t* xw = xc + xwave;
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
+  quantize_all(S0, PC, 0, es + 0 * ESTAGE);
+  quantize_all(S1, PC, 1, es + 1 * ESTAGE);
+  bf16x8 a0[4], b0[4];
+  {
+    // wait for everything but the X DMA of chunk 2 (once per block)
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait(std::integral_constant<int, 8>{});
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      a0[t] = frag(xw + t * 32 * PROW, foff0);
-      b0[t] = frag(ec + t * 32 * PROW, foff0);
+      a0[t] = frag(xs0 + xwave + t * 32 * PROW, foff0);
+      b0[t] = frag(es + t * 32 * PROW, foff0);
     }
-    const SVal tv = get_s(next);
-    const RowQ q0 = row_setup(next, 0);
-    const RowQ q1 = row_setup(next, 1);
-    __builtin_amdgcn_sched_barrier(0);
+    // Consume the W words of chunks 2 and 3 here (one wait, once per block): left unused
+    // before the loop, their loads would be sunk to the loop entry, and the loop head would
+    // then wait for them on every iteration.
+    auto consume = [](const WSet& S) {
+      asm volatile("" ::"v"(S.w[0].x), "v"(S.w[0].y), "v"(S.w[0].z), "v"(S.w[0].w), "v"(S.w[1].x),
+                   "v"(S.w[1].y), "v"(S.w[1].z), "v"(S.w[1].w));
+    };
+    consume(S2);
+    consume(S3);
+  }
+
+  // One pipeline step, hand-scheduled in 32 groups, one per matrix instruction of chunk c
+  // (k = c % 4, known at compile time):
+  //   groups 0-7:  second-half fragment reads of chunk c (A even, B odd groups);
+  //   group 0:     the (s, 1/s) pairs and row ranges for the quantization of chunk c+2;
+  //   groups 3-25, two of every three: its sixteen elements; E stores in groups 14 and 26, so
+  //   the last one lands well before the end-of-step wait;
+  //   groups 16-23: first-half fragment reads of chunk c+1;
+  //   vector-memory slots (below): W words of chunk c+4, X DMA of chunk c+3, and when k = 0
+  //   the next group's scale table and ranges.
+  // vmcnt accounting (loads per step: 2 W + 8 X, plus 2 when k = 0): at the start, W of chunk
+  // c+2 (groups 0 and 6 of step c-2) is followed by at least 7 + 10 loads; in group 16, this
+  // wave's X of chunk c+1 (group 28 of step c-2) by at least 10 + 5.
+  auto step = [&](int c, auto kc, const uint8_t* xc, const uint8_t* xn, uint8_t* xd, const WSet& Q,
+                  WSet& F, const uint8_t* srq, uint8_t* srn) {
+    constexpr int k = decltype(kc)::value;
+    const int cw = c + 4 < nchunks ? c + 4 : nchunks - 1;  // past the end: harmless reload
+    const int cx = c + 3 < nchunks ? c + 3 : nchunks - 1;
+    const int gn = (c >> 2) + 1 < G ? (c >> 2) + 1 : G - 1;
+    const uint32_t kbx = (uint32_t)cx * (PKC * 2);
+    const int e_c = c % NES;
+    const int e_n = e_c + 1 == NES ? 0 : e_c + 1;
+    const int e_q = e_n + 1 == NES ? 0 : e_n + 1;
+    const uint8_t* ec = es + e_c * ESTAGE;
+    const uint8_t* en = es + e_n * ESTAGE;
+    uint8_t* eq = es + e_q * ESTAGE;
+    const uint8_t* sa = sr_addr(srq, c + 2);
+    const uint8_t* xw = xc + xwave;
+    const uint8_t* xnw = xn + xwave;
+    if (k == 2) PC = PN;  // chunks c+2 .. c+5 of this quad after the first two: next group
+    bf16x8 a1[4], b1[4];
+    float4 sv[4];
+    RowQ q0, q1;
     float e[16];
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait(std::integral_constant<int, 17>{});  // W of chunk c+2 landed
 #pragma unroll
     for (int g = 0; g < 32; ++g) {
       const int r = (g >> 2) & 3, cc = g & 3;
@@ -527,10 +586,11 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
         acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[r], b0[cc], acc[r][cc], 0, 0, 0);
       else
         acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[r], b1[cc], acc[r][cc], 0, 0, 0);
-      if (g & 1) {
-        const int el = g >> 1;
-        e[el] = el < 8 ? elem(next, tv, q0, 0, el) : elem(next, tv, q1, 1, el - 8);
-        asm volatile("" : "+v"(e[el]));  // keep the element in this group (no IR sinking)
+      if (g == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
+        q0 = row_setup(PC, 0);
+        q1 = row_setup(PC, 1);
       }
       if (g < 8) {
         if (g & 1)
@@ -538,37 +598,64 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
         else
           a1[g >> 1] = frag(xw + (g >> 1) * 32 * PROW, foff1);
       }
-      if (g == 0) {
-        load_sr(fill, k0);
-      } else if (g == 2) {
-        load_w0(fill, kb);
-      } else if (g == 4) {
-        load_w1(fill, kb);
-      } else if (g == 6) {
-        load_p(fill, k0);
-      } else if (g >= 8 && g <= 22 && (g & 1) == 0) {
-        dma_x_one(xn, (g - 8) >> 1, kb);
-      } else if (g == 17) {
-        store_piece(en, eslot0, e);
+      // element el in group 3 + 3 (el / 2) + el % 2: groups 3-13 for row r0, 15-25 for r1
+      const int el = g >= 3 && g <= 25 && (g - 3) % 3 != 2 ? 2 * ((g - 3) / 3) + (g - 3) % 3 : -1;
+      if (el >= 0) {
+        e[el] = el < 8 ? elem(Q, sv, q0, 0, el) : elem(Q, sv, q1, 1, el - 8);
+        asm volatile("" : "+v"(e[el]));  // keep the element in this group (no IR sinking)
       }
+      if (g == 14) store_piece(eq, eslot0, e);
+      if (g == 26) store_piece(eq, eslot1, e + 8);
+      if (g == 16) vm_wait(std::integral_constant<int, 15>{});  // this wave's X of chunk c+1 landed
+      if (g >= 16 && g < 24) {
+        if (g & 1)
+          b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * PROW, foff0);
+        else
+          a0[(g - 16) >> 1] = frag(xnw + ((g - 16) >> 1) * 32 * PROW, foff0);
+      }
+      // vector-memory slots, spread over the step (bursts back up the address path and stall
+      // the issuing wave): W words in groups 0 and 6, X DMA in 3, 9, 12, 16, 19, 22, 25, 28,
+      // and when k = 0 the ranges in 1 and the scale table DMA in 14
+      if (g == 0) load_w(F, 0, cw);
+      if (g == 6) load_w(F, 1, cw);
+      if (g == 3 || g == 9 || g == 12) dma_x_one(xd, g == 3 ? 0 : g == 9 ? 1 : 2, kbx);
+      if (g >= 16 && g <= 28 && (g - 16) % 3 == 0) dma_x_one(xd, 3 + (g - 16) / 3, kbx);
+      if (k == 0 && g == 1) PN = load_p(gn);
+      if (k == 0 && g == 14) dma_sr(srn, gn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_piece(en, eslot1, e + 8);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm);  // this wave's chunk c+1 loads (X DMA too) landed
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    // k = 1: this wave's scale table DMA of step k = 0 (followed by 5 + 10 loads) has landed
+    if (k == 1) vm_wait(std::integral_constant<int, 15>{});
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // E stores of chunk c+2, fragment reads
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // nchunks = K / 32 is a multiple of 4 (K is a multiple of 128).  Step c reads X stage
-  // c % 4 and E stage c % 2, quantizes register set (c+1) % 4 into E stage (c+1) % 2 and
-  // fills register set (c+3) % 4 and X stage (c+3) % 4 (last read in step c-1).
-  for (int c = 0; c < nchunks; c += 4) {
-    step(c + 0, xs0, xs3, es0, es1, S1, S3);
-    step(c + 1, xs1, xs0, es1, es0, S2, S0);
-    step(c + 2, xs2, xs1, es0, es1, S3, S1);
-    step(c + 3, xs3, xs2, es1, es0, S0, S2);
+  // nchunks = K / 32 is a multiple of 4 (K is a multiple of 128).  Step c multiplies chunk c
+  // from X stage c % 4, prefetches chunk c+1's first half from X stage (c+1) % 4, quantizes W
+  // set (c+2) % 4, DMAs chunk c+3 into X stage (c+3) % 4 and loads chunk c+4's W words into
+  // set c % 4.  The body covers two groups (8 steps) so that each scale table is a distinct
+  // LDS object in a static role: reads of one table never wait for the DMA into the other.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    step(c + 0, I0{}, xs0, xs1, xs3, S2, S0, srs0, srs1);
+    step(c + 1, I1{}, xs1, xs2, xs0, S3, S1, srs0, srs1);
+    step(c + 2, I2{}, xs2, xs3, xs1, S0, S2, srs1, srs1);
+    step(c + 3, I3{}, xs3, xs0, xs2, S1, S3, srs1, srs1);
+    step(c + 4, I0{}, xs0, xs1, xs3, S2, S0, srs1, srs0);
+    step(c + 5, I1{}, xs1, xs2, xs0, S3, S1, srs1, srs0);
+    step(c + 6, I2{}, xs2, xs3, xs1, S0, S2, srs0, srs0);
+    step(c + 7, I3{}, xs3, xs0, xs2, S1, S3, srs0, srs0);
+  }
+  if (c < nchunks) {  // K / 128 odd: one more group
+    step(c + 0, I0{}, xs0, xs1, xs3, S2, S0, srs0, srs1);
+    step(c + 1, I1{}, xs1, xs2, xs0, S3, S1, srs0, srs1);
+    step(c + 2, I2{}, xs2, xs3, xs1, S0, S2, srs1, srs1);
+    step(c + 3, I3{}, xs3, xs0, xs2, S1, S3, srs1, srs1);
   }
 
   double ss = 0.0;
@@ -583,6 +670,9 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  // every wave is past its last LDS access (the barrier ending the last step), so the first
+  // E stage can hold the four wave sums
+  double* red = reinterpret_cast<double*>(es);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   if (tid == 0) partial[(int64_t)al * tiles + tile] = ((red[0] + red[1]) + red[2]) + red[3];
@@ -613,8 +703,8 @@ hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx,
                                                         per_xcd, partial)
   if (!xf32 && !wf32) {
     search_pipelined_kernel<<<grid, THREADS, 0, st>>>(
-        static_cast<const uint16_t*>(X), M, ldx, static_cast<const uint16_t*>(W), N, K, ldw, s_tab,
-        rs_tab, sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
+        static_cast<const uint16_t*>(X), M, ldx, static_cast<const uint16_t*>(W), N, K, ldw, sr_tab,
+        params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
     return hipGetLastError();
   }
   if (xf32 && wf32)
