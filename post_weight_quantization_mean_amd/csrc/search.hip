@@ -304,35 +304,40 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
 //     32w .. 32w+31, lane l rows 32w + l/4 and 32w + 16 + l/4, channels 8 (l%4) .. +7, from
 //     W words loaded two steps earlier, the group ranges of its two rows and the chunk's
 //     (s, 1/s) pairs, read from a per-group table in LDS;
-//   * the fragment reads of chunk c's second K-half, then of chunk c+1's first K-half, so the
-//     next step starts its matrix work without waiting on LDS;
-//   * the vector loads of chunk c+4's W words and the global -> LDS DMA (buffer_load ... lds)
-//     of chunk c+3's X rows; once per group (every 4th step) the next group's ranges and its
-//     (s, 1/s) table.
-// The vector-memory address path is the scarce resource of this kernel: an instruction costs
-// in proportion to the 128-byte lines it touches, and a line-sized 16-row x 64-byte pattern
-// moves about 3.5x the bytes per cycle of a 64-row x 16-byte gather.  So every load here is
-// rows of 64 contiguous bytes (four lanes per row), ranges and scale pairs are fetched once
-// per group, and no scale is loaded per element.
+//   * the fragment reads of chunk c's second K-half, chunk c+1's B fragments of the first
+//     K-half, and the first two (of four) A fragments of chunk c+1; the other two are read as
+//     step c+1 starts and first used eight matrix instructions later;
+//   * the vector-memory traffic for later steps (below).
+// X lives in LDS as pair stages: 2 chunks (64 channels, a full 128-byte line of a row) per
+// stage, two stages.  The global -> LDS DMA (buffer_load ... lds) of a pair moves 8 rows x
+// 128 bytes per instruction: an instruction that fills whole lines costs the vector-memory
+// address path about 1.5x fewer cycles per byte than one that fills 64-byte halves (measured),
+// and every line crosses from L2 once.  Pair p+1 (chunks 2p+2, 2p+3) is DMA'd during steps
+// 2p (this wave's rows 0-63) and 2p+1 (rows 64-127), into the stage pair p-1 used.  Even steps
+// also load the W words of chunks c+4 and c+5 (the two 64-byte halves of the same lines, back
+// to back, so the second is an L1 hit); when c % 4 = 0, the next group's ranges and its
+// (s, 1/s) table.
 // Each wave DMAs only the 128 X rows it multiplies, so X needs no barrier: a wave reads its
 // rows once its own vmcnt says they landed.  E is shared by the four waves; the one barrier
 // per step, after every wave stored its part of E for chunk c+2, makes E of chunk c+1 (stored
-// a step earlier) readable during step c.  X stages are four distinct LDS objects with a
-// static role per unrolled step (the compiler's wait counters for the DMA stay exact); the
-// three E stages are addressed at run time.
-// LDS tiles are unpadded [rows][32 bf16] with the four 16-byte slots of a row permuted by
-// swz(row) = (row >> 2) & 3; with it the 32-row MFMA fragment reads (ds_read_b128) measure
-// zero bank-conflict cycles on gfx950, where unswizzled 64-byte rows cost 12 per read.
+// a step earlier) readable during step c.  X stages are distinct LDS objects with a static role
+// per unrolled step (the compiler's wait counters for the DMA stay exact); the three E stages
+// are addressed at run time.
+// LDS rows are unpadded with their 16-byte slots permuted: X pair rows (128 bytes, 8 slots)
+// by (row >> 1) & 7, E rows (64 bytes, 4 slots) by (row >> 2) & 3.  With them the 32-row MFMA
+// fragment reads (ds_read_b128) are free of bank conflicts on gfx950.
 #define AWQ_LDS __attribute__((address_space(3)))
 
-constexpr int PKC = 32;            // input channels per chunk
-constexpr int PROW = PKC * 2;      // bytes per LDS row
-constexpr int XSTAGE = BM * PROW;  // 32 KiB
-constexpr int ESTAGE = BN * PROW;  // 8 KiB
-constexpr int NES = 3;             // E stages
-constexpr int SRG = kGroup * 8;    // one group's (s, 1/s) pairs: 1 KiB
+constexpr int PKC = 32;                // input channels per chunk
+constexpr int PROW = PKC * 2;          // bytes per E row
+constexpr int XROW = 2 * PROW;         // bytes per X pair row (two chunks)
+constexpr int XPSTAGE = BM * XROW;     // 64 KiB
+constexpr int ESTAGE = BN * PROW;      // 8 KiB
+constexpr int NES = 3;                 // E stages
+constexpr int SRG = kGroup * 8;        // one group's (s, 1/s) pairs: 1 KiB
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int xswz(int row) { return (row >> 1) & 7; }
 
 struct WSet {
   uint4 w[2];  // this lane's 8 bf16 channels of its rows r0 and r1
@@ -347,10 +352,13 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     int64_t N, int64_t K, int64_t ldw, const float2* __restrict__ sr_tab,
     const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles,
     int64_t per_xcd, double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs1[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs2[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs3[XSTAGE];
+  // X pair stages (pairs 0, 2, 4, ... in xp0; 1, 3, 5, ... in xp1), each split into the first
+  // and the last 64 of every wave's 128 rows: distinct LDS objects, so reads of one half never
+  // wait for the DMA into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[XPSTAGE / 2];
   __shared__ __attribute__((aligned(1024))) uint8_t es[NES * ESTAGE];
   // per-wave copies of one group's scale pairs: even groups in srs0, odd groups in srs1
   __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * SRG];
@@ -366,15 +374,14 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int G = (int)(K / kGroup);
   const int64_t NP = padded_n(N);
   const int nchunks = (int)(K / PKC);
+  const int npairs = nchunks / 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // X: DMA instruction i of wave w fills LDS rows 128 w + 16 i + lane / 4 (the wave's own
-  // rows), slot lane % 4, with the global piece kp = slot ^ swz(row).  Buffer resources are
-  // rebased at this tile so rows past M (or N) read as zero; offsets stay below 2^31
-  // (host-checked).
+  // Buffer resources are rebased at this tile so rows past M (or N) read as zero; offsets
+  // stay below 2^31 (host-checked: 512 rows of X, 128 rows of W).
   const int64_t xbytes = (M - m0) * ldx * 2, wbytes = (N - n0) * ldw * 2;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
@@ -384,13 +391,16 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   // from the host check on 512 rows of X)
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(sr_tab + (int64_t)al * K), (short)0, (int)(K * 8), 0x00020000);
-  uint32_t xoff[8];
+  // X DMA instruction i (0..15) of wave w fills pair rows 128 w + 8 i + lane / 8, slot lane % 8,
+  // with the global 16-byte piece slot ^ xswz(row).  xswz depends on i only through i % 2, so
+  // two lane offsets serve all sixteen; the rest of the row offset goes in soffset.
+  uint32_t xoff[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = wave * WAVE_ROWS + 16 * i + (lane >> 2);
-    const int kp = (lane & 3) ^ swz(row);
-    xoff[i] = (uint32_t)(row * ldx * 2 + kp * 16);
+  for (int i = 0; i < 2; ++i) {
+    const int row = wave * WAVE_ROWS + 8 * i + (lane >> 3);
+    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 7) ^ xswz(row)) * 16));
   }
+  const uint32_t xrow16 = (uint32_t)(16 * ldx * 2);  // 16 rows of X, bytes
   // quantization: rows r0, r1 of the E tile, channel piece q4 of each chunk
   const int q4 = lane & 3;
   const int r0 = wave * 32 + (lane >> 2), r1 = r0 + 16;
@@ -403,20 +413,19 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const float4* pbase = reinterpret_cast<const float4*>(params + (int64_t)al * G * NP + n0 + 32 * wave + 2 * (lane >> 2));
   const int64_t pstride = NP / 2;  // float4 per group
 
-  // fragment reads: lane reads row (32 t + fr), slot (2 h + fh) ^ swz(fr) for K-half h
+  // fragment reads: lane reads row (32 t + fr), 16-byte piece 2 h + fh of K-half h of its chunk
   const int fr = lane & 31, fh = lane >> 5;
-  const int fsw = swz(fr);
-  const int foff0 = fr * PROW + (((0 + fh) ^ fsw) * 16);
-  const int foff1 = fr * PROW + (((2 + fh) ^ fsw) * 16);
-  const int xwave = wave * WAVE_ROWS * PROW;
+  const int efoff0 = fr * PROW + (((0 + fh) ^ swz(fr)) * 16);
+  const int efoff1 = fr * PROW + (((2 + fh) ^ swz(fr)) * 16);
+  // in an X pair row the chunk's pieces are 4 (c % 2) + 2 h + fh
+  auto xfoff = [&](int half, int h) { return fr * XROW + (((4 * half + 2 * h + fh) ^ xswz(fr)) * 16); };
+  const int xwave = wave * (WAVE_ROWS / 2) * XROW;  // this wave's 64 rows in a half stage
 
-  auto dma_x_one = [&](uint8_t* stage, int i, uint32_t kb) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        xrsrc, (AWQ_LDS void*)(stage + xwave + i * 1024), 16, (int)xoff[i], (int)kb, 0, 0);
-  };
-  auto load_x = [&](uint8_t* stage, int c) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma_x_one(stage, i, (uint32_t)c * (PKC * 2));
+  // DMA instruction i of pair p into half stage xh (i < 8: the wave's rows 0-63, else 64-127)
+  auto dma_x_one = [&](uint8_t* xh, int i, int p) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(xh + xwave + (i & 7) * 1024), 16,
+                                             (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * XROW),
+                                             0, 0);
   };
   auto load_w = [&](WSet& S, int i, int c) {
     S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -492,50 +501,40 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
 
   WSet S0, S1, S2, S3;  // W words of chunk c live in set c % 4
   float4 PC, PN;        // ranges of the group being quantized, of the next group
-  // Prologue (once per block): group 0's scale table and ranges, W of chunks 0-3 and X of
-  // chunks 0-2, in the order the steady state expects for chunks 2, 3 and X 1, 2.
+  // Prologue (once per block): group 0's scale table and ranges, W of chunks 0-3 and the X
+  // pair of chunks 0 and 1, then chunks 0 and 1 are quantized.
   dma_sr(srs0, 0);
-  __builtin_amdgcn_sched_barrier(0);
   PC = load_p(0);
   load_w(S0, 0, 0);
-  load_w(S0, 1, 0);
   load_w(S1, 0, 1);
+  load_w(S0, 1, 0);
   load_w(S1, 1, 1);
   __builtin_amdgcn_sched_barrier(0);
-  load_x(xs0, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, 0);
   __builtin_amdgcn_sched_barrier(0);
   load_w(S2, 0, 2);
-  load_w(S2, 1, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  load_x(xs1, 1);
-  __builtin_amdgcn_sched_barrier(0);
   load_w(S3, 0, 3);
+  load_w(S2, 1, 2);
   load_w(S3, 1, 3);
   __builtin_amdgcn_sched_barrier(0);
-  load_x(xs2, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  // the scale table DMA, the ranges and W of chunks 0, 1 landed (28 loads follow them)
-  vm_wait(std::integral_constant<int, 28>{});
-  __builtin_amdgcn_s_barrier();
+  vm_wait(std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
   quantize_all(S0, PC, 0, es + 0 * ESTAGE);
   quantize_all(S1, PC, 1, es + 1 * ESTAGE);
   bf16x8 a0[4], b0[4];
   {
-    // wait for everything but the X DMA of chunk 2 (once per block)
     __builtin_amdgcn_sched_barrier(0);
-    vm_wait(std::integral_constant<int, 8>{});
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      a0[t] = frag(xs0 + xwave + t * 32 * PROW, foff0);
-      b0[t] = frag(es + t * 32 * PROW, foff0);
-    }
-    // Consume the W words of chunks 2 and 3 here (one wait, once per block): left unused
-    // before the loop, their loads would be sunk to the loop entry, and the loop head would
-    // then wait for them on every iteration.
+    for (int t = 0; t < 2; ++t) a0[t] = frag(xp0lo + xwave + t * 32 * XROW, xfoff(0, 0));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * PROW, efoff0);
+    // Consume the W words of chunks 2 and 3 here: left unused before the loop, their loads
+    // would be sunk to the loop entry, and the loop head would then wait for them on every
+    // iteration.
     auto consume = [](const WSet& S) {
       asm volatile("" ::"v"(S.w[0].x), "v"(S.w[0].y), "v"(S.w[0].z), "v"(S.w[0].w), "v"(S.w[1].x),
                    "v"(S.w[1].y), "v"(S.w[1].z), "v"(S.w[1].w));
@@ -545,24 +544,31 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   }
 
   // One pipeline step, hand-scheduled in 32 groups, one per matrix instruction of chunk c
-  // (k = c % 4, known at compile time):
+  // (k = c % 4, known at compile time; xc is chunk c's pair stage, xn chunk c+1's):
+  //   groups 0, 1: A fragments 2, 3 of chunk c (first used in groups 8 and 12);
   //   groups 0-7:  second-half fragment reads of chunk c (A even, B odd groups);
   //   group 0:     the (s, 1/s) pairs and row ranges for the quantization of chunk c+2;
-  //   groups 3-25, two of every three: its sixteen elements; E stores in groups 14 and 26, so
-  //   the last one lands well before the end-of-step wait;
-  //   groups 16-23: first-half fragment reads of chunk c+1;
-  //   vector-memory slots (below): W words of chunk c+4, X DMA of chunk c+3, and when k = 0
-  //   the next group's scale table and ranges.
-  // vmcnt accounting (loads per step: 2 W + 8 X, plus 2 when k = 0): at the start, W of chunk
-  // c+2 (groups 0 and 6 of step c-2) is followed by at least 7 + 10 loads; in group 16, this
-  // wave's X of chunk c+1 (group 28 of step c-2) by at least 10 + 5.
-  auto step = [&](int c, auto kc, const uint8_t* xc, const uint8_t* xn, uint8_t* xd, const WSet& Q,
-                  WSet& F, const uint8_t* srq, uint8_t* srn) {
+  //   groups 3-25, two of every three: its sixteen elements; E stores in groups 14 and 26;
+  //   groups 17-23 (odd): chunk c+1's B fragments of the first K-half; groups 24, 25: its A
+  //   fragments 0, 1;
+  //   vector memory (below): even steps W words of chunks c+4 and c+5 (groups 0-3), when k = 0
+  //   the next group's ranges and scale table (4, 5), and X DMA of pair c/2 + 1, rows 0-63
+  //   (groups 6, 9, ..., 27); odd steps the same pair's rows 64-127 (groups 0, 2, ..., 14).
+  // vmcnt accounting (even steps: 4 W + 8 X loads, plus 2 when k = 0; odd steps 8 X):
+  //   * start of an even step: all loads landed (the X rows 64-127 of chunk c, DMA'd by the
+  //     previous step, are read now); start of an odd step: at most the previous step's 12
+  //     outstanding (W of chunk c+2 is from step c-3, chunk c's X from steps c-3, c-2);
+  //   * group 24: chunk c+1's rows 0-63 (from step c-1 at the latest) landed;
+  //   * end of a k = 1 step: this wave's scale table DMA of step k = 0 (followed by 16 X) landed.
+  auto step = [&](int c, auto kc, const uint8_t* xclo, const uint8_t* xchi, const uint8_t* xnlo,
+                  uint8_t* xdlo, uint8_t* xdhi, const WSet& Q, WSet& F4, WSet& F5, const uint8_t* srq,
+                  uint8_t* srn) {
     constexpr int k = decltype(kc)::value;
-    const int cw = c + 4 < nchunks ? c + 4 : nchunks - 1;  // past the end: harmless reload
-    const int cx = c + 3 < nchunks ? c + 3 : nchunks - 1;
+    constexpr bool even = (k & 1) == 0;
+    auto clampc = [&](int q) { return q < nchunks ? q : nchunks - 1; };  // past the end: harmless reload
+    const int cw4 = clampc(c + 4), cw5 = clampc(c + 5);
+    const int pd = (c >> 1) + 1 < npairs ? (c >> 1) + 1 : npairs - 1;   // pair being DMA'd
     const int gn = (c >> 2) + 1 < G ? (c >> 2) + 1 : G - 1;
-    const uint32_t kbx = (uint32_t)cx * (PKC * 2);
     const int e_c = c % NES;
     const int e_n = e_c + 1 == NES ? 0 : e_c + 1;
     const int e_q = e_n + 1 == NES ? 0 : e_n + 1;
@@ -570,15 +576,19 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     const uint8_t* en = es + e_n * ESTAGE;
     uint8_t* eq = es + e_q * ESTAGE;
     const uint8_t* sa = sr_addr(srq, c + 2);
-    const uint8_t* xw = xc + xwave;
-    const uint8_t* xnw = xn + xwave;
+    const uint8_t* xwlo = xclo + xwave;
+    const uint8_t* xwhi = xchi + xwave;
+    const uint8_t* xnw = xnlo + xwave;
+    // A fragment t of chunk c: rows 32 t .. 32 t + 31 of the wave, in the lo (t < 2) or hi half
+    auto xa = [&](int t) { return (t < 2 ? xwlo : xwhi) + (t & 1) * 32 * XROW; };
+    const int xo0 = xfoff(k & 1, 0), xo1 = xfoff(k & 1, 1), xn0 = xfoff((k + 1) & 1, 0);
     if (k == 2) PC = PN;  // chunks c+2 .. c+5 of this quad after the first two: next group
     bf16x8 a1[4], b1[4];
     float4 sv[4];
     RowQ q0, q1;
     float e[16];
     __builtin_amdgcn_sched_barrier(0);
-    vm_wait(std::integral_constant<int, 17>{});  // W of chunk c+2 landed
+    vm_wait(std::integral_constant<int, even ? 0 : 12>{});
 #pragma unroll
     for (int g = 0; g < 32; ++g) {
       const int r = (g >> 2) & 3, cc = g & 3;
@@ -586,6 +596,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
         acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[r], b0[cc], acc[r][cc], 0, 0, 0);
       else
         acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[r], b1[cc], acc[r][cc], 0, 0, 0);
+      if (g < 2) a0[2 + g] = frag(xa(2 + g), xo0);
       if (g == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
@@ -594,9 +605,9 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
       }
       if (g < 8) {
         if (g & 1)
-          b1[g >> 1] = frag(ec + (g >> 1) * 32 * PROW, foff1);
+          b1[g >> 1] = frag(ec + (g >> 1) * 32 * PROW, efoff1);
         else
-          a1[g >> 1] = frag(xw + (g >> 1) * 32 * PROW, foff1);
+          a1[g >> 1] = frag(xa(g >> 1), xo1);
       }
       // element el in group 3 + 3 (el / 2) + el % 2: groups 3-13 for row r0, 15-25 for r1
       const int el = g >= 3 && g <= 25 && (g - 3) % 3 != 2 ? 2 * ((g - 3) / 3) + (g - 3) % 3 : -1;
@@ -606,56 +617,56 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
       }
       if (g == 14) store_piece(eq, eslot0, e);
       if (g == 26) store_piece(eq, eslot1, e + 8);
-      if (g == 16) vm_wait(std::integral_constant<int, 15>{});  // this wave's X of chunk c+1 landed
-      if (g >= 16 && g < 24) {
-        if (g & 1)
-          b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * PROW, foff0);
-        else
-          a0[(g - 16) >> 1] = frag(xnw + ((g - 16) >> 1) * 32 * PROW, foff0);
+      if (g >= 16 && g < 24 && (g & 1)) b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * PROW, efoff0);
+      // chunk c+1's rows 0-63 landed: they come from step c-1 at the latest, followed by this
+      // step's loads before group 24 (even: 4 W, 2 when k = 0, 6 X; odd: 8 X)
+      if (g == 24) vm_wait(std::integral_constant<int, even ? 10 : 8>{});
+      if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * XROW, xn0);
+      if (even) {
+        if (g == 0) load_w(F4, 0, cw4);
+        if (g == 1) load_w(F5, 0, cw5);
+        if (g == 2) load_w(F4, 1, cw4);
+        if (g == 3) load_w(F5, 1, cw5);
+        if (k == 0 && g == 4) PN = load_p(gn);
+        if (k == 0 && g == 5) dma_sr(srn, gn);
+        if (g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(xdlo, (g - 6) / 3, pd);
+      } else {
+        if (g <= 14 && (g & 1) == 0) dma_x_one(xdhi, 8 + g / 2, pd);
       }
-      // vector-memory slots, spread over the step (bursts back up the address path and stall
-      // the issuing wave): W words in groups 0 and 6, X DMA in 3, 9, 12, 16, 19, 22, 25, 28,
-      // and when k = 0 the ranges in 1 and the scale table DMA in 14
-      if (g == 0) load_w(F, 0, cw);
-      if (g == 6) load_w(F, 1, cw);
-      if (g == 3 || g == 9 || g == 12) dma_x_one(xd, g == 3 ? 0 : g == 9 ? 1 : 2, kbx);
-      if (g >= 16 && g <= 28 && (g - 16) % 3 == 0) dma_x_one(xd, 3 + (g - 16) / 3, kbx);
-      if (k == 0 && g == 1) PN = load_p(gn);
-      if (k == 0 && g == 14) dma_sr(srn, gn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // k = 1: this wave's scale table DMA of step k = 0 (followed by 5 + 10 loads) has landed
-    if (k == 1) vm_wait(std::integral_constant<int, 15>{});
+    if (k == 1) vm_wait(std::integral_constant<int, 16>{});  // this wave's scale table landed
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // E stores of chunk c+2, fragment reads
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // nchunks = K / 32 is a multiple of 4 (K is a multiple of 128).  Step c multiplies chunk c
-  // from X stage c % 4, prefetches chunk c+1's first half from X stage (c+1) % 4, quantizes W
-  // set (c+2) % 4, DMAs chunk c+3 into X stage (c+3) % 4 and loads chunk c+4's W words into
-  // set c % 4.  The body covers two groups (8 steps) so that each scale table is a distinct
-  // LDS object in a static role: reads of one table never wait for the DMA into the other.
+  // from pair stage (c / 2) % 2, quantizes W set (c+2) % 4 into E stage (c+2) % 3, DMAs half
+  // of pair c/2 + 1 into stage (c/2 + 1) % 2 (last read by chunk c-1, in step c-1) and, when
+  // even, loads the W words of chunks c+4 and c+5 into sets c % 4 and (c+1) % 4 (quantized in
+  // steps c-2 and c-1).  The body covers two groups (8 steps) so that each scale table and
+  // each X pair stage has a static role: reads of one never wait for the DMA into the other.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   int c = 0;
   for (; c + 8 <= nchunks; c += 8) {
-    step(c + 0, I0{}, xs0, xs1, xs3, S2, S0, srs0, srs1);
-    step(c + 1, I1{}, xs1, xs2, xs0, S3, S1, srs0, srs1);
-    step(c + 2, I2{}, xs2, xs3, xs1, S0, S2, srs1, srs1);
-    step(c + 3, I3{}, xs3, xs0, xs2, S1, S3, srs1, srs1);
-    step(c + 4, I0{}, xs0, xs1, xs3, S2, S0, srs1, srs0);
-    step(c + 5, I1{}, xs1, xs2, xs0, S3, S1, srs1, srs0);
-    step(c + 6, I2{}, xs2, xs3, xs1, S0, S2, srs0, srs0);
-    step(c + 7, I3{}, xs3, xs0, xs2, S1, S3, srs0, srs0);
+    step(c + 0, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1);
+    step(c + 1, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1);
+    step(c + 2, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1);
+    step(c + 3, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1);
+    step(c + 4, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs1, srs0);
+    step(c + 5, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs1, srs0);
+    step(c + 6, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs0, srs0);
+    step(c + 7, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs0, srs0);
   }
   if (c < nchunks) {  // K / 128 odd: one more group
-    step(c + 0, I0{}, xs0, xs1, xs3, S2, S0, srs0, srs1);
-    step(c + 1, I1{}, xs1, xs2, xs0, S3, S1, srs0, srs1);
-    step(c + 2, I2{}, xs2, xs3, xs1, S0, S2, srs1, srs1);
-    step(c + 3, I3{}, xs3, xs0, xs2, S1, S3, srs1, srs1);
+    step(c + 0, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1);
+    step(c + 1, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1);
+    step(c + 2, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1);
+    step(c + 3, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1);
   }
 
   double ss = 0.0;
