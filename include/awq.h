@@ -48,7 +48,9 @@ extern "C" {
 typedef enum {
   AWQ_OK = 0,
   AWQ_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, ld < K, n_grid outside [1, 64] */
-  AWQ_ERR_SHAPE = 2,       /* K not a multiple of the group size, 64-bit size overflow */
+  AWQ_ERR_SHAPE = 2,       /* K not a multiple of the group size, 64-bit size overflow,
+                              awq_search: 512 rows of X, 128 rows of W or one candidate's
+                              group ranges (8 N K / 128 bytes) span 2^31 bytes or more */
   AWQ_ERR_UNSUPPORTED = 3, /* dtype other than F32/BF16, group other than 128 */
   AWQ_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than the size function says */
   AWQ_ERR_HIP = 5          /* a HIP launch or runtime call failed */

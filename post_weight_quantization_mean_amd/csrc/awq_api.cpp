@@ -134,6 +134,8 @@ AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, i
   if (mul_ok(mul_ok(awq::kSearchBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX ||
       mul_ok(mul_ok(awq::kSearchBN, ldw), dsize(w_dtype)) >= (int64_t)INT32_MAX)
     return AWQ_ERR_SHAPE;
+  // one candidate's group ranges (float2 [K/128][Npad]) are addressed with 32-bit offsets
+  if (mul_ok(mul_ok(K / kGroup, awq::padded_n(N)), 8) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
   SearchLayout L;
   if (!search_layout(M, K, N, n_grid, &L)) return AWQ_ERR_SHAPE;
   if (ws == nullptr || ws_bytes < L.total) return AWQ_ERR_WORKSPACE;

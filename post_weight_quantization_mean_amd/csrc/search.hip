@@ -374,7 +374,6 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int G = (int)(K / kGroup);
   const int64_t NP = padded_n(N);
   const int nchunks = (int)(K / PKC);
-  const int npairs = nchunks / 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -409,9 +408,12 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int eslot0 = r0 * PROW + ((q4 ^ swz(r0)) * 16);
   const int eslot1 = r1 * PROW + ((q4 ^ swz(r1)) * 16);
   const bool live0 = n0 + r0 < N, live1 = n0 + r1 < N;
-  // ranges of rows r0 and r1 are adjacent (range_slot); rows past N are masked
-  const float4* pbase = reinterpret_cast<const float4*>(params + (int64_t)al * G * NP + n0 + 32 * wave + 2 * (lane >> 2));
-  const int64_t pstride = NP / 2;  // float4 per group
+  // ranges of rows r0 and r1 are adjacent (range_slot); rows past N are masked.  A buffer
+  // resource over this candidate's ranges (G Npad float2 < 2^31 bytes: host-checked) reads
+  // groups past the end as zero.
+  const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(params + (int64_t)al * G * NP), (short)0, (int)((int64_t)G * NP * 8), 0x00020000);
+  const int poff = (int)((n0 + 32 * wave + 2 * (lane >> 2)) * 8);
 
   // fragment reads: lane reads row (32 t + fr), 16-byte piece 2 h + fh of K-half h of its chunk
   const int fr = lane & 31, fh = lane >> 5;
@@ -427,11 +429,15 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
                                              (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * XROW),
                                              0, 0);
   };
-  auto load_w = [&](WSet& S, int i, int c) {
+  // W words of row i of chunk (cb / 64 + j): the constant part of the offset goes in the
+  // instruction's immediate field; chunks past the end read other bytes of the tile (unused)
+  auto load_w = [&](WSet& S, int i, int cb, int j) {
     S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           wrsrc, (int)(i == 0 ? woff0 : woff1), c * (PKC * 2), 0));
+                                           wrsrc, (int)(i == 0 ? woff0 : woff1) + j * (PKC * 2), cb, 0));
   };
-  auto load_p = [&](int g) { return pbase[(int64_t)g * pstride]; };
+  auto load_p = [&](int g) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prsrc, poff, (int)(g * NP * 8), 0));
+  };
   // each wave copies group g's 1 KiB of pairs into its own slot of table (g even: srs0), one
   // 16-byte-per-lane DMA (a 4-byte DMA costs several times more per instruction)
   auto dma_sr = [&](uint8_t* table, int g) {
@@ -505,18 +511,18 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   // pair of chunks 0 and 1, then chunks 0 and 1 are quantized.
   dma_sr(srs0, 0);
   PC = load_p(0);
-  load_w(S0, 0, 0);
-  load_w(S1, 0, 1);
-  load_w(S0, 1, 0);
-  load_w(S1, 1, 1);
+  load_w(S0, 0, 0, 0);
+  load_w(S1, 0, 0, 1);
+  load_w(S0, 1, 0, 0);
+  load_w(S1, 1, 0, 1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(S2, 0, 2);
-  load_w(S3, 0, 3);
-  load_w(S2, 1, 2);
-  load_w(S3, 1, 3);
+  load_w(S2, 0, 0, 2);
+  load_w(S3, 0, 0, 3);
+  load_w(S2, 1, 0, 2);
+  load_w(S3, 1, 0, 3);
   __builtin_amdgcn_sched_barrier(0);
   vm_wait(std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
@@ -560,22 +566,24 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   //     outstanding (W of chunk c+2 is from step c-3, chunk c's X from steps c-3, c-2);
   //   * group 24: chunk c+1's rows 0-63 (from step c-1 at the latest) landed;
   //   * end of a k = 1 step: this wave's scale table DMA of step k = 0 (followed by 16 X) landed.
-  auto step = [&](int c, auto kc, const uint8_t* xclo, const uint8_t* xchi, const uint8_t* xnlo,
+  // c8: first chunk of the 8-step body, j: step within it (c = c8 + j); eo0, eo1, eo2: byte
+  // offsets of the E stages of chunks c, c+1, c+2, rotated after every step (in the unrolled
+  // body the rotation is register renaming).  Loads past the last chunk, pair or group read
+  // other bytes of their tiles or zeros (buffer bounds) and are never used.
+  auto step = [&](int c8, auto jc, const uint8_t* xclo, const uint8_t* xchi, const uint8_t* xnlo,
                   uint8_t* xdlo, uint8_t* xdhi, const WSet& Q, WSet& F4, WSet& F5, const uint8_t* srq,
-                  uint8_t* srn) {
-    constexpr int k = decltype(kc)::value;
+                  uint8_t* srn, int& eo0, int& eo1, int& eo2) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int k = j & 3;
     constexpr bool even = (k & 1) == 0;
-    auto clampc = [&](int q) { return q < nchunks ? q : nchunks - 1; };  // past the end: harmless reload
-    const int cw4 = clampc(c + 4), cw5 = clampc(c + 5);
-    const int pd = (c >> 1) + 1 < npairs ? (c >> 1) + 1 : npairs - 1;   // pair being DMA'd
-    const int gn = (c >> 2) + 1 < G ? (c >> 2) + 1 : G - 1;
-    const int e_c = c % NES;
-    const int e_n = e_c + 1 == NES ? 0 : e_c + 1;
-    const int e_q = e_n + 1 == NES ? 0 : e_n + 1;
-    const uint8_t* ec = es + e_c * ESTAGE;
-    const uint8_t* en = es + e_n * ESTAGE;
-    uint8_t* eq = es + e_q * ESTAGE;
-    const uint8_t* sa = sr_addr(srq, c + 2);
+    const int c = c8 + j;
+    const int cb = c8 * (PKC * 2);                 // chunk c8's byte offset in a row
+    const int pd = (c8 >> 1) + (j >> 1) + 1;       // pair being DMA'd
+    const int gn = (c8 >> 2) + (j >> 2) + 1;       // next group (k = 0 steps)
+    const uint8_t* ec = es + eo0;
+    const uint8_t* en = es + eo1;
+    uint8_t* eq = es + eo2;
+    const uint8_t* sa = sr_addr(srq, k + 2);
     const uint8_t* xwlo = xclo + xwave;
     const uint8_t* xwhi = xchi + xwave;
     const uint8_t* xnw = xnlo + xwave;
@@ -617,16 +625,19 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
       }
       if (g == 14) store_piece(eq, eslot0, e);
       if (g == 26) store_piece(eq, eslot1, e + 8);
+      // every fragment read before group 8 (a1, b1) has landed; only the E store of group 14
+      // may be in flight.  One wait here spares the compiler's per-use waits in groups 16-31.
+      if (g == 15) __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x1 << 8) | (0x3 << 14));
       if (g >= 16 && g < 24 && (g & 1)) b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * PROW, efoff0);
       // chunk c+1's rows 0-63 landed: they come from step c-1 at the latest, followed by this
       // step's loads before group 24 (even: 4 W, 2 when k = 0, 6 X; odd: 8 X)
       if (g == 24) vm_wait(std::integral_constant<int, even ? 10 : 8>{});
       if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * XROW, xn0);
       if (even) {
-        if (g == 0) load_w(F4, 0, cw4);
-        if (g == 1) load_w(F5, 0, cw5);
-        if (g == 2) load_w(F4, 1, cw4);
-        if (g == 3) load_w(F5, 1, cw5);
+        if (g == 0) load_w(F4, 0, cb, j + 4);
+        if (g == 1) load_w(F5, 0, cb, j + 5);
+        if (g == 2) load_w(F4, 1, cb, j + 4);
+        if (g == 3) load_w(F5, 1, cb, j + 5);
         if (k == 0 && g == 4) PN = load_p(gn);
         if (k == 0 && g == 5) dma_sr(srn, gn);
         if (g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(xdlo, (g - 6) / 3, pd);
@@ -639,6 +650,10 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // E stores of chunk c+2, fragment reads
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    const int et = eo0;
+    eo0 = eo1;
+    eo1 = eo2;
+    eo2 = et;
   };
 
   // nchunks = K / 32 is a multiple of 4 (K is a multiple of 128).  Step c multiplies chunk c
@@ -651,22 +666,27 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+  int eo0 = 0, eo1 = ESTAGE, eo2 = 2 * ESTAGE;
   int c = 0;
   for (; c + 8 <= nchunks; c += 8) {
-    step(c + 0, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1);
-    step(c + 1, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1);
-    step(c + 2, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1);
-    step(c + 3, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1);
-    step(c + 4, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs1, srs0);
-    step(c + 5, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs1, srs0);
-    step(c + 6, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs0, srs0);
-    step(c + 7, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs0, srs0);
+    step(c, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I4{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I5{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I6{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I7{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
   }
   if (c < nchunks) {  // K / 128 odd: one more group
-    step(c + 0, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1);
-    step(c + 1, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1);
-    step(c + 2, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1);
-    step(c + 3, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1);
+    step(c, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
   }
 
   double ss = 0.0;

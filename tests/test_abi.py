@@ -88,6 +88,7 @@ def search(L, X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, 
     (dict(n_grid=0), INVALID), (dict(n_grid=65), INVALID), (dict(xt=3), UNSUP), (dict(wt=-1), UNSUP),
     (dict(ws=None), WS), (dict(wsb=1000), WS), (dict(a=P + 4), INVALID), (dict(tab=P + 4), INVALID),
     (dict(ldx=1 << 21, K=256), SHAPE),  # 512 rows of X would span more than 2^31 bytes
+    (dict(K=1 << 17, ldx=1 << 17, ldw=1 << 17, N=1 << 21), SHAPE),  # group ranges span 2^31 bytes
 ])
 def test_search_argument_errors(L, kw, status):
     assert search(L, **kw) == status
