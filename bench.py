@@ -78,6 +78,51 @@ def search_traffic(config: str):
     return float(fields["traffic bytes per launch"])
 
 
+def hbm_kernels(torch, awq, dev, reps: int = 10):
+    """The two bandwidth-bound kernels at the largest shapes of the decoder-block workload, so
+    that every call streams from HBM (the inputs exceed the 256 MB last-level cache): awq_stats
+    on the MLP down-projection input X bf16 [16384 x 14336] (2 bytes per element read) and
+    awq_pack on the fused gate+up weight W bf16 [28672 x 4096] (2 bytes read, 0.53125 written
+    per weight).  Seeded random values; the kernels' cost does not depend on them."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    res = {}
+    M, K = 16384, 14336
+    X = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    a = torch.empty(K, dtype=torch.float32, device=dev)
+    ws = torch.empty(awq.stats_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    ms = _time_reps(torch, lambda: awq.stats(X, out=a, workspace=ws, flags=fl, check=False), reps)
+    nbytes = 2.0 * M * K + 4.0 * K
+    res["stats"] = {"shape": [M, K], "bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del X, ws
+    N, K = 28672, 4096
+    W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
+    sv = torch.ones(K, dtype=torch.float32, device=dev)
+    out = (torch.empty((N, K // 8), dtype=torch.int32, device=dev),
+           torch.empty((N, K // 128), dtype=torch.float16, device=dev),
+           torch.empty((N, K // 128), dtype=torch.float16, device=dev))
+    ms = _time_reps(torch, lambda: awq.pack(W, sv, flags=fl, out=out, check=False), reps)
+    nbytes = 2.53125 * N * K + 4.0 * K
+    res["pack"] = {"shape": [N, K], "bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                   "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    awq.raise_for_flags(fl)
+    return res
+
+
+def _time_reps(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
 def copy_probe(mib: int, reps: int):
     """A plain device-to-device copy of a known size, the calibration run for the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE per dispatch against 2 x mib MiB moved)."""
@@ -102,6 +147,7 @@ def main():
     ap.add_argument("--config", default="attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="output channels of the oracle sample")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the large-input stats / pack timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -214,6 +260,8 @@ def main():
         "best_alpha": res.best_index / 20.0,
         "wall_s": wall,
     }
+    if not args.no_hbm:
+        out["hbm"] = hbm_kernels(torch, awq, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
     print(json.dumps(out), flush=True)

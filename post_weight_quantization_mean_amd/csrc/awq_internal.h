@@ -26,6 +26,35 @@ StatsPlan stats_plan(int64_t M, int64_t K, bool f32);
 hipError_t launch_stats(const void* X, bool f32, int64_t M, int64_t K, int64_t ldx, float* a_out,
                         double* partial, const StatsPlan& plan, uint32_t* flags, hipStream_t st);
 
+// ---- lane permutations (DPP: plain VALU operands, no LDS traffic) -------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane i reads lane i ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane i reads lane i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // within 8 lanes, lane i reads lane 7 - i
+constexpr int kDppMirror = 0x140;      // within 16 lanes, lane i reads lane 15 - i
+// max / min over each group of four, or of sixteen, consecutive lanes (every lane gets it)
+__device__ __forceinline__ float max4(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  return fmaxf(x, dpp<kDppXor2>(x));
+}
+__device__ __forceinline__ float min4(float x) {
+  x = fminf(x, dpp<kDppXor1>(x));
+  return fminf(x, dpp<kDppXor2>(x));
+}
+__device__ __forceinline__ float max16(float x) {
+  x = max4(x);
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  return fmaxf(x, dpp<kDppMirror>(x));
+}
+__device__ __forceinline__ float min16(float x) {
+  x = min4(x);
+  x = fminf(x, dpp<kDppHalfMirror>(x));
+  return fminf(x, dpp<kDppMirror>(x));
+}
+
 // ---- search ----------------------------------------------------------------------------
 constexpr int kSearchBM = 512;  // tokens per block tile
 constexpr int kSearchBN = 128;  // output channels per block tile

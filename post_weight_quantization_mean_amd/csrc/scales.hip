@@ -10,9 +10,15 @@
 namespace awq {
 namespace {
 
-// ---- scale table: one block per candidate -----------------------------------------------
+// ---- scale table ---------------------------------------------------------------------------
 // fp64 power, clamp and normalisation, each s rounded once to fp32; rs = fp32(1 / s).
-constexpr int kScaleThreads = 1024;
+// x^alpha is non-decreasing in x for alpha >= 0, so max_j r_j = max((max_j a_j)^alpha, 1e-4)
+// and likewise for the minimum: the normalisation needs only the extremes of a, and every
+// (candidate, channel) is independent.  Each block reduces max / min of a itself (a is a few
+// KiB and stays in L2) and writes 1024 channels of one candidate.
+constexpr int kScaleThreads = 256;
+constexpr int kScalePerThread = 4;
+constexpr int kScaleCols = kScaleThreads * kScalePerThread;
 
 __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float* __restrict__ a,
                                                                    int64_t K, int n_grid,
@@ -22,16 +28,15 @@ __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float*
                                                                    uint32_t* __restrict__ flags) {
   __shared__ double smax[kScaleThreads / 64];
   __shared__ double smin[kScaleThreads / 64];
-  const int i = blockIdx.x;
+  const int i = blockIdx.y;
   const double alpha = (double)i / (double)n_grid;
   double lmax = 0.0, lmin = INFINITY;
-  bool bad = false;
+  bool bad = false;  // a_j negative, NaN or infinite
   for (int64_t j = threadIdx.x; j < K; j += kScaleThreads) {
     const double aj = (double)a[j];
     if (!(aj >= 0.0) || isinf(aj)) bad = true;
-    const double r = fmax(pow(aj, alpha), 1e-4);
-    lmax = fmax(lmax, r);
-    lmin = fmin(lmin, r);
+    lmax = fmax(lmax, aj);
+    lmin = fmin(lmin, aj);
   }
   for (int off = 32; off > 0; off >>= 1) {
     lmax = fmax(lmax, __shfl_xor(lmax, off));
@@ -43,93 +48,139 @@ __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float*
     smin[wave] = lmin;
   }
   __syncthreads();
-  double rmax = smax[0], rmin = smin[0];
+  double amax = smax[0], amin = smin[0];
   for (int w = 1; w < kScaleThreads / 64; ++w) {
-    rmax = fmax(rmax, smax[w]);
-    rmin = fmin(rmin, smin[w]);
+    amax = fmax(amax, smax[w]);
+    amin = fmin(amin, smin[w]);
   }
-  const double norm = sqrt(rmax * rmin);
-  for (int64_t j = threadIdx.x; j < K; j += kScaleThreads) {
-    const double r = fmax(pow((double)a[j], alpha), 1e-4);
-    const float s = (float)(r / norm);
-    const float rs = (float)(1.0 / (double)s);
-    if (!(s > 0.0f) || isinf(s) || isinf(rs)) bad = true;
-    s_tab[(int64_t)i * K + j] = s;
-    rs_tab[(int64_t)i * K + j] = rs;
-    sr_tab[(int64_t)i * K + j] = make_float2(s, rs);
+  const double norm = sqrt(fmax(pow(amax, alpha), 1e-4) * fmax(pow(amin, alpha), 1e-4));
+  bool bad_s = false;
+#pragma unroll
+  for (int t = 0; t < kScalePerThread; ++t) {
+    const int64_t j = (int64_t)blockIdx.x * kScaleCols + t * kScaleThreads + threadIdx.x;
+    if (j < K) {
+      const double r = fmax(pow((double)a[j], alpha), 1e-4);
+      const float sv = (float)(r / norm);
+      const float rs = (float)(1.0 / (double)sv);
+      if (!(sv > 0.0f) || isinf(sv) || isinf(rs)) bad_s = true;
+      s_tab[(int64_t)i * K + j] = sv;
+      rs_tab[(int64_t)i * K + j] = rs;
+      sr_tab[(int64_t)i * K + j] = make_float2(sv, rs);
+    }
   }
-  if (bad) atomicOr(flags, kFlagScaleRange);
+  // every block sees all of a; the ones of column block 0 report a bad statistic
+  if (bad_s || (bad && blockIdx.x == 0)) atomicOr(flags, kFlagScaleRange);
 }
 
 // ---- group ranges: Delta and z of every (candidate, output channel, group) ---------------
-// Sixteen lanes share one group of 128 (8 channels each); W is read once and every
-// candidate's range is formed from it.  Delta = max(max - min, 1e-5) / 15 and
-// z = clamp(rne(-min / Delta), 0, 15), both with correctly rounded fp32 division.
+// Four lanes share one row's group of 128 (32 channels, 64 bytes each, so a load instruction
+// covers 16 rows x 64 bytes); a block covers 64 consecutive rows of one group, whose range
+// slots are contiguous for every candidate.  W is read once; every candidate's scales for the
+// group come from LDS.  Per candidate a lane forms its 32 scaled values, their max and min
+// (v_max3 / v_min3), and the four lanes of a row combine through lane swizzles.  The
+// divisions Delta = max(max - min, 1e-5) / 15 and z = clamp(rne(-min / Delta), 0, 15) (both
+// correctly rounded) are spread over the four lanes (candidates q, q + 4, ...), and the
+// results are gathered in LDS and written as contiguous runs.
+constexpr int kRangeThreads = 256;
+constexpr int kRangeRows = kRangeThreads / 4;  // 64 rows per block
+
 template <bool WF32>
-__global__ __launch_bounds__(256) void group_range_kernel(const void* __restrict__ W, int64_t N,
-                                                         int64_t K, int64_t ldw,
-                                                         const float* __restrict__ s_tab,
-                                                         int n_grid, float2* __restrict__ params,
-                                                         uint32_t* __restrict__ flags) {
+__global__ __launch_bounds__(kRangeThreads) void group_range_kernel(const void* __restrict__ W, int64_t N,
+                                                                   int64_t K, int64_t ldw,
+                                                                   const float* __restrict__ s_tab,
+                                                                   int n_grid, float2* __restrict__ params,
+                                                                   uint32_t* __restrict__ flags) {
+  // dynamic LDS: this group's scales for every candidate (n_grid x 128 floats), then the
+  // (Delta, z) of every candidate and row (n_grid x 64 float2)
+  extern __shared__ float4 dyn[];
+  float4* ss = dyn;
+  float2* out = reinterpret_cast<float2*>(dyn + n_grid * (kGroup / 4));
   const int64_t G = K / kGroup;
   const int64_t NP = padded_n(N);
-  // 16 lanes per (group g, channel n); a block covers 16 consecutive channels of one group
-  const int64_t grp = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  const bool live = grp < N * G;
-  const int64_t g = live ? grp / N : 0;
-  const int64_t n = live ? grp % N : 0;
-  const int64_t k0 = g * kGroup + sub * 8;
+  const int64_t g = blockIdx.y;
+  const int64_t nb = (int64_t)blockIdx.x * kRangeRows;   // first row of the block
+  const int tid = threadIdx.x;
+  const int row = tid >> 2, q = tid & 3;
+  const int64_t n = nb + row;
+  const bool live = n < N;
 
-  float w[8];
+  for (int t = tid; t < n_grid * (kGroup / 4); t += kRangeThreads) {
+    const int al = t / (kGroup / 4), c4 = t % (kGroup / 4);
+    ss[t] = *reinterpret_cast<const float4*>(s_tab + (int64_t)al * K + g * kGroup + 4 * c4);
+  }
+
+  float w[32];
   if (live) {
     if constexpr (WF32) {
-      const float* p = static_cast<const float*>(W) + n * ldw + k0;
-      const float4 u0 = *reinterpret_cast<const float4*>(p);
-      const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
-      w[0] = u0.x; w[1] = u0.y; w[2] = u0.z; w[3] = u0.w;
-      w[4] = u1.x; w[5] = u1.y; w[6] = u1.z; w[7] = u1.w;
-    } else {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + n * ldw + k0);
-      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + n * ldw + g * kGroup + 32 * q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[2 * i] = __uint_as_float(uu[i] << 16);
-        w[2 * i + 1] = __uint_as_float(uu[i] & 0xffff0000u);
+      for (int t = 0; t < 8; ++t) {
+        const float4 u = p[t];
+        w[4 * t] = u.x; w[4 * t + 1] = u.y; w[4 * t + 2] = u.z; w[4 * t + 3] = u.w;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + n * ldw + g * kGroup + 32 * q);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint4 u = p[t];
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          w[8 * t + 2 * h] = __uint_as_float(uu[h] << 16);
+          w[8 * t + 2 * h + 1] = __uint_as_float(uu[h] & 0xffff0000u);
+        }
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+    for (int t = 0; t < 32; ++t) w[t] = 0.0f;
   }
   bool bad = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) bad |= !isfinite(w[i]);
+  for (int t = 0; t < 32; ++t) bad |= !isfinite(w[t]);
+  __syncthreads();
 
-  for (int al = 0; al < n_grid; ++al) {
-    const float* sp = s_tab + (int64_t)al * K + k0;
-    const float4 s0 = *reinterpret_cast<const float4*>(sp);
-    const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
-    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    float mx = -INFINITY, mn = INFINITY;
+  // candidates four at a time; afterwards lane q finishes candidate al4 + q of its row
+#pragma unroll 1
+  for (int al4 = 0; al4 < n_grid; al4 += 4) {
+    float mxd[4], mnd[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = w[i] * s[i];
-      mx = fmaxf(mx, v);
-      mn = fminf(mn, v);
-    }
+    for (int d = 0; d < 4; ++d) {
+      const int al = al4 + d < n_grid ? al4 + d : n_grid - 1;
+      const float4* sp = ss + al * (kGroup / 4) + 8 * q;
+      float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-      mn = fminf(mn, __shfl_xor(mn, off, 16));
+      for (int t = 0; t < 8; ++t) {
+        const float4 sv = sp[t];
+        const float v0 = w[4 * t] * sv.x, v1 = w[4 * t + 1] * sv.y;
+        const float v2 = w[4 * t + 2] * sv.z, v3 = w[4 * t + 3] * sv.w;
+        mx = fmaxf(fmaxf(mx, v0), v1);
+        mx = fmaxf(fmaxf(mx, v2), v3);
+        mn = fminf(fminf(mn, v0), v1);
+        mn = fminf(fminf(mn, v2), v3);
+      }
+      mxd[d] = max4(mx);
+      mnd[d] = min4(mn);
     }
-    if (live && sub == 0) {
+    const float mx = q == 0 ? mxd[0] : q == 1 ? mxd[1] : q == 2 ? mxd[2] : mxd[3];
+    const float mn = q == 0 ? mnd[0] : q == 1 ? mnd[1] : q == 2 ? mnd[2] : mnd[3];
+    const int al = al4 + q;
+    if (al < n_grid) {
       const float range = mx - mn;
-      if (!isfinite(range)) bad = true;
+      if (live && !isfinite(range)) bad = true;
       const float delta = fmaxf(range, 1e-5f) / 15.0f;
       const float z = fminf(fmaxf(rintf(-mn / delta), 0.0f), 15.0f);
-      params[((int64_t)al * G + g) * NP + range_slot(n)] = make_float2(delta, z);
+      out[al * kRangeRows + row] = make_float2(delta, z);
     }
+  }
+  __syncthreads();
+  // rows nb .. nb + 63 occupy 64 consecutive slots starting at range_slot(nb)
+  const int64_t slot0 = range_slot(nb);
+  for (int t = tid; t < n_grid * kRangeRows; t += kRangeThreads) {
+    const int al = t / kRangeRows, j = t % kRangeRows;  // j: slot offset
+    // slot offset j = 32 w' + 2 jj + i  <->  row offset 32 w' + 16 i + jj
+    const int r = (j & ~31) + 16 * (j & 1) + ((j & 31) >> 1);
+    if (nb + r < NP) params[((int64_t)al * G + g) * NP + slot0 + j] = out[al * kRangeRows + r];
   }
   if (live && bad) atomicOr(flags, kFlagNonfiniteW);
 }
@@ -172,19 +223,20 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 
 hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
                               float2* sr_tab, uint32_t* flags, hipStream_t st) {
-  scale_table_kernel<<<n_grid, kScaleThreads, 0, st>>>(a, K, n_grid, s_tab, rs_tab, sr_tab, flags);
+  const dim3 grid((unsigned)((K + kScaleCols - 1) / kScaleCols), (unsigned)n_grid);
+  scale_table_kernel<<<grid, kScaleThreads, 0, st>>>(a, K, n_grid, s_tab, rs_tab, sr_tab, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
                               const float* s_tab, int n_grid, float2* params, uint32_t* flags,
                               hipStream_t st) {
-  const int64_t groups = N * (K / kGroup);
-  const unsigned blocks = (unsigned)((groups + 15) / 16);
+  const dim3 grid((unsigned)((N + kRangeRows - 1) / kRangeRows), (unsigned)(K / kGroup));
+  const size_t lds = (size_t)n_grid * (kGroup * 4 + kRangeRows * 8);  // <= 64 KiB (n_grid <= 64)
   if (wf32)
-    group_range_kernel<true><<<blocks, 256, 0, st>>>(W, N, K, ldw, s_tab, n_grid, params, flags);
+    group_range_kernel<true><<<grid, kRangeThreads, lds, st>>>(W, N, K, ldw, s_tab, n_grid, params, flags);
   else
-    group_range_kernel<false><<<blocks, 256, 0, st>>>(W, N, K, ldw, s_tab, n_grid, params, flags);
+    group_range_kernel<false><<<grid, kRangeThreads, lds, st>>>(W, N, K, ldw, s_tab, n_grid, params, flags);
   return hipGetLastError();
 }
 

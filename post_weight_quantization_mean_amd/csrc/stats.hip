@@ -15,6 +15,10 @@
 namespace awq {
 namespace {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// X is streamed once: non-temporal loads keep it from displacing the caches' other contents
+
 constexpr int kStatsWaves = 8;
 constexpr int kStatsThreads = kStatsWaves * 64;
 
@@ -39,9 +43,9 @@ __global__ __launch_bounds__(kStatsThreads) void stats_partial_kernel(
   if (col < K) {
     if constexpr (F32) {
       const float* base = static_cast<const float*>(X) + col;
-#pragma unroll 4
+#pragma unroll 16
       for (int64_t r = r0 + wave; r < r1; r += kStatsWaves) {
-        const float4 v = *reinterpret_cast<const float4*>(base + r * ldx);
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + r * ldx));
         acc[0] += fabs((double)v.x);
         acc[1] += fabs((double)v.y);
         acc[2] += fabs((double)v.z);
@@ -49,9 +53,9 @@ __global__ __launch_bounds__(kStatsThreads) void stats_partial_kernel(
       }
     } else {
       const uint16_t* base = static_cast<const uint16_t*>(X) + col;
-#pragma unroll 4
+#pragma unroll 16
       for (int64_t r = r0 + wave; r < r1; r += kStatsWaves) {
-        const uint4 v = *reinterpret_cast<const uint4*>(base + r * ldx);
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + r * ldx));
         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -75,21 +79,34 @@ __global__ __launch_bounds__(kStatsThreads) void stats_partial_kernel(
       double s = 0.0;
 #pragma unroll
       for (int w = 0; w < kStatsWaves; ++w) s += red[w][c];
-      partial[(int64_t)blockIdx.y * K + gc] = s;
+      partial[gc * gridDim.y + blockIdx.y] = s;  // [column][split]
     }
   }
 }
 
-__global__ __launch_bounds__(256) void stats_finalize_kernel(const double* __restrict__ partial,
-                                                            int splits, int64_t M, int64_t K,
-                                                            float* __restrict__ a_out,
-                                                            uint32_t* __restrict__ flags) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= K) return;
+// Eight lanes per column: lane t sums splits t, t + 8, t + 16, ... in order, then a fixed
+// xor tree (1, 2, 4) combines the eight, so the result does not depend on scheduling.
+constexpr int kFinThreads = 256;
+constexpr int kFinCols = kFinThreads / 8;
+
+__global__ __launch_bounds__(kFinThreads) void stats_finalize_kernel(const double* __restrict__ partial,
+                                                                    int splits, int64_t M, int64_t K,
+                                                                    float* __restrict__ a_out,
+                                                                    uint32_t* __restrict__ flags) {
+  const int64_t j = (int64_t)blockIdx.x * kFinCols + (threadIdx.x >> 3);
+  const int t = threadIdx.x & 7;
   double s = 0.0;
-  for (int p = 0; p < splits; ++p) s += partial[(int64_t)p * K + j];
-  if (!isfinite(s)) atomicOr(flags, kFlagNonfiniteX);
-  a_out[j] = (float)(s / (double)M);
+  if (j < K) {
+    const double* p = partial + j * splits;
+    for (int i = t; i < splits; i += 8) s += p[i];
+  }
+  s += __shfl_xor(s, 1, 8);
+  s += __shfl_xor(s, 2, 8);
+  s += __shfl_xor(s, 4, 8);
+  if (j < K && t == 0) {
+    if (!isfinite(s)) atomicOr(flags, kFlagNonfiniteX);
+    a_out[j] = (float)(s / (double)M);
+  }
 }
 
 }  // namespace
@@ -120,8 +137,8 @@ hipError_t launch_stats(const void* X, bool f32, int64_t M, int64_t K, int64_t l
                                                                 partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  stats_finalize_kernel<<<(unsigned)((K + 255) / 256), 256, 0, st>>>(partial, plan.splits, M, K,
-                                                                     a_out, flags);
+  stats_finalize_kernel<<<(unsigned)((K + kFinCols - 1) / kFinCols), kFinThreads, 0, st>>>(
+      partial, plan.splits, M, K, a_out, flags);
   return hipGetLastError();
 }
 

@@ -250,6 +250,33 @@ def test_pack_hand_vectors(awq):
     assert np.array_equal(sc.cpu().numpy(), art["scales"])
 
 
+def test_pack_near_tie_quotients(awq):
+    """Values whose quotient v / Delta lies within a few ulps of a half-integer: the codes
+    depend on the correctly rounded fp32 quotient, which the kernel forms from a reciprocal and
+    FMA corrections; they must equal the oracle's, which divides exactly."""
+    rng = np.random.default_rng(11)
+    rows = []
+    for _ in range(256):
+        lo, hi = np.float32(-rng.uniform(0.1, 4.0)), np.float32(rng.uniform(0.1, 4.0))
+        delta = np.float32(np.float32(hi - lo) / np.float32(15.0))
+        v = [lo, hi]
+        for _ in range(126):
+            k = rng.integers(-15, 15)
+            x = np.float32((k + 0.5) * float(delta))
+            for _ in range(int(rng.integers(-4, 5))):
+                x = np.nextafter(x, np.float32(np.inf) if rng.random() < 0.5 else np.float32(-np.inf))
+            v.append(np.float32(np.clip(x, lo, hi)))
+        rows.append(np.array(v, np.float32))
+    W = np.stack(rows)
+    W = np.concatenate([W, W[:, ::-1]], axis=1).astype(np.float32)  # K = 256, two groups
+    s = np.ones(256, np.float32)
+    qw, sc, zz = awq.pack(torch.from_numpy(W).to(DEV), torch.from_numpy(s).to(DEV))
+    art = o.pack(W, s)
+    assert np.array_equal(qw.cpu().numpy(), art["qweight"])
+    assert np.array_equal(zz.cpu().numpy(), art["zeros"])
+    assert np.array_equal(sc.cpu().numpy(), art["scales"])
+
+
 # ------------------------------------------------------------------------------ data errors
 def test_flags_nonfinite(awq):
     _, X, W = synth.custom_layer(64, 256, 64, seed=6)
