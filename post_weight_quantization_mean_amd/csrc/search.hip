@@ -507,6 +507,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
 
   WSet S0, S1, S2, S3;  // W words of chunk c live in set c % 4
   float4 PC, PN;        // ranges of the group being quantized, of the next group
+  RowQ q0, q1;          // row_setup of PC (rows r0, r1), renewed when PC changes
   // Prologue (once per block): group 0's scale table and ranges, W of chunks 0-3 and the X
   // pair of chunks 0 and 1, then chunks 0 and 1 are quantized.
   dma_sr(srs0, 0);
@@ -528,6 +529,8 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   __builtin_amdgcn_sched_barrier(0);
   quantize_all(S0, PC, 0, es + 0 * ESTAGE);
   quantize_all(S1, PC, 1, es + 1 * ESTAGE);
+  q0 = row_setup(PC, 0);
+  q1 = row_setup(PC, 1);
   bf16x8 a0[4], b0[4];
   {
     __builtin_amdgcn_sched_barrier(0);
@@ -553,7 +556,8 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   // (k = c % 4, known at compile time; xc is chunk c's pair stage, xn chunk c+1's):
   //   groups 0, 1: A fragments 2, 3 of chunk c (first used in groups 8 and 12);
   //   groups 0-7:  second-half fragment reads of chunk c (A even, B odd groups);
-  //   group 0:     the (s, 1/s) pairs and row ranges for the quantization of chunk c+2;
+  //   group 0:     the (s, 1/s) pairs for the quantization of chunk c+2 (row ranges are set up
+  //                when the group changes);
   //   groups 3-25, two of every three: its sixteen elements; E stores in groups 14 and 26;
   //   groups 17-23 (odd): chunk c+1's B fragments of the first K-half; groups 24, 25: its A
   //   fragments 0, 1;
@@ -590,10 +594,13 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     // A fragment t of chunk c: rows 32 t .. 32 t + 31 of the wave, in the lo (t < 2) or hi half
     auto xa = [&](int t) { return (t < 2 ? xwlo : xwhi) + (t & 1) * 32 * XROW; };
     const int xo0 = xfoff(k & 1, 0), xo1 = xfoff(k & 1, 1), xn0 = xfoff((k + 1) & 1, 0);
-    if (k == 2) PC = PN;  // chunks c+2 .. c+5 of this quad after the first two: next group
+    if (k == 2) {  // chunks c+2 .. c+5 of this quad after the first two: next group
+      PC = PN;
+      q0 = row_setup(PC, 0);
+      q1 = row_setup(PC, 1);
+    }
     bf16x8 a1[4], b1[4];
     float4 sv[4];
-    RowQ q0, q1;
     float e[16];
     __builtin_amdgcn_sched_barrier(0);
     vm_wait(std::integral_constant<int, even ? 0 : 12>{});
@@ -608,8 +615,6 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
       if (g == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
-        q0 = row_setup(PC, 0);
-        q1 = row_setup(PC, 1);
       }
       if (g < 8) {
         if (g & 1)
