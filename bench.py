@@ -79,20 +79,22 @@ def search_traffic(config: str):
 
 
 def hbm_kernels(torch, awq, dev, reps: int = 10):
-    """The two bandwidth-bound kernels at the largest shapes of the decoder-block workload, so
-    that every call streams from HBM (the inputs exceed the 256 MB last-level cache): awq_stats
-    on the MLP down-projection input X bf16 [16384 x 14336] (2 bytes per element read) and
-    awq_pack on the fused gate+up weight W bf16 [28672 x 4096] (2 bytes read, 0.53125 written
-    per weight).  Seeded random values; the kernels' cost does not depend on them."""
+    """The two bandwidth-bound kernels at the largest shapes of the decoder-block workload:
+    awq_stats on the MLP down-projection input X bf16 [16384 x 14336] (2 bytes per element
+    read) and awq_pack on the fused gate+up weight W bf16 [28672 x 4096] (2 bytes read, 0.53125
+    written per weight).  Each call streams from HBM: a 512 MiB buffer is overwritten between
+    calls, so no input is left in the 256 MB last-level cache.  Seeded random values; the
+    kernels' cost does not depend on them."""
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     res = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # 2x the 256 MB last-level cache
     M, K = 16384, 14336
     X = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     a = torch.empty(K, dtype=torch.float32, device=dev)
     ws = torch.empty(awq.stats_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
     fl = torch.zeros(1, dtype=torch.int32, device=dev)
-    ms = _time_reps(torch, lambda: awq.stats(X, out=a, workspace=ws, flags=fl, check=False), reps)
+    ms = _time_reps(torch, lambda: awq.stats(X, out=a, workspace=ws, flags=fl, check=False), reps, flush)
     nbytes = 2.0 * M * K + 4.0 * K
     res["stats"] = {"shape": [M, K], "bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -103,7 +105,7 @@ def hbm_kernels(torch, awq, dev, reps: int = 10):
     out = (torch.empty((N, K // 8), dtype=torch.int32, device=dev),
            torch.empty((N, K // 128), dtype=torch.float16, device=dev),
            torch.empty((N, K // 128), dtype=torch.float16, device=dev))
-    ms = _time_reps(torch, lambda: awq.pack(W, sv, flags=fl, out=out, check=False), reps)
+    ms = _time_reps(torch, lambda: awq.pack(W, sv, flags=fl, out=out, check=False), reps, flush)
     nbytes = 2.53125 * N * K + 4.0 * K
     res["pack"] = {"shape": [N, K], "bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -111,11 +113,16 @@ def hbm_kernels(torch, awq, dev, reps: int = 10):
     return res
 
 
-def _time_reps(torch, fn, reps):
+def _time_reps(torch, fn, reps, flush=None):
+    """Median of reps event-timed calls.  flush, when given, is a buffer larger than the
+    last-level cache that is overwritten between calls (outside the timed intervals), so that
+    every call reads its input from HBM."""
     fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for e0, e1 in evs:
+        if flush is not None:
+            flush.zero_()
         e0.record()
         fn()
         e1.record()

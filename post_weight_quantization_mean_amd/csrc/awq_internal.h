@@ -19,8 +19,7 @@ constexpr uint32_t kFlagNonfiniteLoss = 0x10u;
 // ---- statistic -------------------------------------------------------------------------
 struct StatsPlan {
   int col_blocks;  // blocks across K
-  int splits;      // row splits (partials per column)
-  int64_t rows_per_split;
+  int splits;      // interleaved row splits (partials per column)
 };
 StatsPlan stats_plan(int64_t M, int64_t K, bool f32);
 hipError_t launch_stats(const void* X, bool f32, int64_t M, int64_t K, int64_t ldx, float* a_out,
