@@ -101,7 +101,9 @@ def hbm_kernels(torch, awq, dev, reps: int = 10):
     del X, ws
     N, K = 28672, 4096
     W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
-    sv = torch.ones(K, dtype=torch.float32, device=dev)
+    # per-channel scales spread like the search's a^alpha (log-normal, sigma 0.25); s = 1, the
+    # alpha = 0 candidate, is slower on bf16 weights (exact fp32 quotient ties take the exact path)
+    sv = torch.exp(0.25 * torch.randn(K, generator=g, device=dev, dtype=torch.float32))
     out = (torch.empty((N, K // 8), dtype=torch.int32, device=dev),
            torch.empty((N, K // 128), dtype=torch.float16, device=dev),
            torch.empty((N, K // 128), dtype=torch.float16, device=dev))

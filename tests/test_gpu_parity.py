@@ -95,7 +95,8 @@ def run_search_case(awq, X, W, n_grid=20):
 
 # ------------------------------------------------------------------------------ statistic
 @pytest.mark.parametrize("shape,dtype", [((64, 256), "f32"), ((1000, 640), "bf16"), ((3, 128), "f32"),
-                                         ((1, 128), "bf16"), ((4096, 4096), "bf16"), ((700, 11008), "bf16")])
+                                         ((1, 128), "bf16"), ((4096, 4096), "bf16"), ((700, 11008), "bf16"),
+                                         ((1001, 1024), "bf16")])  # 15 interleaved splits, one-row tail
 def test_stats_parity(awq, shape, dtype):
     M, K = shape
     banner(f"stats {shape} {dtype}")
@@ -233,6 +234,22 @@ def test_pack_bit_exact(awq, N, K, wd):
         assert np.array_equal(qw.cpu().numpy(), art["qweight"]), f"qweight differs at candidate {i}"
         assert np.array_equal(sc.cpu().numpy(), art["scales"])
         assert np.array_equal(zz.cpu().numpy(), art["zeros"])
+
+
+def test_pack_bf16_many_rows_strided(awq):
+    """bf16 W with more rows than one sweep of the pack grid covers (several iterations, a
+    partial last one) and a row stride larger than K: every code, scale and zero point of all
+    2500 rows against the oracle."""
+    banner("pack bf16 N=2500 K=4096 ldw=4160")
+    g = torch.Generator().manual_seed(21)
+    full = (torch.randn(2500, 4160, generator=g) / 64).to(torch.bfloat16)
+    W = full[:, :4096]  # ldw = 4160
+    s = (torch.rand(4096, generator=g) + 0.5).to(torch.float32)
+    qw, sc, zz = awq.pack(full.to(DEV)[:, :4096], s.to(DEV))
+    art = o.pack(synth.to_f32(W.contiguous()), s.numpy())
+    assert np.array_equal(qw.cpu().numpy(), art["qweight"])
+    assert np.array_equal(sc.cpu().numpy(), art["scales"])
+    assert np.array_equal(zz.cpu().numpy(), art["zeros"])
 
 
 def test_pack_hand_vectors(awq):
