@@ -15,7 +15,10 @@ Sources (cited by page title and section):
   sqrt(max*min) normalisation, the per-candidate module-output MSE, first minimum wins),
   §7 (the asymmetric group pseudo-quantizer actually used for the artefact: round w/Delta,
   add z, clamp to [0, 15], reconstruct Delta(q - z); group size divides K; K-axis grouping
-  of a PyTorch [N, K] weight), §8 (g128 + fp16 scale + fp16 zero = 4.25 bits/weight).
+  of a PyTorch [N, K] weight), §8 (g128 + fp16 scale + fp16 zero = 4.25 bits/weight),
+  §5 (the clipping search that follows the scale search: ten thresholds 1, 0.95, ..., 0.55
+  of each group's absmax, chosen per output channel and input group by the squared error of
+  the group's partial output on the calibration tokens; the symmetric counterexample).
 * [DREAMVFIA] "AWQ salient weight / GGUF compilation" report (dreamvfia.cn), §二: the
   statistic (1/B) sum_b |X_bk| and the scale-equivalence algebra.
 * [MODULES] "5. 核心模块：校准器、压缩算法、格式封装与 kernel 后端" (ai-infra.cypggs.com), §5.3:
@@ -32,6 +35,11 @@ Readings where the pages are silent (each is listed in the design doc):
   scale table is computed in fp64 and rounded once to fp32.  The loss is fp64.
 * The loss of a candidate is the mean over the M x N outputs of (X E)^2 with
   E = W - S^-1 Q(S W): the module-output MSE of §4 for a single linear layer.
+* Clipping: the threshold of candidate i is fp32(absmax * fp32(1 - i/20)) of the scaled
+  weight v = fp32(W s); the clipped group clamp(v, -c, c) goes through the same asymmetric
+  quantizer; the error of (n, g) is the mean over the given tokens of
+  (sum_{k in g} X[m,k] e[n,k])^2 with e = W - S^-1 Q(clamp(S W)), in float64; the first
+  minimum wins.  Which tokens are sampled is the caller's choice.
 * Packing: qweight int32 [N, K/8], nibble i of word j holds the code of k = 8j + i (least
   significant nibble first); scales fp16 [N, K/g] hold Delta (round-to-nearest-even);
   zeros fp16 [N, K/g] hold the integer z.
@@ -340,3 +348,137 @@ def teaching_search(x: Sequence[float], w: Sequence[float], n_grid: int = N_GRID
         y, _, _ = teaching_forward(x, w, s)
         history.append(((y - target) ** 2, alpha, y))
     return history, first_argmin([h[0] for h in history])
+
+
+# ---------------------------------------------------------------------------------------
+# After the scale search: clipping search  [EXPLAINER §5]
+# ---------------------------------------------------------------------------------------
+CLIP_CANDIDATES = 10  # [EXPLAINER §5] thresholds 1, 0.95, ..., 0.55 of the group absmax
+
+
+def clip_factors(n_clip: int = CLIP_CANDIDATES) -> np.ndarray:
+    """Shrink factors f_i = 1 - i/20 for i < n_clip (the value 0.5 itself is not tried), as the
+    fp32 numbers the thresholds are multiplied with."""
+    if not 1 <= n_clip <= 20:
+        raise ValueError("between 1 and 20 clipping candidates")
+    return np.array([1.0 - i / 20.0 for i in range(n_clip)], dtype=np.float32)
+
+
+def teaching_clip_qdq(values: Sequence[float], factor: float) -> List[float]:
+    """The symmetric teaching quantizer with a clipping threshold ([EXPLAINER §5]): the
+    threshold is factor * max|v|, the step is threshold / 7, values are clamped to
+    +-threshold and then rounded to the nearest step (ties to even), codes limited to
+    [-7, 7].  An all-zero group stays zero.  Finite values and 0 < factor <= 1 only."""
+    vals = [float(v) for v in values]
+    if not vals or any(not isfinite(v) for v in vals):
+        raise ValueError("a group needs finite values")
+    if not (isfinite(factor) and 0.0 < factor <= 1.0):
+        raise ValueError("the clipping factor must lie in (0, 1]")
+    peak = max(abs(v) for v in vals)
+    if peak == 0.0:
+        return [0.0] * len(vals)
+    thr = peak * factor
+    step = thr / 7.0
+    if not (isfinite(step) and step > 0.0):
+        raise ValueError("threshold outside the float range")
+    out = []
+    for v in vals:
+        c = round(min(thr, max(-thr, v)) / step)  # Python round: ties to even
+        out.append(step * min(7, max(-7, c)))
+    return out
+
+
+def teaching_clip_search(groups: Sequence[Tuple[Sequence[float], Sequence[float]]],
+                         n_clip: int = CLIP_CANDIDATES) -> List[Tuple[float, float, float]]:
+    """Independent per-group clipping choice of [EXPLAINER §5] on one token: for each group
+    (x, w) the reference partial output x.w is compared with x.Q_c(w) for every factor, and
+    the first factor with the least squared difference wins.  Returns, per group,
+    (factor, prediction, reference)."""
+    out = []
+    for x, w in groups:
+        ref = sum(float(a) * float(b) for a, b in zip(x, w))
+        best = None
+        for i in range(n_clip):
+            f = 1.0 - i / 20.0
+            pred = sum(float(a) * b for a, b in zip(x, teaching_clip_qdq(w, f)))
+            loss = (pred - ref) ** 2
+            if best is None or loss < best[0]:
+                best = (loss, f, pred)
+        out.append((best[1], best[2], ref))
+    return out
+
+
+def clip_thresholds(W32: np.ndarray, s32: np.ndarray, n_clip: int = CLIP_CANDIDATES,
+                    group: int = GROUP) -> np.ndarray:
+    """Candidate thresholds c[i, n, g] = fp32(absmax_g |v[n, .]| * f_i) of the scaled weight
+    v = fp32(W s) ([EXPLAINER §5]: a shrink of the original group absmax)."""
+    W32 = np.asarray(W32, dtype=np.float32)
+    N, K = W32.shape
+    if group <= 0 or K % group != 0:
+        raise ValueError("the group size must divide K")
+    v = (W32 * np.asarray(s32, dtype=np.float32)[None, :]).reshape(N, K // group, group)
+    peak = np.abs(v).max(axis=-1)
+    return (clip_factors(n_clip)[:, None, None] * peak[None, :, :]).astype(np.float32)
+
+
+def quantize_clipped(W32: np.ndarray, s32: np.ndarray, c: np.ndarray, group: int = GROUP
+                     ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Quantize clamp(S W, -c, c) with the asymmetric group quantizer, c [N, K/g] one threshold
+    per (row, group).  Same returns as ``quantize``; the clamp is exact in fp32."""
+    W32 = np.asarray(W32, dtype=np.float32)
+    s32 = np.asarray(s32, dtype=np.float32)
+    N, K = W32.shape
+    if group <= 0 or K % group != 0:
+        raise ValueError("the group size must divide K")
+    if not np.all(np.isfinite(W32)):
+        raise ValueError("weights must be finite")
+    if s32.shape != (K,) or not np.all(np.isfinite(s32)) or np.any(s32 <= 0):
+        raise ValueError("scales must be finite and positive")
+    c = np.asarray(c, dtype=np.float32)
+    if c.shape != (N, K // group) or not np.all(np.isfinite(c)) or np.any(c < 0):
+        raise ValueError("thresholds must be finite and non-negative, one per (row, group)")
+    v = (W32 * s32[None, :]).reshape(N, K // group, group)
+    v = np.minimum(np.maximum(v, -c[..., None]), c[..., None])
+    delta, z = asym_params(v)
+    q = asym_codes(v, delta, z)
+    return q.reshape(N, K), z, delta
+
+
+def clip_errors(X: np.ndarray, W32: np.ndarray, s32: np.ndarray, n_clip: int = CLIP_CANDIDATES,
+                group: int = GROUP) -> Dict[str, np.ndarray]:
+    """The clipping search of [EXPLAINER §5] for one linear layer after its scales s: for every
+    output channel n, input group g and candidate i, the mean over the given tokens of the
+    squared error of the group's partial output,
+        err[i, n, g] = mean_m ( sum_{k in g} X[m, k] e_i[n, k] )^2,
+    e_i = W - S^-1 Q(clamp(S W, -c_i, c_i)), in float64 from the fp32 codes.  Each (n, g)
+    keeps the first candidate with the least error.  Returns err, best [N, K/g] and the
+    chosen thresholds max_val [N, K/g] (fp32)."""
+    X64 = np.asarray(X, dtype=np.float64)
+    W32 = np.asarray(W32, dtype=np.float32)
+    M, K = X64.shape
+    N = W32.shape[0]
+    if not np.all(np.isfinite(X64)):
+        raise ValueError("activations must be finite")
+    G = K // group
+    cs = clip_thresholds(W32, s32, n_clip, group)
+    err = np.empty((n_clip, N, G))
+    for i in range(n_clip):
+        q, z, d = quantize_clipped(W32, s32, cs[i], group)
+        E = W32.astype(np.float64) - effective_weight(q, z, d, s32, group)
+        for g in range(G):
+            Y = X64[:, g * group:(g + 1) * group] @ E[:, g * group:(g + 1) * group].T  # [M, N]
+            err[i, :, g] = np.mean(Y * Y, axis=0)
+    best = np.argmin(err, axis=0)  # numpy argmin returns the first minimum
+    max_val = np.take_along_axis(cs, best[None], axis=0)[0]
+    return {"err": err, "best": best.astype(np.int32), "max_val": max_val, "thresholds": cs}
+
+
+def pack_clipped(W: np.ndarray, s32: np.ndarray, max_val: np.ndarray, group: int = GROUP
+                 ) -> Dict[str, np.ndarray]:
+    """The artefact of ``pack`` for the clipped weight clamp(S W, -max_val, max_val)."""
+    q, z, d = quantize_clipped(W, s32, max_val, group)
+    scales = d.astype(np.float16)
+    if not np.all(np.isfinite(scales)):
+        raise ValueError("a group step overflows fp16")
+    return {"qweight": pack_words(q), "scales": scales, "zeros": z.astype(np.float16),
+            "codes": q, "z": z, "delta": d}
