@@ -1,6 +1,7 @@
 /*
  * awq.h -- C ABI of libawq: AWQ activation-aware INT4 weight quantization, the
- * data-parallel hot path (statistic, 20-candidate scale search, pack) on one MI355X.
+ * data-parallel hot path (statistic, 20-candidate scale search, pack) on one MI355X, and the
+ * clipping search that follows the scale search.
  *
  * Sources (cited by page title and section):
  *   [EXPLAINER] "AWQ：为什么 4-bit 权重量化要先观察 Activation" (charlestar.github.io)
@@ -36,7 +37,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 1
+#define AWQ_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -47,10 +48,12 @@ extern "C" {
 /* Status codes returned synchronously. */
 typedef enum {
   AWQ_OK = 0,
-  AWQ_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, ld < K, n_grid outside [1, 64] */
+  AWQ_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, ld < K, n_grid outside [1, 64],
+                              n_clip outside [1, 20] */
   AWQ_ERR_SHAPE = 2,       /* K not a multiple of the group size, 64-bit size overflow,
-                              awq_search: 512 rows of X, 128 rows of W or one candidate's
-                              group ranges (8 N K / 128 bytes) span 2^31 bytes or more */
+                              awq_search / awq_clip: 512 rows of X or 128 rows of W span 2^31
+                              bytes or more; awq_search: one candidate's group ranges
+                              (8 N K / 128 bytes) do */
   AWQ_ERR_UNSUPPORTED = 3, /* dtype other than F32/BF16, group other than 128 */
   AWQ_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than the size function says */
   AWQ_ERR_HIP = 5          /* a HIP launch or runtime call failed */
@@ -63,10 +66,13 @@ typedef enum { AWQ_DTYPE_F32 = 0, AWQ_DTYPE_BF16 = 1 } awq_dtype;
 #define AWQ_FLAG_NONFINITE_X 0x1u    /* awq_stats: X holds NaN or Inf */
 #define AWQ_FLAG_NONFINITE_W 0x2u    /* awq_pack: W holds NaN or Inf, or W*s overflows fp32 */
 #define AWQ_FLAG_SCALE_RANGE 0x4u    /* a scale candidate is not finite and positive in fp32,
-                                        or the statistic a is negative or not finite */
+                                        or the statistic a is negative or not finite; awq_clip,
+                                        awq_pack*: a given scale is not finite and positive;
+                                        awq_pack_clipped: a threshold is negative or not finite */
 #define AWQ_FLAG_F16_RANGE 0x8u      /* awq_pack: a group step does not fit fp16 */
-#define AWQ_FLAG_NONFINITE_LOSS 0x10u /* awq_search: a candidate loss is not finite (NaN/Inf
-                                         in X or W reach every loss through the product) */
+#define AWQ_FLAG_NONFINITE_LOSS 0x10u /* awq_search / awq_clip: a candidate loss is not finite
+                                         (NaN/Inf in X or W reach the losses through the
+                                         product) */
 
 typedef struct ihipStream_t* awq_stream_t; /* the same type as hipStream_t */
 typedef struct ihipEvent_t* awq_event_t;   /* the same type as hipEvent_t */
@@ -148,6 +154,43 @@ AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, i
 AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
                      const float* s, int32_t group, int32_t* qweight, uint16_t* scales,
                      uint16_t* zeros, uint32_t* flags, awq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * After the scale search: the clipping search ([EXPLAINER §5]).  With the scales s (normally
+ * awq_search's s_best_out), v = W*s (fp32); for every row n and group g of 128 k,
+ * absmax = max |v| over the group, and for i < n_clip (10 in the method):
+ *   f_i = fp32(1 - i/20)  (1, 0.95, ..., 0.55),   c_i = fp32(absmax * f_i)
+ *   the clipped group clamp(v, -c_i, c_i) is quantized with the contract of awq_search
+ *   (Delta and z from the clipped group's own max and min, exact fp32 division), and
+ *   err_i[n, g] = (1/M) sum_m ( sum_{k in g} X[m, k] E_i[n, k] )^2,
+ *   E_i[n, k] = W[n, k] - Delta (q - z) / s_k:
+ * the mean squared error of the group's partial output over the M given tokens.  The caller
+ * passes the calibration tokens to score as X (a row stride ldx = r K takes every r-th row
+ * of a larger X).  Each (n, g) keeps the first i with the least error.  The products run on
+ * the bf16 matrix cores as in awq_search; the codes inside them use the exact contract.
+ *   s             fp32 [K], finite and positive
+ *   group, n_clip 128 and 1..20
+ *   max_val_out   fp32 [N, K/128]: c of the chosen candidate (the clamp of awq_pack_clipped)
+ *   best_out      int32 [N, K/128] or NULL: the chosen i
+ *   err_out       fp64 [n_clip, N, K/128] or NULL: every candidate's error
+ *   ws            workspace of at least awq_clip_workspace_bytes(...) bytes (device)
+ *   flags         AWQ_FLAG_NONFINITE_W, AWQ_FLAG_SCALE_RANGE, AWQ_FLAG_NONFINITE_LOSS
+ * ------------------------------------------------------------------------------------- */
+AWQ_API size_t awq_clip_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
+                                        int32_t n_clip);
+AWQ_API int awq_clip(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                     const void* W, int w_dtype, int64_t N, int64_t ldw, const float* s,
+                     int32_t group, int32_t n_clip, float* max_val_out, int32_t* best_out,
+                     double* err_out, void* ws, size_t ws_bytes, uint32_t* flags,
+                     awq_stream_t stream);
+
+/* awq_pack of the clipped weight clamp(W*s, -max_val, max_val) ([EXPLAINER §5]: the chosen
+ * thresholds apply to the real quantization).  max_val: fp32 [N, K/128] (normally
+ * awq_clip's max_val_out); NULL gives awq_pack.  Outputs, contract and flags as awq_pack. */
+AWQ_API int awq_pack_clipped(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                             const float* s, const float* max_val, int32_t group,
+                             int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                             uint32_t* flags, awq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,12 +27,13 @@ FLAG_NONFINITE_LOSS = 0x10
 _FLAG_TEXT = {
     FLAG_NONFINITE_X: "activations must be finite",
     FLAG_NONFINITE_W: "weights (and weights times scales) must be finite",
-    FLAG_SCALE_RANGE: "scale candidates must be finite and positive",
+    FLAG_SCALE_RANGE: "scales must be finite and positive (and clip thresholds finite and non-negative)",
     FLAG_F16_RANGE: "a group step does not fit fp16",
     FLAG_NONFINITE_LOSS: "a candidate loss is not finite (non-finite X or W)",
 }
 GROUP = 128
 N_GRID = 20
+N_CLIP = 10
 
 _lib = None
 
@@ -70,7 +71,14 @@ def lib() -> ctypes.CDLL:
         L.awq_search_timed.argtypes = L.awq_search.argtypes + [vp, vp]
         L.awq_pack.restype = ctypes.c_int
         L.awq_pack.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, vp, vp, vp]
-        if L.awq_abi_version() != 1:
+        L.awq_pack_clipped.restype = ctypes.c_int
+        L.awq_pack_clipped.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp]
+        L.awq_clip_workspace_bytes.restype = sz
+        L.awq_clip_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+        L.awq_clip.restype = ctypes.c_int
+        L.awq_clip.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, i64, i64, vp,
+                               i32, i32, vp, vp, vp, vp, sz, vp, vp]
+        if L.awq_abi_version() != 2:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -192,14 +200,18 @@ def search(X: torch.Tensor, W: torch.Tensor, a: torch.Tensor, group_size: int = 
     return SearchResult(losses, best, s_best, s_table, fl)
 
 
-def pack(W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, *, flags: Optional[torch.Tensor] = None,
-         out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+def pack(W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, *, max_val: Optional[torch.Tensor] = None,
+         flags: Optional[torch.Tensor] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
          check: bool = True) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Quantize S W exactly and pack: qweight int32 [N, K/8], scales fp16 [N, K/128] (Delta),
-    zeros fp16 [N, K/128] (integer zero points)."""
+    zeros fp16 [N, K/128] (integer zero points).  ``max_val`` (fp32 [N, K/128], normally
+    ``clip(...).max_val``) clamps S W to [-max_val, max_val] per (row, group) first."""
     N, K, ldw = _matrix(W, "W")
     if s.shape != (K,) or s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous():
         raise ValueError("s must be a contiguous fp32 device vector of length K")
+    if max_val is not None and (max_val.shape != (N, K // group_size) or max_val.dtype != torch.float32
+                                or not max_val.is_cuda or not max_val.is_contiguous()):
+        raise ValueError("max_val must be a contiguous fp32 device tensor [N, K/group]")
     dev = W.device
     if out is None:
         qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
@@ -208,9 +220,57 @@ def pack(W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, *, flags: Op
     else:
         qweight, scales, zeros = out
     fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    st = lib().awq_pack(W.data_ptr(), _dtype_code(W), N, K, ldw, s.data_ptr(), group_size, qweight.data_ptr(),
-                        scales.data_ptr(), zeros.data_ptr(), fl.data_ptr(), _stream(dev))
+    if max_val is None:
+        st = lib().awq_pack(W.data_ptr(), _dtype_code(W), N, K, ldw, s.data_ptr(), group_size,
+                            qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), fl.data_ptr(), _stream(dev))
+    else:
+        st = lib().awq_pack_clipped(W.data_ptr(), _dtype_code(W), N, K, ldw, s.data_ptr(), max_val.data_ptr(),
+                                    group_size, qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                    fl.data_ptr(), _stream(dev))
     _check(st, "awq_pack")
     if check:
         raise_for_flags(fl)
     return qweight, scales, zeros
+
+
+def clip_workspace_bytes(M: int, K: int, N: int, group: int = GROUP, n_clip: int = N_CLIP) -> int:
+    return int(lib().awq_clip_workspace_bytes(M, K, N, group, n_clip))
+
+
+@dataclasses.dataclass
+class ClipResult:
+    max_val: torch.Tensor             # fp32 [N, K/128]: the chosen thresholds (device)
+    best: torch.Tensor                # int32 [N, K/128]: the chosen candidate (device)
+    err: Optional[torch.Tensor]       # fp64 [n_clip, N, K/128] when requested (device)
+    flags: torch.Tensor               # int32 [1] (device)
+
+
+def clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, n_clip: int = N_CLIP,
+         *, return_err: bool = False, workspace: Optional[torch.Tensor] = None,
+         flags: Optional[torch.Tensor] = None, check: bool = True) -> ClipResult:
+    """The clipping search after the scales s: per (output channel, group) the first of the
+    thresholds absmax * (1 - i/20), i < n_clip, with the least mean squared partial-output
+    error over the tokens of X (pass the sampled calibration tokens; a strided view such as
+    ``X[::8]`` works without a copy)."""
+    M, K, ldx = _matrix(X, "X")
+    N, Kw, ldw = _matrix(W, "W")
+    if Kw != K:
+        raise ValueError("X and W disagree on K")
+    if s.shape != (K,) or s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous():
+        raise ValueError("s must be a contiguous fp32 device vector of length K")
+    dev = X.device
+    G = K // group_size if group_size > 0 else 0
+    max_val = torch.empty((N, G), dtype=torch.float32, device=dev)
+    best = torch.empty((N, G), dtype=torch.int32, device=dev)
+    err = torch.empty((n_clip, N, G), dtype=torch.float64, device=dev) if return_err else None
+    need = clip_workspace_bytes(M, K, N, group_size, n_clip)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    st = lib().awq_clip(X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
+                        s.data_ptr(), group_size, n_clip, max_val.data_ptr(), best.data_ptr(),
+                        err.data_ptr() if err is not None else None, ws.data_ptr(), ws.numel(),
+                        fl.data_ptr(), _stream(dev))
+    _check(st, "awq_clip")
+    if check:
+        raise_for_flags(fl)
+    return ClipResult(max_val, best, err, fl)

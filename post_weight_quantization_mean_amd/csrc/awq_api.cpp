@@ -64,6 +64,26 @@ bool search_layout(int64_t M, int64_t K, int64_t N, int n_grid, SearchLayout* ou
   return true;
 }
 
+struct ClipLayout {
+  size_t rs, params, partial, total;
+};
+
+bool clip_layout(int64_t M, int64_t K, int64_t N, int n_clip, ClipLayout* out) {
+  const int64_t G = K / kGroup;
+  const int64_t mtiles = (M + awq::kClipBM - 1) / awq::kClipBM;
+  const int64_t rs = mul_ok(K, 4);
+  const int64_t par = mul_ok(mul_ok(mul_ok(n_clip, G), N), 16);
+  const int64_t part = mul_ok(mul_ok(mul_ok(mul_ok(n_clip, G), mtiles), N), 4);
+  if (rs < 0 || par < 0 || part < 0) return false;
+  ClipLayout L;
+  L.rs = 0;
+  L.params = L.rs + align_up((size_t)rs);
+  L.partial = L.params + align_up((size_t)par);
+  L.total = L.partial + align_up((size_t)part);
+  *out = L;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,9 +198,10 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
                           stream, nullptr, nullptr);
 }
 
-AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
-                     const float* s, int32_t group, int32_t* qweight, uint16_t* scales,
-                     uint16_t* zeros, uint32_t* flags, awq_stream_t stream) {
+AWQ_API int awq_pack_clipped(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                             const float* s, const float* max_val, int32_t group,
+                             int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                             uint32_t* flags, awq_stream_t stream) {
   int st = check_matrix(W, w_dtype, N, K, ldw);
   if (st != AWQ_OK) return st;
   if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
@@ -189,8 +210,54 @@ AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t l
     return AWQ_ERR_INVALID_ARG;
   if (!aligned16(s)) return AWQ_ERR_INVALID_ARG;
   if (mul_ok(N, K) < 0) return AWQ_ERR_SHAPE;
-  return map_hip(awq::launch_pack(W, w_dtype == AWQ_DTYPE_F32, N, K, ldw, s, qweight, scales,
-                                  zeros, flags, reinterpret_cast<hipStream_t>(stream)));
+  return map_hip(awq::launch_pack(W, w_dtype == AWQ_DTYPE_F32, N, K, ldw, s, max_val, qweight,
+                                  scales, zeros, flags, reinterpret_cast<hipStream_t>(stream)));
+}
+
+AWQ_API int awq_pack(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,
+                     const float* s, int32_t group, int32_t* qweight, uint16_t* scales,
+                     uint16_t* zeros, uint32_t* flags, awq_stream_t stream) {
+  return awq_pack_clipped(W, w_dtype, N, K, ldw, s, nullptr, group, qweight, scales, zeros, flags,
+                          stream);
+}
+
+AWQ_API size_t awq_clip_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
+                                        int32_t n_clip) {
+  if (M <= 0 || K <= 0 || N <= 0 || group != kGroup || K % kGroup != 0 || n_clip < 1 || n_clip > 20)
+    return 0;
+  ClipLayout L;
+  if (!clip_layout(M, K, N, n_clip, &L)) return 0;
+  return L.total;
+}
+
+AWQ_API int awq_clip(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                     const void* W, int w_dtype, int64_t N, int64_t ldw, const float* s,
+                     int32_t group, int32_t n_clip, float* max_val_out, int32_t* best_out,
+                     double* err_out, void* ws, size_t ws_bytes, uint32_t* flags,
+                     awq_stream_t stream) {
+  int st = check_matrix(X, x_dtype, M, K, ldx);
+  if (st != AWQ_OK) return st;
+  st = check_matrix(W, w_dtype, N, K, ldw);
+  if (st != AWQ_OK) return st;
+  if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
+  if (n_clip < 1 || n_clip > 20) return AWQ_ERR_INVALID_ARG;
+  if (s == nullptr || max_val_out == nullptr || flags == nullptr) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(s)) return AWQ_ERR_INVALID_ARG;
+  // block-relative 32-bit buffer offsets: 512 rows of X and 128 rows of W
+  if (mul_ok(mul_ok(awq::kClipBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX ||
+      mul_ok(mul_ok(awq::kClipBN, ldw), dsize(w_dtype)) >= (int64_t)INT32_MAX)
+    return AWQ_ERR_SHAPE;
+  ClipLayout L;
+  if (!clip_layout(M, K, N, n_clip, &L)) return AWQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < L.total) return AWQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return AWQ_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(ws);
+  return map_hip(awq::launch_clip(X, x_dtype == AWQ_DTYPE_F32, M, K, ldx, W, w_dtype == AWQ_DTYPE_F32,
+                                  N, ldw, s, n_clip, max_val_out, best_out, err_out,
+                                  reinterpret_cast<float4*>(base + L.params),
+                                  reinterpret_cast<float*>(base + L.rs),
+                                  reinterpret_cast<float*>(base + L.partial), flags,
+                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -92,8 +92,19 @@ hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64
                          float* s_best, uint32_t* flags, hipStream_t st);
 
 // ---- pack ------------------------------------------------------------------------------
+// clip: fp32 [N, K/128] thresholds of the clipped pack, or null
 hipError_t launch_pack(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s,
-                       int32_t* qweight, uint16_t* scales, uint16_t* zeros, uint32_t* flags,
-                       hipStream_t st);
+                       const float* clip, int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                       uint32_t* flags, hipStream_t st);
+
+// ---- clipping search --------------------------------------------------------------------
+constexpr int kClipBM = 512;  // tokens per product tile
+constexpr int kClipBN = 128;  // output channels per product tile
+// params: float4 [n_clip][K/128][N] (Delta, z, c, 0); rs: fp32 [K]; partial: fp32
+// [n_clip][K/128][ceil(M/512)][N]
+hipError_t launch_clip(const void* X, bool xf32, int64_t M, int64_t K, int64_t ldx, const void* W,
+                       bool wf32, int64_t N, int64_t ldw, const float* s, int n_clip, float* max_val,
+                       int32_t* best, double* err, float4* params, float* rs, float* partial,
+                       uint32_t* flags, hipStream_t st);
 
 }  // namespace awq

@@ -59,23 +59,36 @@ __device__ __forceinline__ void load_scales(const float* __restrict__ s, int64_t
 
 // Quantize the lane's 32 weights w of unit (n, g) and store its four code words (and, lane
 // q = 0, the unit's scale and zero point).  All four lanes of the unit's quad must be active.
+// CLIP: the scaled weights are first clamped to [-clip[n G + g], clip[n G + g]] (the
+// threshold chosen by the clipping search); a negative or non-finite threshold sets the range
+// flag.
+template <bool CLIP>
 __device__ __forceinline__ void encode_unit(const float (&w)[32], const float (&sc)[32], int64_t n,
-                                            int64_t g, int q, int64_t K, int32_t* __restrict__ qweight,
-                                            uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
-                                            uint32_t& bad) {
+                                            int64_t g, int q, int64_t K, const float* __restrict__ clip,
+                                            int32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
+                                            uint16_t* __restrict__ zeros, uint32_t& bad) {
   const int64_t G = K / kGroup;
+  float c = 0.0f;
+  if constexpr (CLIP) {
+    c = clip[n * G + g];
+    if (!(c >= 0.0f) || isinf(c)) bad |= kFlagScaleRange;
+  }
   float v[32];
   float mx = -INFINITY, mn = INFINITY;
   bool nan = false;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     v[i] = w[i] * sc[i];  // s is finite and positive: a non-finite w gives a non-finite v
-    mx = fmaxf(mx, v[i]);  // an Inf reaches the range
-    mn = fminf(mn, v[i]);
   }
 #pragma unroll
   for (int i = 0; i < 32; i += 2) nan |= __builtin_isunordered(v[i], v[i + 1]);
   if (nan) bad |= kFlagNonfiniteW;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if constexpr (CLIP) v[i] = fminf(fmaxf(v[i], -c), c);  // exact
+    mx = fmaxf(mx, v[i]);  // an Inf reaches the range
+    mn = fminf(mn, v[i]);
+  }
   mx = max4(mx);
   mn = min4(mn);
   const float range = mx - mn;
@@ -136,10 +149,11 @@ __device__ __forceinline__ void encode_unit(const float (&w)[32], const float (&
 // LDS into the four-lanes-per-unit layout.  LDS slot s is stored at s ^ ((s >> 4) & 15):
 // both the slot-order writes and the unit-order reads hit 16 distinct 16-byte bank groups per
 // 16 lanes.  Two iterations of loads are in flight per wave.
+template <bool CLIP>
 __global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(
     const uint16_t* __restrict__ W, int64_t N, int64_t K, int64_t ldw, const float* __restrict__ s,
-    int64_t R, int32_t* __restrict__ qweight, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
-    uint32_t* __restrict__ flags) {
+    const float* __restrict__ clip, int64_t R, int32_t* __restrict__ qweight,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, uint32_t* __restrict__ flags) {
   __shared__ __attribute__((aligned(16))) u32x4 lds[kPackThreads / 64][kWaveUnits * 16];
   const int64_t G = K / kGroup;
   const int64_t U = R * G;
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(
           w[8 * t + 2 * h + 1] = __uint_as_float(uu[h] & 0xffff0000u);
         }
       }
-      encode_unit(w, sc, n, g, q, K, qweight, scales, zeros, bad);
+      encode_unit<CLIP>(w, sc, n, g, q, K, clip, qweight, scales, zeros, bad);
     }
   };
   // the wave's first row is uw / G: the loop runs while any of its units has a row left
@@ -210,10 +224,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(
 
 // fp32 W (small layers and mixed inputs): each lane loads its own 128 bytes per row, one row
 // ahead.
+template <bool CLIP>
 __global__ __launch_bounds__(kPackThreads) void pack_f32_kernel(
     const float* __restrict__ W, int64_t N, int64_t K, int64_t ldw, const float* __restrict__ s,
-    int64_t R, int32_t* __restrict__ qweight, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
-    uint32_t* __restrict__ flags) {
+    const float* __restrict__ clip, int64_t R, int32_t* __restrict__ qweight,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, uint32_t* __restrict__ flags) {
   const int64_t G = K / kGroup;
   const int64_t ui = (int64_t)blockIdx.x * kPackUnits + (threadIdx.x >> 2);
   if (ui >= R * G) return;  // the last block's spare units (whole quads; no barrier here)
@@ -238,7 +253,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_f32_kernel(
       w[4 * t] = raw[t].x; w[4 * t + 1] = raw[t].y; w[4 * t + 2] = raw[t].z; w[4 * t + 3] = raw[t].w;
     }
     if (n + R < N) load(n + R);
-    encode_unit(w, sc, n, g, q, K, qweight, scales, zeros, bad);
+    encode_unit<CLIP>(w, sc, n, g, q, K, clip, qweight, scales, zeros, bad);
   }
   if (bad) atomicOr(flags, bad);
 }
@@ -246,19 +261,23 @@ __global__ __launch_bounds__(kPackThreads) void pack_f32_kernel(
 }  // namespace
 
 hipError_t launch_pack(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s,
-                       int32_t* qweight, uint16_t* scales, uint16_t* zeros, uint32_t* flags,
-                       hipStream_t st) {
+                       const float* clip, int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                       uint32_t* flags, hipStream_t st) {
   const int64_t G = K / kGroup;
   int64_t R = (kPackWindow + G / 2) / G;  // rows per grid iteration
   if (R < 1) R = 1;
   if (R > N) R = N;
   const unsigned blocks = (unsigned)((R * G + kPackUnits - 1) / kPackUnits);
-  if (wf32)
-    pack_f32_kernel<<<blocks, kPackThreads, 0, st>>>(static_cast<const float*>(W), N, K, ldw, s, R,
-                                                     qweight, scales, zeros, flags);
+  const float* Wf = static_cast<const float*>(W);
+  const uint16_t* Wh = static_cast<const uint16_t*>(W);
+  if (wf32 && clip)
+    pack_f32_kernel<true><<<blocks, kPackThreads, 0, st>>>(Wf, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
+  else if (wf32)
+    pack_f32_kernel<false><<<blocks, kPackThreads, 0, st>>>(Wf, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
+  else if (clip)
+    pack_bf16_kernel<true><<<blocks, kPackThreads, 0, st>>>(Wh, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
   else
-    pack_bf16_kernel<<<blocks, kPackThreads, 0, st>>>(static_cast<const uint16_t*>(W), N, K, ldw, s, R,
-                                                      qweight, scales, zeros, flags);
+    pack_bf16_kernel<false><<<blocks, kPackThreads, 0, st>>>(Wh, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
-                          "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack"}
+                          "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack",
+                          "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip"}
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -39,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 1
+    assert L.awq_abi_version() == 2
     for st in range(6):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
@@ -58,6 +59,13 @@ def test_workspace_size_functions(L):
     assert L.awq_search_workspace_bytes(4096, 4000, 4096, 128, 20) == 0
     assert L.awq_search_workspace_bytes(4096, 4096, 4096, 128, 0) == 0
     assert L.awq_search_workspace_bytes(4096, 4096, 4096, 128, 65) == 0
+    # clip: thresholds (16 B) + partial column sums (4 B) per (candidate, group, row, token tile)
+    assert L.awq_clip_workspace_bytes(512, 4096, 4096, 128, 10) >= 10 * 32 * 4096 * 20
+    assert L.awq_clip_workspace_bytes(1024, 4096, 4096, 128, 10) > L.awq_clip_workspace_bytes(512, 4096, 4096, 128, 10)
+    assert L.awq_clip_workspace_bytes(512, 4096, 4096, 64, 10) == 0
+    assert L.awq_clip_workspace_bytes(512, 4096, 4096, 128, 0) == 0
+    assert L.awq_clip_workspace_bytes(512, 4096, 4096, 128, 21) == 0
+    assert L.awq_clip_workspace_bytes(512, 4000, 4096, 128, 10) == 0
 
 
 def stats(L, X=P, dt=BF16, M=64, K=256, ldx=256, a=P, ws=P, wsb=1 << 30, fl=P):
@@ -125,3 +133,31 @@ def test_python_binding_rejects_host_tensors():
         awq.stats(torch.zeros(4, 128))
     with pytest.raises(TypeError):
         awq._dtype_code(torch.zeros(2, dtype=torch.float16))
+
+
+def pack_clipped(L, W=P, wt=BF16, N=128, K=256, ldw=256, s=P, mv=P, group=128, q=P, sc=P, z=P, fl=P):
+    return L.awq_pack_clipped(W, wt, N, K, ldw, s, mv, group, q, sc, z, fl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), INVALID), (dict(s=None), INVALID), (dict(q=None), INVALID), (dict(fl=None), INVALID),
+    (dict(K=100, ldw=100), SHAPE), (dict(group=32), UNSUP), (dict(wt=5), UNSUP), (dict(s=P + 2), INVALID),
+])
+def test_pack_clipped_argument_errors(L, kw, status):
+    assert pack_clipped(L, **kw) == status
+
+
+def clip(L, X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, s=P, group=128, n_clip=10,
+         mv=P, best=None, err=None, ws=P, wsb=1 << 30, fl=P):
+    return L.awq_clip(X, xt, M, K, ldx, W, wt, N, ldw, s, group, n_clip, mv, best, err, ws, wsb, fl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(W=None), INVALID), (dict(s=None), INVALID), (dict(mv=None), INVALID),
+    (dict(fl=None), INVALID), (dict(M=0), INVALID), (dict(ldw=128), INVALID), (dict(K=192, ldx=192, ldw=192), SHAPE),
+    (dict(group=64), UNSUP), (dict(n_clip=0), INVALID), (dict(n_clip=21), INVALID), (dict(xt=3), UNSUP),
+    (dict(ws=None), WS), (dict(wsb=1000), WS), (dict(s=P + 4), INVALID), (dict(ws=P + 8), INVALID),
+    (dict(ldx=1 << 21, K=256), SHAPE),  # 512 rows of X would span more than 2^31 bytes
+])
+def test_clip_argument_errors(L, kw, status):
+    assert clip(L, **kw) == status

@@ -52,13 +52,14 @@ def check_choice(best_gpu, losses_oracle, best_oracle, tol=None):
 
 def loss_tolerance(X64, W32, s_table, ref_losses, x_is_f32):
     """Per-candidate tolerance: max(1e-3 relative, a bound derived from the kernel's
-    arithmetic).  Each output y = sum_k x_k e_k is formed from e rounded once to bf16
-    (|de| <= 2^-9 |e|), fp32 quantities rounded a few times (<= 2^-21 |w|), an fp32 split of
-    fp32 X into two bf16 terms (<= 2^-16 |x|) and fp32 accumulation over K (<= K 2^-24).
+    arithmetic).  Each output y = sum_k x_k e_k is formed from e rounded once to bf16 (8
+    significand bits: |de| <= 2^-8 |e|), fp32 quantities rounded a few times (<= 2^-21 |w|), an
+    fp32 split of fp32 X into two bf16 terms (<= 2^-16 |x|) and fp32 accumulation over K
+    (<= K 2^-24).
     So |dy| <= c_A sum|x||e| + c_B sum|x||w| and |d(y^2)| <= 2|y||dy| + dy^2.  The bound only
     matters for a handful of outputs (M N small), where no averaging hides bf16 rounding."""
     K = X64.shape[1]
-    cA = 2.0 ** -9 + K * 2.0 ** -24 + (2.0 ** -16 if x_is_f32 else 0.0)
+    cA = 2.0 ** -8 + K * 2.0 ** -24 + (2.0 ** -16 if x_is_f32 else 0.0)
     cB = 2.0 ** -21
     absX = np.abs(X64)
     B = absX @ np.abs(W32.astype(np.float64)).T
