@@ -115,6 +115,25 @@ def hbm_kernels(torch, awq, dev, reps: int = 10):
     return res
 
 
+def clip_search(torch, awq, Xd, Wd, s_best, stride: int = 8, reps: int = 10):
+    """The clipping search that follows the scale search, on the same layer at its winning
+    scales, scoring every ``stride``-th token (a strided view, no copy): 10 thresholds per
+    (output channel, group).  Reported beside the step, not inside it: work 10 x 2*Ms*K*N
+    flop on the matrix cores (Ms sampled tokens), plus the range and select launches."""
+    Xs = Xd[::stride]
+    Ms, K = Xs.shape
+    N = Wd.shape[0]
+    ws = torch.empty(awq.clip_workspace_bytes(Ms, K, N), dtype=torch.uint8, device=Xd.device)
+    fl = torch.zeros(1, dtype=torch.int32, device=Xd.device)
+    ms = _time_reps(torch, lambda: awq.clip(Xs, Wd, s_best, workspace=ws, flags=fl, check=False), reps)
+    awq.raise_for_flags(fl)
+    flops = 10 * 2.0 * Ms * K * N
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tokens": Ms, "token_stride": stride, "n_clip": 10, "ms": ms, "flop": flops,
+            "tflops": tf, "frac_mfma_peak": tf / PEAK_BF16_TFLOPS,
+            "note": "whole awq_clip call (range pre-pass, clipped qdq + bf16 MFMA product, select)"}
+
+
 def _time_reps(torch, fn, reps, flush=None):
     """Median of reps event-timed calls.  flush, when given, is a buffer larger than the
     last-level cache that is overwritten between calls (outside the timed intervals), so that
@@ -157,6 +176,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=4096, help="output channels of the oracle sample")
     ap.add_argument("--no-hbm", action="store_true", help="skip the large-input stats / pack timing")
+    ap.add_argument("--no-clip", action="store_true", help="skip the clipping-search timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -269,6 +289,8 @@ def main():
         "best_alpha": res.best_index / 20.0,
         "wall_s": wall,
     }
+    if not args.no_clip:
+        out["clip"] = clip_search(torch, awq, Xd, Wd, res.s_best)
     if not args.no_hbm:
         out["hbm"] = hbm_kernels(torch, awq, dev)
     if not args.no_cpu_baseline:

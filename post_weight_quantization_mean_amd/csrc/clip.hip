@@ -17,6 +17,8 @@
 //     group, and after every group the column sums of Y^2 (fp32 over the tile's 512 tokens);
 //   * clip_select_kernel: per (n, g) the fixed-order fp64 sum over token tiles, the mean and
 //     the first minimum.
+#include <type_traits>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -353,6 +355,251 @@ __global__ __launch_bounds__(CTHREADS, 1) void clip_err_kernel(
   }
 }
 
+// ---- bf16 X: one group's X resident in LDS for all candidates ----------------------------
+// Block = (128-row tile, 512-token tile, block of groups); every candidate is handled inside
+// the block.  Per group the block loads X[512 tokens x 128 channels] into LDS once (136 KiB,
+// rows padded to 272 bytes: the 32-row fragment reads hit 16 distinct bank groups) and its W
+// pieces into registers once; then for each candidate it quantizes the four 32-channel E
+// chunks with that candidate's (Delta, z, c), multiplies, and writes the group's column sums
+// of Y^2.  Each X and W byte serves n_clip candidates, so the product runs on data already in
+// the CU instead of waiting for memory at every chunk.
+constexpr int XGP = kGroup + 8;  // LDS pitch of a group row of X, in bf16
+
+template <bool WF32>
+__global__ __launch_bounds__(CTHREADS, 1) void clip_err_group_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const void* __restrict__ W, int64_t N,
+    int64_t K, int64_t ldw, const float* __restrict__ s, const float* __restrict__ rs,
+    const float4* __restrict__ params, int n_clip, int64_t mtiles, int64_t ntiles, int gpb,
+    float* __restrict__ partial) {
+  constexpr int KC = 32;                      // channels per E chunk
+  constexpr int EP = KC + 8;                  // LDS pitch of an E row
+  constexpr int WEL = WF32 ? 4 : 8;           // W elements per 16-byte piece
+  constexpr int WSZ = WF32 ? 4 : 2;
+  constexpr int WPPR = KC / WEL;              // W pieces per row per chunk
+  constexpr int WP = CBN * WPPR / CTHREADS;   // W pieces per thread per chunk
+  constexpr int WROW_STEP = CTHREADS / WPPR;
+  constexpr int CPG = kGroup / KC;            // 4 chunks per group
+  constexpr int XPG = CBM * (kGroup / 8) / CTHREADS;  // 16-byte X pieces per thread per group (32)
+
+  __shared__ __attribute__((aligned(16))) uint16_t xg[CBM][XGP];
+  __shared__ __attribute__((aligned(16))) uint16_t es[2][CBN][EP];
+  __shared__ __attribute__((aligned(16))) float2 srs[kGroup];  // (s, 1/s) of the group
+  __shared__ float red[4][CBN];
+
+  const int64_t G = K / kGroup;
+  const int64_t gblocks = (G + gpb - 1) / gpb;
+  int64_t L = blockIdx.x;
+  const int64_t nt = L % ntiles;
+  L /= ntiles;
+  const int64_t mt = L % mtiles;
+  const int64_t gb = L / mtiles;
+  if (gb >= gblocks) return;
+  const int64_t m0 = mt * CBM, n0 = nt * CBN;
+  const int g0 = (int)(gb * gpb), g1 = (int)((g0 + gpb < G) ? g0 + gpb : G);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wkp = tid % WPPR, wrow0 = tid / WPPR;
+
+  const int64_t xbytes = (M - m0) * ldx * 2, wbytes = (N - n0) * ldw * WSZ;
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const char*>(W) + n0 * ldw * WSZ), (short)0,
+      (int)(wbytes < 0x7fffffff ? wbytes : 0x7fffffff), 0x00020000);
+  // X piece p (0..31) of this thread: row tid / 16 + 16 p, 16-byte piece tid % 16 of the group
+  const int xpc = tid & 15, xr0 = tid >> 4;
+  const uint32_t xoff0 = (uint32_t)(xr0 * ldx * 2 + xpc * 16);
+  const uint32_t xstep = (uint32_t)(16 * ldx * 2);
+  const uint32_t woff0 = (uint32_t)(wrow0 * ldw * WSZ + wkp * 16);
+  const uint32_t wstep = (uint32_t)(WROW_STEP * ldw * WSZ);
+  bool wlive[WP];
+  int64_t prow[WP];
+#pragma unroll
+  for (int r = 0; r < WP; ++r) {
+    const int64_t n = n0 + wrow0 + WROW_STEP * r;
+    wlive[r] = n < N;
+    prow[r] = wlive[r] ? n : 0;
+  }
+
+  f32x16 acc[4][4];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
+  };
+  zero_acc();
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+
+  for (int g = g0; g < g1; ++g) {
+    const uint32_t kb = (uint32_t)g * kGroup;
+    // W of the group, all four chunks, in registers for every candidate
+    uint4 wreg[CPG][WP];
+#pragma unroll
+    for (int j = 0; j < CPG; ++j)
+#pragma unroll
+      for (int r = 0; r < WP; ++r)
+        wreg[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   wrsrc, (int)(woff0 + r * wstep + (kb + j * KC) * WSZ), 0, 0));
+    __syncthreads();  // the previous group's X and scale reads are done
+    if (tid < kGroup) srs[tid] = make_float2(s[kb + tid], rs[kb + tid]);
+    // X of the group -> LDS, eight pieces in flight per step
+#pragma unroll
+    for (int h = 0; h < XPG / 8; ++h) {
+      uint4 xv[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        xv[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xrsrc, (int)(xoff0 + (8 * h + p) * xstep + kb * 2), 0, 0));
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        *reinterpret_cast<uint4*>(&xg[xr0 + 16 * (8 * h + p)][xpc * 8]) = xv[p];
+    }
+    __syncthreads();
+
+    // Steps t = 4 al + j (candidate al, chunk j): step t multiplies chunk t from E stage t % 2
+    // with the matrix instructions issued one at a time, and between them quantizes chunk t+1
+    // into the other stage (pinned by sched_barrier), so the vector ALU work runs under the
+    // matrix work; one barrier per step.  A candidate's (Delta, z, c) are loaded one candidate
+    // ahead.
+    struct RowP { float delta, inv, lo, hi, c; };
+    auto rowp = [&](const float4& P, int r) {
+      RowP q;
+      q.delta = wlive[r] ? P.x : 1.0f;  // rows past N: Delta 1, z 0, c 0 and w 0 give e = 0
+      const float z = wlive[r] ? P.y : 0.0f;
+      q.c = wlive[r] ? P.z : 0.0f;
+      q.inv = 1.0f / q.delta;  // correctly rounded
+      q.lo = -z;
+      q.hi = 15.0f - z;
+      return q;
+    };
+    auto load_params = [&](int al, float4* P) {
+#pragma unroll
+      for (int r = 0; r < WP; ++r) P[r] = params[((int64_t)al * G + g) * N + prow[r]];
+    };
+    // element t (0 .. WP*WEL-1) of chunk j: row t / WEL, channel t % WEL of this thread's piece
+    auto elem = [&](int j, int t, const RowP* rp, const float* sv, const float* rsv) {
+      const int r = t / WEL, k = t % WEL;
+      const uint4 u4 = wreg[j][r];
+      float w;
+      if constexpr (WF32) {
+        const uint32_t u = k == 0 ? u4.x : k == 1 ? u4.y : k == 2 ? u4.z : u4.w;
+        w = __uint_as_float(u);
+      } else {
+        const uint32_t u = k < 2 ? u4.x : k < 4 ? u4.y : k < 6 ? u4.z : u4.w;
+        w = (k & 1) ? hi16(u) : lo16(u);
+      }
+      const float v = __builtin_amdgcn_fmed3f(w * sv[k], -rp[r].c, rp[r].c);
+      const float q = rintf(exact_quot(v, rp[r].delta, rp[r].inv));
+      const float qz = __builtin_amdgcn_fmed3f(q, rp[r].lo, rp[r].hi);
+      return fmaf(-(qz * rp[r].delta), rsv[k], w);
+    };
+    auto store_row = [&](uint16_t (*eb)[EP], int r, const float* e) {
+      const int row = wrow0 + WROW_STEP * r;
+      uint32_t pk[WEL / 2];
+#pragma unroll
+      for (int t = 0; t < WEL / 2; ++t) pk[t] = to_bf16x2(e[2 * t], e[2 * t + 1]);
+      if constexpr (WEL == 8)
+        *reinterpret_cast<uint4*>(&eb[row][wkp * 8]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      else
+        *reinterpret_cast<uint2*>(&eb[row][wkp * 4]) = make_uint2(pk[0], pk[1]);
+    };
+    auto load_sr = [&](int j, float* sv, float* rsv) {
+#pragma unroll
+      for (int t = 0; t < WEL; ++t) {
+        const float2 p = srs[j * KC + wkp * WEL + t];
+        sv[t] = p.x;
+        rsv[t] = p.y;
+      }
+    };
+    constexpr int NE = WP * WEL;  // elements per thread per chunk (16)
+    float4 PC[WP], PN[WP];
+    load_params(0, PC);
+    RowP rq[WP];
+#pragma unroll
+    for (int r = 0; r < WP; ++r) rq[r] = rowp(PC[r], r);
+    if (n_clip > 1) load_params(1, PN);
+    {  // prologue: chunk 0 of candidate 0
+      float sv[WEL], rsv[WEL], e[NE];
+      load_sr(0, sv, rsv);
+#pragma unroll
+      for (int t = 0; t < NE; ++t) e[t] = elem(0, t, rq, sv, rsv);
+#pragma unroll
+      for (int r = 0; r < WP; ++r) store_row(es[0], r, e + r * WEL);
+      __syncthreads();
+    }
+    // one step: chunk j of candidate al (j known at compile time)
+    auto step = [&](int al, auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int jn = (j + 1) % CPG;
+      const bool more = j + 1 < CPG || al + 1 < n_clip;
+      if (jn == 0 && more) {  // the next chunk belongs to the next candidate
+#pragma unroll
+        for (int r = 0; r < WP; ++r) rq[r] = rowp(PN[r], r);
+        if (al + 2 < n_clip) load_params(al + 2, PN);
+      }
+      uint16_t (*ec)[EP] = es[j & 1];
+      uint16_t (*en)[EP] = es[jn & 1];
+      float sv[WEL], rsv[WEL], e[NE];
+      if (more) load_sr(jn, sv, rsv);
+      bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bfr[h][c] = *reinterpret_cast<const bf16x8*>(&ec[c * 32 + frow][h * 16 + fk]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          af[h][r] = *reinterpret_cast<const bf16x8*>(&xg[wave * 128 + r * 32 + frow][j * KC + h * 16 + fk]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gi = 0; gi < 32; ++gi) {
+        const int h = gi >> 4, r = (gi >> 2) & 3, c = gi & 3;
+        acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[h][r], bfr[h][c], acc[r][c], 0, 0, 0);
+        // the next chunk's elements, one per matrix instruction from the second on
+        if (gi >= 1 && gi <= NE) {
+          if (more) {
+            e[gi - 1] = elem(jn, gi - 1, rq, sv, rsv);
+            asm volatile("" : "+v"(e[gi - 1]));  // keep the element in this slot
+            if (gi % WEL == 0) store_row(en, gi / WEL - 1, e + (gi / WEL - 1) * WEL);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == CPG - 1) {
+        // column sums of Y^2 for (candidate al, group g), as in clip_err_kernel
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float tt = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tt = fmaf(acc[r][c][i], acc[r][c][i], tt);
+          tt += __shfl_xor(tt, 32);
+          if (lane < 32) red[wave][c * 32 + lane] = tt;
+        }
+        zero_acc();
+        __syncthreads();
+        if (tid < CBN && n0 + tid < N) {
+          const float tot = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+          partial[(((int64_t)al * G + g) * mtiles + mt) * N + n0 + tid] = tot;
+        }
+      }
+      // chunk t+1 is complete in its stage, chunk t's stage is free; red is written again
+      // only after four more of these barriers
+      __syncthreads();
+    };
+    for (int al = 0; al < n_clip; ++al) {
+      step(al, std::integral_constant<int, 0>{});
+      step(al, std::integral_constant<int, 1>{});
+      step(al, std::integral_constant<int, 2>{});
+      step(al, std::integral_constant<int, 3>{});
+    }
+  }
+}
+
 // ---- per (n, g): fixed-order sum over token tiles, mean, first minimum ---------------------
 __global__ __launch_bounds__(256) void clip_select_kernel(const float* __restrict__ partial,
                                                           const float4* __restrict__ params, int n_clip,
@@ -382,8 +629,11 @@ __global__ __launch_bounds__(256) void clip_select_kernel(const float* __restric
   if (bad) atomicOr(flags, kFlagNonfiniteLoss);
 }
 
+#ifndef AWQ_CLIP_GPB
+#define AWQ_CLIP_GPB 4
+#endif
 // groups per product block: four (16 chunks of work) unless K is smaller
-int64_t clip_groups_per_block(int64_t G) { return G < 4 ? G : 4; }
+int64_t clip_groups_per_block(int64_t G) { return G < AWQ_CLIP_GPB ? G : AWQ_CLIP_GPB; }
 
 }  // namespace
 
@@ -402,6 +652,25 @@ hipError_t launch_clip(const void* X, bool xf32, int64_t M, int64_t K, int64_t l
     if (e != hipSuccess) return e;
   }
   const int64_t mtiles = (M + CBM - 1) / CBM, ntiles = (N + CBN - 1) / CBN;
+  if (!xf32) {
+    // enough blocks to fill the chip: split the groups so that the blocks number >= 2 per CU
+    const int64_t tiles = mtiles * ntiles;
+    int64_t gpb = (G * tiles + 511) / 512;
+    if (gpb < 1) gpb = 1;
+    const int64_t gblocks = (G + gpb - 1) / gpb;
+    const unsigned blocks = (unsigned)(tiles * gblocks);
+    if (wf32)
+      clip_err_group_kernel<true><<<blocks, CTHREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, N, K, ldw, s, rs,
+                                                              params, n_clip, mtiles, ntiles, (int)gpb, partial);
+    else
+      clip_err_group_kernel<false><<<blocks, CTHREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, N, K, ldw, s, rs,
+                                                               params, n_clip, mtiles, ntiles, (int)gpb, partial);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    clip_select_kernel<<<(unsigned)((N * G + 255) / 256), 256, 0, st>>>(partial, params, n_clip, M, N, G,
+                                                                       mtiles, max_val, best, err, flags);
+    return hipGetLastError();
+  }
   const int gpb = (int)clip_groups_per_block(G);
   const int64_t gblocks = (G + gpb - 1) / gpb;
   const unsigned blocks = (unsigned)(n_clip * ntiles * mtiles * gblocks);
