@@ -18,7 +18,10 @@ Sources (cited by page title and section):
   of a PyTorch [N, K] weight), §8 (g128 + fp16 scale + fp16 zero = 4.25 bits/weight),
   §5 (the clipping search that follows the scale search: ten thresholds 1, 0.95, ..., 0.55
   of each group's absmax, chosen per output channel and input group by the squared error of
-  the group's partial output on the calibration tokens; the symmetric counterexample).
+  the group's partial output on the calibration tokens; the symmetric counterexample),
+  §6 (where S^-1 goes: a LayerNorm's gamma and beta, an RMSNorm's gamma, a preceding Linear's
+  output rows and bias, or act(x) / s after a non-linearity, never through it; every
+  consuming projection's input columns take s).
 * [DREAMVFIA] "AWQ salient weight / GGUF compilation" report (dreamvfia.cn), §二: the
   statistic (1/B) sum_b |X_bk| and the scale-equivalence algebra.
 * [MODULES] "5. 核心模块：校准器、压缩算法、格式封装与 kernel 后端" (ai-infra.cypggs.com), §5.3:
@@ -40,6 +43,8 @@ Readings where the pages are silent (each is listed in the design doc):
   quantizer; the error of (n, g) is the mean over the given tokens of
   (sum_{k in g} X[m,k] e[n,k])^2 with e = W - S^-1 Q(clamp(S W)), in float64; the first
   minimum wins.  Which tokens are sampled is the caller's choice.
+* Folding: every folded or scaled parameter is the exact quotient or product rounded once
+  to its storage type (fp32, or bf16 with ties to even).
 * Packing: qweight int32 [N, K/8], nibble i of word j holds the code of k = 8j + i (least
   significant nibble first); scales fp16 [N, K/g] hold Delta (round-to-nearest-even);
   zeros fp16 [N, K/g] hold the integer z.
@@ -482,3 +487,66 @@ def pack_clipped(W: np.ndarray, s32: np.ndarray, max_val: np.ndarray, group: int
         raise ValueError("a group step overflows fp16")
     return {"qweight": pack_words(q), "scales": scales, "zeros": z.astype(np.float16),
             "codes": q, "z": z, "delta": d}
+
+
+# ---------------------------------------------------------------------------------------
+# Applying the scales: folding S^-1 into the producer of X  [EXPLAINER §6]
+# ---------------------------------------------------------------------------------------
+def _round_to(values64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values once to the storage type ("f32", or "bf16" returned as float32
+    holding bf16 values, round to nearest even)."""
+    v32 = np.asarray(values64, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return v32
+    if dtype != "bf16":
+        raise ValueError("dtype is f32 or bf16")
+    # bf16 rounding of the exact value: round the float64 value directly to 8 significand bits
+    x = np.asarray(values64, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # nearest with ties to even at 8 bits
+    return r.astype(np.float32)
+
+
+def fold_rows(A: np.ndarray, s32: np.ndarray, dtype: str = "f32") -> np.ndarray:
+    """Row k of A divided by s_k, rounded once to the storage type.  This is the fold of
+    [EXPLAINER §6] for every producer whose output channel k feeds input channel k of the
+    scaled layers: a LayerNorm's gamma and beta (A = [K] or [K, 1]), an RMSNorm's gamma, or a
+    preceding Linear's output rows and bias (A = W_prev [K, K_in])."""
+    A64 = np.asarray(A, dtype=np.float64)
+    s64 = np.asarray(s32, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(s64)) or np.any(s64 <= 0):
+        raise ValueError("scales must be finite and positive")
+    shape = (-1,) + (1,) * (A64.ndim - 1)
+    return _round_to(A64 / s64.reshape(shape), dtype)
+
+
+def scale_cols(W: np.ndarray, s32: np.ndarray, dtype: str = "f32") -> np.ndarray:
+    """Column k of a consuming Linear weight W [N, K] multiplied by s_k, rounded once: every
+    projection that reads the folded X takes its s ([EXPLAINER §6]: Q, K and V together)."""
+    W64 = np.asarray(W, dtype=np.float64)
+    s64 = np.asarray(s32, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(s64)) or np.any(s64 <= 0):
+        raise ValueError("scales must be finite and positive")
+    return _round_to(W64 * s64[None, :], dtype)
+
+
+def gelu(x):
+    """The exact GELU of [EXPLAINER §6]: 0.5 x (1 + erf(x / sqrt 2)), float64."""
+    from math import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.vectorize(erf)(x / sqrt(2.0)))
+
+
+def silu(x):
+    """x sigmoid(x) = x / (1 + exp(-x)), float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def scaled_activation(X: np.ndarray, s32: np.ndarray, act: str = "gelu") -> np.ndarray:
+    """act(X) / s per input channel, float64: the runtime form where the inverse scaling
+    cannot be folded into parameters; the division comes after the activation, never before
+    it ([EXPLAINER §6])."""
+    f = {"gelu": gelu, "silu": silu}[act]
+    s64 = np.asarray(s32, dtype=np.float32).astype(np.float64)
+    return f(X) / s64[None, :]
