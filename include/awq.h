@@ -1,7 +1,7 @@
 /*
  * awq.h -- C ABI of libawq: AWQ activation-aware INT4 weight quantization, the
- * data-parallel hot path (statistic, 20-candidate scale search, pack) on one MI355X, and the
- * clipping search that follows the scale search.
+ * data-parallel hot path (statistic, 20-candidate scale search, pack) on one MI355X, the
+ * clipping search that follows the scale search, and the folding of the chosen scales.
  *
  * Sources (cited by page title and section):
  *   [EXPLAINER] "AWQ：为什么 4-bit 权重量化要先观察 Activation" (charlestar.github.io)
@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 2
+#define AWQ_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -191,6 +191,35 @@ AWQ_API int awq_pack_clipped(const void* W, int w_dtype, int64_t N, int64_t K, i
                              const float* s, const float* max_val, int32_t group,
                              int32_t* qweight, uint16_t* scales, uint16_t* zeros,
                              uint32_t* flags, awq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Applying the chosen scales ([EXPLAINER §6]).  The inverse scaling goes into the producer of
+ * X and every projection that reads X takes s on its input columns (all of them: Q, K and V
+ * share one X).  Each result is the exact quotient or product rounded once to the operand's
+ * type (fp32 correctly rounded; bf16 round to nearest even).  In place unless noted; dtype
+ * AWQ_DTYPE_F32 or AWQ_DTYPE_BF16; no group constraint on the sizes; elementwise and
+ * bandwidth-bound (16-byte accesses when every row start is 16-byte aligned).
+ *   awq_fold_rows   A [rows, cols], row stride lda: A[r, c] /= s[r].  A producer's output
+ *                   channel r feeds input channel r of the scaled layer: a LayerNorm's gamma
+ *                   and beta (rows = K, cols = lda = 1; both must be folded), an RMSNorm's
+ *                   gamma, or a preceding Linear's weight [K, K_in] and bias [K].
+ *   awq_scale_cols  W [N, K], row stride ldw: W[n, k] *= s[k] (a consuming Linear).
+ *   awq_scaled_act  Y[m, k] = act(X[m, k]) / s[k], X and Y [M, K] with row stride ld (Y may be
+ *                   X): the runtime form after a non-linearity, where nothing can absorb S^-1;
+ *                   the division follows the activation.  act: AWQ_ACT_GELU (exact,
+ *                   0.5 x (1 + erf(x / sqrt 2))) or AWQ_ACT_SILU (x / (1 + exp(-x))), in fp32
+ *                   with the device erfc / exp, so within a few fp32 ulps of the exact value.
+ *   s               fp32 [rows] (fold) or [K], 4-byte aligned
+ *   flags           AWQ_FLAG_SCALE_RANGE if a scale is not finite and positive
+ * ------------------------------------------------------------------------------------- */
+#define AWQ_ACT_GELU 0
+#define AWQ_ACT_SILU 1
+AWQ_API int awq_fold_rows(void* A, int dtype, int64_t rows, int64_t cols, int64_t lda, const float* s,
+                          uint32_t* flags, awq_stream_t stream);
+AWQ_API int awq_scale_cols(void* W, int dtype, int64_t N, int64_t K, int64_t ldw, const float* s,
+                           uint32_t* flags, awq_stream_t stream);
+AWQ_API int awq_scaled_act(const void* X, void* Y, int dtype, int64_t M, int64_t K, int64_t ld, int act,
+                           const float* s, uint32_t* flags, awq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -531,10 +531,12 @@ def scale_cols(W: np.ndarray, s32: np.ndarray, dtype: str = "f32") -> np.ndarray
 
 
 def gelu(x):
-    """The exact GELU of [EXPLAINER §6]: 0.5 x (1 + erf(x / sqrt 2)), float64."""
-    from math import erf
+    """The exact GELU of [EXPLAINER §6], 0.5 x (1 + erf(x / sqrt 2)), evaluated as
+    0.5 x erfc(-x / sqrt 2) (the same function: 1 + erf(z) = erfc(-z)), so that large negative
+    x keep their relative precision in float64 instead of cancelling to zero."""
+    from math import erfc
     x = np.asarray(x, dtype=np.float64)
-    return 0.5 * x * (1.0 + np.vectorize(erf)(x / sqrt(2.0)))
+    return 0.5 * x * np.vectorize(erfc)(-x / sqrt(2.0))
 
 
 def silu(x):

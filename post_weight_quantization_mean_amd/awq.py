@@ -34,6 +34,8 @@ _FLAG_TEXT = {
 GROUP = 128
 N_GRID = 20
 N_CLIP = 10
+ACT_GELU = 0
+ACT_SILU = 1
 
 _lib = None
 
@@ -78,7 +80,12 @@ def lib() -> ctypes.CDLL:
         L.awq_clip.restype = ctypes.c_int
         L.awq_clip.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, i64, i64, vp,
                                i32, i32, vp, vp, vp, vp, sz, vp, vp]
-        if L.awq_abi_version() != 2:
+        for name in ("awq_fold_rows", "awq_scale_cols"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp]
+        L.awq_scaled_act.restype = ctypes.c_int
+        L.awq_scaled_act.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp]
+        if L.awq_abi_version() != 3:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -274,3 +281,65 @@ def clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, group_size: int = GR
     if check:
         raise_for_flags(fl)
     return ClipResult(max_val, best, err, fl)
+
+
+def _rows2d(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
+    """[rows, cols] view of a 1-D or 2-D device tensor with unit stride along its last axis."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() == 1:
+        if t.stride(0) != 1:
+            raise ValueError(f"{name} must be contiguous")
+        return t.shape[0], 1, 1
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 1-D or 2-D with unit stride along its last axis")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def _scales_vec(s: torch.Tensor, n: int) -> None:
+    if s.shape != (n,) or s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous():
+        raise ValueError(f"s must be a contiguous fp32 device vector of length {n}")
+
+
+def fold_rows(A: torch.Tensor, s: torch.Tensor, *, flags: Optional[torch.Tensor] = None,
+              check: bool = True) -> torch.Tensor:
+    """In place: row k of A divided by s[k] -- a norm's gamma or beta ([K]) or a preceding
+    Linear's weight [K, K_in] and bias [K] absorb the inverse scaling.  Returns A."""
+    rows, cols, ld = _rows2d(A, "A")
+    _scales_vec(s, rows)
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=A.device)
+    _check(lib().awq_fold_rows(A.data_ptr(), _dtype_code(A), rows, cols, ld, s.data_ptr(), fl.data_ptr(),
+                               _stream(A.device)), "awq_fold_rows")
+    if check:
+        raise_for_flags(fl)
+    return A
+
+
+def scale_cols(W: torch.Tensor, s: torch.Tensor, *, flags: Optional[torch.Tensor] = None,
+               check: bool = True) -> torch.Tensor:
+    """In place: column k of a consuming Linear weight W [N, K] multiplied by s[k].  Returns W."""
+    N, K, ld = _matrix(W, "W")
+    _scales_vec(s, K)
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=W.device)
+    _check(lib().awq_scale_cols(W.data_ptr(), _dtype_code(W), N, K, ld, s.data_ptr(), fl.data_ptr(),
+                                _stream(W.device)), "awq_scale_cols")
+    if check:
+        raise_for_flags(fl)
+    return W
+
+
+def scaled_act(X: torch.Tensor, s: torch.Tensor, act: str = "gelu", *, out: Optional[torch.Tensor] = None,
+               flags: Optional[torch.Tensor] = None, check: bool = True) -> torch.Tensor:
+    """act(X) / s per input channel (``act`` "gelu" (exact) or "silu"); ``out`` may be X."""
+    M, K, ld = _matrix(X, "X")
+    _scales_vec(s, K)
+    code = {"gelu": ACT_GELU, "silu": ACT_SILU}[act]
+    Y = out if out is not None else torch.empty_strided(X.shape, X.stride(), dtype=X.dtype, device=X.device)
+    if Y.shape != X.shape or Y.stride() != X.stride() or Y.dtype != X.dtype:
+        raise ValueError("out must match X in shape, strides and dtype")
+    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=X.device)
+    _check(lib().awq_scaled_act(X.data_ptr(), Y.data_ptr(), _dtype_code(X), M, K, ld, code, s.data_ptr(),
+                                fl.data_ptr(), _stream(X.device)), "awq_scaled_act")
+    if check:
+        raise_for_flags(fl)
+    return Y

@@ -64,6 +64,29 @@ bool search_layout(int64_t M, int64_t K, int64_t N, int n_grid, SearchLayout* ou
   return true;
 }
 
+// Checks of an elementwise operand [rows, cols] with row stride ld (no group constraint).
+int check_elems(const void* p, int dtype, int64_t rows, int64_t cols, int64_t ld) {
+  if (p == nullptr) return AWQ_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return AWQ_ERR_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || ld < cols) return AWQ_ERR_INVALID_ARG;
+  if (mul_ok(mul_ok(rows, ld), dsize(dtype)) < 0) return AWQ_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(p) % (uintptr_t)dsize(dtype)) != 0) return AWQ_ERR_INVALID_ARG;
+  return AWQ_OK;
+}
+
+int scale_op(int op, const void* X, void* Y, int dtype, int64_t rows, int64_t cols, int64_t ld, const float* s,
+             int act, uint32_t* flags, awq_stream_t stream) {
+  int st = check_elems(X, dtype, rows, cols, ld);
+  if (st != AWQ_OK) return st;
+  if (Y == nullptr || s == nullptr || flags == nullptr) return AWQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(Y) % (uintptr_t)dsize(dtype)) != 0 || (reinterpret_cast<uintptr_t>(s) & 3u) != 0)
+    return AWQ_ERR_INVALID_ARG;
+  if (op == 2 && act != awq::kActGelu && act != awq::kActSilu) return AWQ_ERR_UNSUPPORTED;
+  const bool vec = aligned16(X) && aligned16(Y) && (ld * dsize(dtype)) % 16 == 0;
+  return map_hip(awq::launch_scale_op(op, X, Y, dtype == AWQ_DTYPE_BF16, rows, cols, ld, s, act, vec, flags,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
 struct ClipLayout {
   size_t rs, params, partial, total;
 };
@@ -258,6 +281,21 @@ AWQ_API int awq_clip(const void* X, int x_dtype, int64_t M, int64_t K, int64_t l
                                   reinterpret_cast<float*>(base + L.rs),
                                   reinterpret_cast<float*>(base + L.partial), flags,
                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+AWQ_API int awq_fold_rows(void* A, int dtype, int64_t rows, int64_t cols, int64_t lda, const float* s,
+                          uint32_t* flags, awq_stream_t stream) {
+  return scale_op(0, A, A, dtype, rows, cols, lda, s, 0, flags, stream);
+}
+
+AWQ_API int awq_scale_cols(void* W, int dtype, int64_t N, int64_t K, int64_t ldw, const float* s,
+                           uint32_t* flags, awq_stream_t stream) {
+  return scale_op(1, W, W, dtype, N, K, ldw, s, 0, flags, stream);
+}
+
+AWQ_API int awq_scaled_act(const void* X, void* Y, int dtype, int64_t M, int64_t K, int64_t ld, int act,
+                           const float* s, uint32_t* flags, awq_stream_t stream) {
+  return scale_op(2, X, Y, dtype, M, K, ld, s, act, flags, stream);
 }
 
 }  // extern "C"

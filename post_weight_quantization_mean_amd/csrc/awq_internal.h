@@ -97,6 +97,14 @@ hipError_t launch_pack(const void* W, bool wf32, int64_t N, int64_t K, int64_t l
                        const float* clip, int32_t* qweight, uint16_t* scales, uint16_t* zeros,
                        uint32_t* flags, hipStream_t st);
 
+// ---- applying the scales ----------------------------------------------------------------
+constexpr int kActGelu = 0;  // the values of the ABI's activation codes
+constexpr int kActSilu = 1;
+// op 0: A[r, c] /= s[r] (fold into a producer); 1: A[r, c] *= s[c] (scale a consumer);
+// 2: Y[r, c] = act(X[r, c]) / s[c].  vec: X (and Y) rows start 16-byte aligned.
+hipError_t launch_scale_op(int op, const void* X, void* Y, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                           const float* s, int act, bool vec, uint32_t* flags, hipStream_t st);
+
 // ---- clipping search --------------------------------------------------------------------
 constexpr int kClipBM = 512;  // tokens per product tile
 constexpr int kClipBN = 128;  // output channels per product tile

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
                           "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack",
-                          "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip"}
+                          "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip", "awq_fold_rows",
+                          "awq_scale_cols", "awq_scaled_act"}
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -40,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 2
+    assert L.awq_abi_version() == 3
     for st in range(6):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
@@ -161,3 +162,25 @@ def clip(L, X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, s=
 ])
 def test_clip_argument_errors(L, kw, status):
     assert clip(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), INVALID), (dict(s=None), INVALID), (dict(fl=None), INVALID), (dict(rows=0), INVALID),
+    (dict(cols=0), INVALID), (dict(ld=3, cols=4), INVALID), (dict(dt=9), UNSUP), (dict(A=P + 1), INVALID),
+    (dict(s=P + 2), INVALID), (dict(rows=1 << 62, ld=1 << 10, cols=4), SHAPE),
+])
+def test_fold_and_scale_argument_errors(L, kw, status):
+    a = dict(A=P, dt=BF16, rows=64, cols=4, ld=4, s=P, fl=P)
+    a.update(kw)
+    assert L.awq_fold_rows(a["A"], a["dt"], a["rows"], a["cols"], a["ld"], a["s"], a["fl"], None) == status
+    assert L.awq_scale_cols(a["A"], a["dt"], a["rows"], a["cols"], a["ld"], a["s"], a["fl"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(Y=None), INVALID), (dict(act=2), UNSUP), (dict(act=-1), UNSUP),
+    (dict(Y=P + 1), INVALID), (dict(M=0), INVALID),
+])
+def test_scaled_act_argument_errors(L, kw, status):
+    a = dict(X=P, Y=P, dt=F32, M=8, K=16, ld=16, act=0, s=P, fl=P)
+    a.update(kw)
+    assert L.awq_scaled_act(a["X"], a["Y"], a["dt"], a["M"], a["K"], a["ld"], a["act"], a["s"], a["fl"], None) == status
