@@ -21,7 +21,8 @@ Sources (cited by page title and section):
   the group's partial output on the calibration tokens; the symmetric counterexample),
   §6 (where S^-1 goes: a LayerNorm's gamma and beta, an RMSNorm's gamma, a preceding Linear's
   output rows and bias, or act(x) / s after a non-linearity, never through it; every
-  consuming projection's input columns take s).
+  consuming projection's input columns take s); §7 and §8 for using the artefact: decode
+  scales * (q - zeros) and multiply with 16-bit activations that carry S^-1 (W4A16).
 * [DREAMVFIA] "AWQ salient weight / GGUF compilation" report (dreamvfia.cn), §二: the
   statistic (1/B) sum_b |X_bk| and the scale-equivalence algebra.
 * [MODULES] "5. 核心模块：校准器、压缩算法、格式封装与 kernel 后端" (ai-infra.cypggs.com), §5.3:
@@ -552,3 +553,29 @@ def scaled_activation(X: np.ndarray, s32: np.ndarray, act: str = "gelu") -> np.n
     f = {"gelu": gelu, "silu": silu}[act]
     s64 = np.asarray(s32, dtype=np.float32).astype(np.float64)
     return f(X) / s64[None, :]
+
+
+# ---------------------------------------------------------------------------------------
+# Using the artefact: W4A16 products over the packed weight  [EXPLAINER §7, §8]
+# ---------------------------------------------------------------------------------------
+def dequant_artefact(qweight: np.ndarray, scales16: np.ndarray, zeros16: np.ndarray,
+                     group: int = GROUP) -> np.ndarray:
+    """The weight the artefact encodes, in float64 [N, K]: scales[n, g] * (q[n, k] - zeros[n, g])
+    with the fp16 scale and the integer zero point ([EXPLAINER §7]: reconstruct Delta (q - z);
+    this is what a deployed kernel multiplies with the inputs that carry S^-1)."""
+    q = unpack_words(np.asarray(qweight)).astype(np.float64)
+    N, K = q.shape
+    d = np.asarray(scales16, dtype=np.float16).astype(np.float64)
+    z = np.asarray(zeros16, dtype=np.float16).astype(np.float64)
+    if d.shape != (N, K // group) or z.shape != d.shape:
+        raise ValueError("scales and zeros must be [N, K / group]")
+    return (d[..., None] * (q.reshape(N, K // group, group) - z[..., None])).reshape(N, K)
+
+
+def w4a16_matmul(Xs: np.ndarray, qweight: np.ndarray, scales16: np.ndarray, zeros16: np.ndarray,
+                 group: int = GROUP) -> np.ndarray:
+    """Y = X' W_hat^T in float64 for activations X' [M, K] that already carry S^-1 (the folded
+    producer's output) and the artefact's weight W_hat [N, K]: the W4A16 product of
+    [EXPLAINER §8] (4-bit weights, 16-bit activations) with exact arithmetic."""
+    X64 = np.asarray(Xs, dtype=np.float64)
+    return X64 @ dequant_artefact(qweight, scales16, zeros16, group).T
