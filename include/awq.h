@@ -1,7 +1,8 @@
 /*
  * awq.h -- C ABI of libawq: AWQ activation-aware INT4 weight quantization, the
  * data-parallel hot path (statistic, 20-candidate scale search, pack) on one MI355X, the
- * clipping search that follows the scale search, and the folding of the chosen scales.
+ * clipping search that follows the scale search, the folding of the chosen scales and the
+ * W4A16 product over the packed artefact.
  *
  * Sources (cited by page title and section):
  *   [EXPLAINER] "AWQ：为什么 4-bit 权重量化要先观察 Activation" (charlestar.github.io)
@@ -37,7 +38,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 3
+#define AWQ_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -220,6 +221,25 @@ AWQ_API int awq_scale_cols(void* W, int dtype, int64_t N, int64_t K, int64_t ldw
                            uint32_t* flags, awq_stream_t stream);
 AWQ_API int awq_scaled_act(const void* X, void* Y, int dtype, int64_t M, int64_t K, int64_t ld, int act,
                            const float* s, uint32_t* flags, awq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Using the artefact: the W4A16 product ([EXPLAINER §7]: decode Delta (q - z); §8: 4-bit
+ * weights with 16-bit activations, the weight decoded on the fly and never written back).
+ *   Y[m, n] = sum_k X'[m, k] * scales[n, k/128] * (q[n, k] - zeros[n, k/128])
+ * with the artefact of awq_pack / awq_pack_clipped (qweight int32 [N, K/8], nibble i of word j
+ * = code of k = 8j+i; scales, zeros fp16 [N, K/128]) and activations X' that already carry
+ * S^-1 (folded into their producer, awq_fold_rows, or awq_scaled_act).
+ *   X        [M, K], AWQ_DTYPE_BF16 or AWQ_DTYPE_F32, row stride ldx (16-byte aligned rows)
+ *   Y        fp32 [M, N], row stride ldy >= N
+ * Up to 8 bf16 tokens (any number of fp32 tokens, 8 per launch) take the decode kernel:
+ * products exact in fp32, the group scale applied per 32 channels, fp32 sums.  More bf16
+ * tokens take the prefill kernel on the bf16 matrix cores, which rounds the decoded weight
+ * Delta (q - z) once to bf16 (relative 2^-8) and accumulates in fp32.
+ * qweight must be 16-byte aligned.  No data-error flags: non-finite X reaches Y.
+ * ------------------------------------------------------------------------------------- */
+AWQ_API int awq_w4a16(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                      const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
+                      int64_t ldy, awq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -85,7 +85,9 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp]
         L.awq_scaled_act.restype = ctypes.c_int
         L.awq_scaled_act.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp]
-        if L.awq_abi_version() != 3:
+        L.awq_w4a16.restype = ctypes.c_int
+        L.awq_w4a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i32, vp, i64, vp]
+        if L.awq_abi_version() != 4:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -342,4 +344,24 @@ def scaled_act(X: torch.Tensor, s: torch.Tensor, act: str = "gelu", *, out: Opti
                                 fl.data_ptr(), _stream(X.device)), "awq_scaled_act")
     if check:
         raise_for_flags(fl)
+    return Y
+
+
+def w4a16(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+          group_size: int = GROUP, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X' W_hat^T (fp32 [M, N]) for activations X' [M, K] that already carry S^-1 and the
+    artefact (qweight int32 [N, K/8], scales and zeros fp16 [N, K/128]) of ``pack``."""
+    M, K, ldx = _matrix(X, "X")
+    N = qweight.shape[0]
+    if qweight.shape != (N, K // 8) or qweight.dtype != torch.int32 or not qweight.is_contiguous():
+        raise ValueError("qweight must be a contiguous int32 [N, K/8] tensor")
+    for t, name in ((scales, "scales"), (zeros, "zeros")):
+        if t.shape != (N, K // group_size) or t.dtype != torch.float16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp16 [N, K/group] tensor")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=X.device)
+    if Y.shape != (M, N) or Y.dtype != torch.float32 or Y.stride(1) != 1:
+        raise ValueError("out must be fp32 [M, N] with unit stride along N")
+    _check(lib().awq_w4a16(X.data_ptr(), _dtype_code(X), M, K, ldx, qweight.data_ptr(), scales.data_ptr(),
+                           zeros.data_ptr(), N, group_size, Y.data_ptr(), Y.stride(0), _stream(X.device)),
+           "awq_w4a16")
     return Y

@@ -298,4 +298,22 @@ AWQ_API int awq_scaled_act(const void* X, void* Y, int dtype, int64_t M, int64_t
   return scale_op(2, X, Y, dtype, M, K, ld, s, act, flags, stream);
 }
 
+AWQ_API int awq_w4a16(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                      const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
+                      int64_t ldy, awq_stream_t stream) {
+  int st = check_matrix(X, x_dtype, M, K, ldx);
+  if (st != AWQ_OK) return st;
+  if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
+  if (qweight == nullptr || scales == nullptr || zeros == nullptr || Y == nullptr || N <= 0 || ldy < N)
+    return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(qweight) || (reinterpret_cast<uintptr_t>(scales) & 1u) != 0 ||
+      (reinterpret_cast<uintptr_t>(zeros) & 1u) != 0 || (reinterpret_cast<uintptr_t>(Y) & 3u) != 0)
+    return AWQ_ERR_INVALID_ARG;
+  if (mul_ok(mul_ok(M, ldy), 4) < 0 || mul_ok(N, K) < 0) return AWQ_ERR_SHAPE;
+  // prefill tiles use 32-bit offsets within 512 rows of X
+  if (mul_ok(mul_ok(awq::kW4a16BM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  return map_hip(awq::launch_w4a16(X, x_dtype == AWQ_DTYPE_F32, M, K, ldx, qweight, scales, zeros, N, Y, ldy,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -105,6 +105,13 @@ constexpr int kActSilu = 1;
 hipError_t launch_scale_op(int op, const void* X, void* Y, bool bf16, int64_t rows, int64_t cols, int64_t ld,
                            const float* s, int act, bool vec, uint32_t* flags, hipStream_t st);
 
+// ---- W4A16 products over the artefact -----------------------------------------------------
+constexpr int64_t kW4a16GemvMax = 8;  // tokens per decode launch; bf16 X above this runs on MFMA
+constexpr int kW4a16BM = 512;         // tokens per prefill tile
+hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, float* Y, int64_t ldy,
+                        hipStream_t st);
+
 // ---- clipping search --------------------------------------------------------------------
 constexpr int kClipBM = 512;  // tokens per product tile
 constexpr int kClipBN = 128;  // output channels per product tile

@@ -1,0 +1,285 @@
+// Using the artefact ("AWQ：为什么 4-bit 权重量化要先观察 Activation", §7 and §8): the W4A16
+// product Y = X' W_hat^T of 16-bit activations X' [M, K] (which already carry S^-1, folded
+// into their producer) with the packed weight W_hat[n, k] = scales[n, g] (q[n, k] - zeros[n, g])
+// (fp16 scale, integer zero point, nibble i of word j = code of k = 8 j + i).  The weight is
+// decoded on the fly and never written back.
+//
+// Two kernels:
+//   * decode, M <= 8 tokens (more with fp32 X, eight per launch): bandwidth-bound on the 4.25
+//     bits per weight.  A wave streams
+//     four weight rows at a time with 1 KiB-contiguous loads; every lane keeps 32 channels
+//     (one quarter of a group) and their activations.  A nibble becomes a float through a byte
+//     mask and v_cvt_f32_ubyte (1.4 instructions per code), and the group's scale is applied
+//     once per 32 channels: sum_k x_k Delta (q_k - z) = Delta (sum_k x_k q_k - z sum_k x_k).
+//     Products x q are exact in fp32; only the fp32 sums round.
+//   * prefill, M > 8: the bf16 matrix cores.  A 128-row tile of W_hat is decoded per 32-channel
+//     chunk into LDS as bf16 (Delta (q - z) rounded once to bf16), X' is staged as bf16, and
+//     each of four waves accumulates 128 tokens x 128 outputs in fp32.
+#include "awq_internal.h"
+
+namespace awq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+// byte c of x as a float (one v_cvt_f32_ubyte<c>)
+template <int C>
+__device__ __forceinline__ float ubyte(uint32_t x) { return (float)((x >> (8 * C)) & 0xffu); }
+
+// ---- decode ------------------------------------------------------------------------------
+constexpr int kGvRows = 4;     // weight rows per wave step
+constexpr int kGvThreads = 256;
+
+// K is covered in passes of kc channels (4096 for up to two tokens, else 2048): X of the pass
+// is staged in LDS as fp32 [M][kc] (at most 64 KiB), then every wave streams its rows over
+// the pass.  Lane l owns, per 1 KiB segment t of a row's words, words 4 (64 t + l) .. + 3,
+// i.e. 32 channels, a quarter of one group.  The wave that owns row n adds each pass's sum
+// into Y itself, so the result does not depend on scheduling.
+template <int M, bool XF32>
+__global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
+    const void* __restrict__ X, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
+    float* __restrict__ Y, int64_t ldy, int64_t kc) {
+  extern __shared__ float xs[];  // [M][kc]
+  const int64_t G = K / kGroup;
+  const int64_t words = K / 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kGvThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kGvThreads) >> 6;
+  for (int64_t c0 = 0; c0 < K; c0 += kc) {
+    const int64_t kw = K - c0 < kc ? K - c0 : kc;  // channels in this pass (a multiple of 128)
+    __syncthreads();  // the previous pass is done with xs
+    for (int64_t i = threadIdx.x; i < (int64_t)M * kw; i += kGvThreads) {
+      const int64_t m = i / kw, k = i - m * kw;
+      xs[m * kc + k] = XF32 ? static_cast<const float*>(X)[m * ldx + c0 + k]
+                            : __uint_as_float((uint32_t)static_cast<const uint16_t*>(X)[m * ldx + c0 + k] << 16);
+    }
+    __syncthreads();
+    const int64_t pw = kw / 8;                 // words of a row in this pass
+    const int64_t segs = (pw + 255) / 256;
+    for (int64_t n0 = wave * kGvRows; n0 < N; n0 += nwaves * kGvRows) {
+      float acc[kGvRows][M];
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+      for (int64_t t = 0; t < segs; ++t) {
+        const int64_t lw = 4 * (64 * t + lane);  // first word of this lane within the pass
+        if (lw >= pw) continue;
+        const int64_t w0 = c0 / 8 + lw;
+        const int64_t g = (8 * w0) / kGroup;
+        uint4 qv[kGvRows];
+        float d[kGvRows], z[kGvRows];
+#pragma unroll
+        for (int r = 0; r < kGvRows; ++r) {
+          const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: load row N-1, store nothing
+          qv[r] = *reinterpret_cast<const uint4*>(qweight + n * words + w0);
+          d[r] = h2f(scales[n * G + g]);
+          z[r] = h2f(zeros[n * G + g]);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float* xr = xs + (int64_t)m * kc + 8 * lw;
+          float sx = 0.0f, sq[kGvRows];
+#pragma unroll
+          for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {  // word j: codes 8 j .. 8 j + 7
+            const float4 xa = *reinterpret_cast<const float4*>(xr + 8 * j);
+            const float4 xb = *reinterpret_cast<const float4*>(xr + 8 * j + 4);
+            const float x8[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sx += x8[c];
+#pragma unroll
+            for (int r = 0; r < kGvRows; ++r) {
+              const uint32_t w = j == 0 ? qv[r].x : j == 1 ? qv[r].y : j == 2 ? qv[r].z : qv[r].w;
+              const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;  // codes 0,2,4,6 / 1,3,5,7
+              sq[r] = fmaf(x8[0], ubyte<0>(ev), sq[r]);
+              sq[r] = fmaf(x8[1], ubyte<0>(od), sq[r]);
+              sq[r] = fmaf(x8[2], ubyte<1>(ev), sq[r]);
+              sq[r] = fmaf(x8[3], ubyte<1>(od), sq[r]);
+              sq[r] = fmaf(x8[4], ubyte<2>(ev), sq[r]);
+              sq[r] = fmaf(x8[5], ubyte<2>(od), sq[r]);
+              sq[r] = fmaf(x8[6], ubyte<3>(ev), sq[r]);
+              sq[r] = fmaf(x8[7], ubyte<3>(od), sq[r]);
+            }
+          }
+          // Delta (sum x q - z sum x) for this quarter group
+#pragma unroll
+          for (int r = 0; r < kGvRows; ++r) acc[r][m] = fmaf(d[r], fmaf(-z[r], sx, sq[r]), acc[r][m]);
+        }
+      }
+      // sum over the wave's lanes, one row and token at a time
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float v = acc[r][m];
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+          if (lane == 0 && n0 + r < N) {
+            float* y = Y + (int64_t)m * ldy + n0 + r;
+            *y = c0 == 0 ? v : *y + v;
+          }
+        }
+    }
+  }
+}
+
+// ---- prefill -------------------------------------------------------------------------------
+constexpr int PBM = 512, PBN = 128, PKC = 32, PPITCH = PKC + 8;
+
+__device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
+  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
+    float* __restrict__ Y, int64_t ldy, int64_t ntiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][PBM][PPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][PBN][PPITCH];
+  const int64_t G = K / kGroup, words = K / 8;
+  const int64_t mt = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
+  const int64_t m0 = mt * PBM, n0 = nt * PBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // X chunk: 512 rows x 64 bytes, thread: rows tid / 4 + 64 i, piece tid % 4 (16 bytes)
+  const int xkp = tid & 3, xr0 = tid >> 2;
+  const int64_t xbytes = (M - m0) * ldx * 2;
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
+  // W chunk: 128 rows x 4 words (32 channels); thread: row tid / 2, words 2 (tid % 2) .. + 1
+  const int wr = tid >> 1, wq = tid & 1;
+  const int64_t wn = n0 + wr;
+  const bool wlive = wn < N;
+  const int32_t* wrow = qweight + (wlive ? wn : 0) * words;
+  uint4 xv[8];
+  uint2 qv;
+  float dv, zv;
+  auto load = [&](int64_t c) {
+    const uint32_t kb = (uint32_t)(c * PKC);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xrsrc, (int)((xr0 + 64 * i) * ldx * 2 + kb * 2 + xkp * 16), 0, 0));
+    qv = *reinterpret_cast<const uint2*>(wrow + kb / 8 + 2 * wq);
+    const int64_t g = kb / kGroup;
+    dv = wlive ? h2f(scales[(wlive ? wn : 0) * G + g]) : 0.0f;  // rows past N: weight 0
+    zv = h2f(zeros[(wlive ? wn : 0) * G + g]);
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&xs[b][xr0 + 64 * i][xkp * 8]) = xv[i];
+    uint32_t pk[8];
+    const uint32_t wv[2] = {qv.x, qv.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float a = dv * ((float)((wv[j] >> (8 * c)) & 15u) - zv);      // exact in fp32
+        const float bq = dv * ((float)((wv[j] >> (8 * c + 4)) & 15u) - zv);
+        pk[4 * j + c] = bf16x2_of(a, bq);
+      }
+    *reinterpret_cast<uint4*>(&ws[b][wr][wq * 16]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(&ws[b][wr][wq * 16 + 8]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  const int64_t nch = K / PKC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int64_t c = 0; c < nch; ++c) {
+    const int b = (int)(c & 1);
+    load(c + 1 < nch ? c + 1 : c);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) bfr[cc] = *reinterpret_cast<const bf16x8*>(&ws[b][cc * 32 + frow][h * 16 + fk]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) af[r] = *reinterpret_cast<const bf16x8*>(&xs[b][wave * 128 + r * 32 + frow][h * 16 + fk]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[r], bfr[cc], acc[r][cc], 0, 0, 0);
+    }
+    store(b ^ 1);
+    __syncthreads();
+  }
+  // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t m = m0 + wave * 128 + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+        const int64_t n = n0 + cc * 32 + (lane % 32);
+        if (m < M && n < N) Y[m * ldy + n] = acc[r][cc][i];
+      }
+}
+
+}  // namespace
+
+// channels per decode pass: X of one pass takes at most 64 KiB of LDS (fp32)
+int64_t w4a16_gemv_kc(int64_t M) { return M <= 2 ? 4096 : 2048; }
+
+hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, float* Y, int64_t ldy,
+                        hipStream_t st) {
+  if (!xf32 && M > kW4a16GemvMax) {
+    const int64_t mtiles = (M + PBM - 1) / PBM, ntiles = (N + PBN - 1) / PBN;
+    w4a16_gemm_kernel<<<(unsigned)(mtiles * ntiles), 256, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, K,
+                                                                   qweight, scales, zeros, N, Y, ldy, ntiles);
+    return hipGetLastError();
+  }
+  // decode path, up to 8 tokens per launch (fp32 X always takes it)
+  const int64_t waves = (N + kGvRows - 1) / kGvRows;
+  int64_t blocks = (waves + 3) / 4;
+  if (blocks > 1024) blocks = 1024;
+  for (int64_t m0 = 0; m0 < M; m0 += kW4a16GemvMax) {
+    const int64_t mb = M - m0 < kW4a16GemvMax ? M - m0 : kW4a16GemvMax;
+    const char* xp = static_cast<const char*>(X) + m0 * ldx * (xf32 ? 4 : 2);
+    float* yp = Y + m0 * ldy;
+    const int64_t kc = w4a16_gemv_kc(mb);
+    const size_t lds = (size_t)mb * (size_t)kc * 4;
+#define AWQ_GV(MV)                                                                                       \
+  do {                                                                                                   \
+    if (xf32)                                                                                            \
+      w4a16_gemv_kernel<MV, true><<<(unsigned)blocks, kGvThreads, lds, st>>>(xp, ldx, K, qweight, scales, \
+                                                                            zeros, N, yp, ldy, kc);      \
+    else                                                                                                 \
+      w4a16_gemv_kernel<MV, false><<<(unsigned)blocks, kGvThreads, lds, st>>>(xp, ldx, K, qweight, scales, \
+                                                                             zeros, N, yp, ldy, kc);     \
+  } while (0)
+    switch (mb) {
+      case 1: AWQ_GV(1); break;
+      case 2: AWQ_GV(2); break;
+      case 3: AWQ_GV(3); break;
+      case 4: AWQ_GV(4); break;
+      case 5: AWQ_GV(5); break;
+      case 6: AWQ_GV(6); break;
+      case 7: AWQ_GV(7); break;
+      default: AWQ_GV(8); break;
+    }
+#undef AWQ_GV
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace awq

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
                           "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack",
                           "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip", "awq_fold_rows",
-                          "awq_scale_cols", "awq_scaled_act"}
+                          "awq_scale_cols", "awq_scaled_act", "awq_w4a16"}
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 3
+    assert L.awq_abi_version() == 4
     for st in range(6):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
@@ -184,3 +184,16 @@ def test_scaled_act_argument_errors(L, kw, status):
     a = dict(X=P, Y=P, dt=F32, M=8, K=16, ld=16, act=0, s=P, fl=P)
     a.update(kw)
     assert L.awq_scaled_act(a["X"], a["Y"], a["dt"], a["M"], a["K"], a["ld"], a["act"], a["s"], a["fl"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(q=None), INVALID), (dict(sc=None), INVALID), (dict(z=None), INVALID),
+    (dict(Y=None), INVALID), (dict(N=0), INVALID), (dict(ldy=127), INVALID), (dict(q=P + 4), INVALID),
+    (dict(sc=P + 1), INVALID), (dict(Y=P + 2), INVALID), (dict(group=64), UNSUP), (dict(xt=4), UNSUP),
+    (dict(K=200, ldx=200), SHAPE), (dict(ldx=1 << 21), SHAPE),
+])
+def test_w4a16_argument_errors(L, kw, status):
+    a = dict(X=P, xt=BF16, M=4, K=256, ldx=256, q=P, sc=P, z=P, N=128, group=128, Y=P, ldy=128)
+    a.update(kw)
+    assert L.awq_w4a16(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["q"], a["sc"], a["z"], a["N"], a["group"],
+                       a["Y"], a["ldy"], None) == status

@@ -1,0 +1,111 @@
+"""GPU parity of the W4A16 product over the packed artefact ("AWQ：为什么 4-bit 权重量化要先观察
+Activation", §7, §8) against the oracle's exact product, on artefacts the oracle packed.
+Decode (<= 8 bf16 tokens, or fp32 tokens): products exact in fp32, fp32 sums, the group scale
+applied to partial sums, so the bound is a few dozen fp32 roundings of sum |x| Delta (q + z + 1).
+Prefill (> 8 bf16 tokens): the decoded weight is rounded once to bf16 for the matrix cores,
+so the bound adds 2^-8 sum |x| |W_hat| and K 2^-24 of fp32 accumulation."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import awq_oracle as o
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_weight_quantization_mean_amd import awq as _awq
+    _awq.lib()
+    return _awq
+
+
+def banner(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def artefact(N, K, seed):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)
+    s = np.exp(0.3 * rng.standard_normal(K)).astype(np.float32)
+    return o.pack(W, s)
+
+
+def run(awq, art, X, prefill):
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    sc = torch.from_numpy(art["scales"].view(np.float16)).to(DEV)
+    zz = torch.from_numpy(art["zeros"].view(np.float16)).to(DEV)
+    Y = awq.w4a16(X.to(DEV), q, sc, zz).cpu().numpy().astype(np.float64)
+    X64 = X.float().numpy().astype(np.float64)
+    ref = o.w4a16_matmul(X64, art["qweight"], art["scales"], art["zeros"])
+    Wh = o.dequant_artefact(art["qweight"], art["scales"], art["zeros"])
+    K = X64.shape[1]
+    codes = o.unpack_words(art["qweight"]).astype(np.float64)
+    d = art["scales"].astype(np.float64).repeat(128, axis=1)
+    z = art["zeros"].astype(np.float64).repeat(128, axis=1)
+    mag = np.abs(X64) @ (d * (codes + z + 1.0)).T  # sum |x| Delta (q + z + 1)
+    tol = 64 * 2.0 ** -24 * mag
+    if prefill:
+        tol = tol + (2.0 ** -8 + K * 2.0 ** -24) * (np.abs(X64) @ np.abs(Wh).T)
+    err = np.abs(Y - ref)
+    bad = np.argwhere(err > tol + 1e-30)
+    assert bad.size == 0, f"{len(bad)} outputs outside tolerance, first {bad[:4].tolist()}"
+    return float(np.max(err / np.maximum(np.abs(ref), 1e-30)))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 256), (3, 14336, 130), (8, 384, 64), (2, 5120, 4)])
+def test_decode_bf16(awq, M, K, N):
+    banner(f"w4a16 decode M={M} K={K} N={N}")
+    art = artefact(N, K, 1)
+    X = torch.from_numpy(np.random.default_rng(2).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    run(awq, art, X, prefill=False)
+
+
+def test_decode_fp32_many_tokens(awq):
+    """fp32 activations take the decode kernel at any M, eight tokens per launch."""
+    art = artefact(96, 1024, 3)
+    X = torch.from_numpy(np.random.default_rng(4).standard_normal((20, 1024)).astype(np.float32))
+    run(awq, art, X, prefill=False)
+
+
+@pytest.mark.parametrize("M,K,N", [(9, 512, 128), (600, 4096, 200), (1024, 1024, 384)])
+def test_prefill_bf16(awq, M, K, N):
+    banner(f"w4a16 prefill M={M} K={K} N={N}")
+    art = artefact(N, K, 5)
+    X = torch.from_numpy(np.random.default_rng(6).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    run(awq, art, X, prefill=True)
+
+
+def test_strided_activations_and_output(awq):
+    art = artefact(64, 512, 7)
+    full = torch.from_numpy(np.random.default_rng(8).standard_normal((4, 640)).astype(np.float32)).to(torch.bfloat16)
+    Xd = full.to(DEV)[:, :512]  # row stride 640
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    sc = torch.from_numpy(art["scales"].view(np.float16)).to(DEV)
+    zz = torch.from_numpy(art["zeros"].view(np.float16)).to(DEV)
+    Yfull = torch.full((4, 80), -7.0, device=DEV)
+    awq.w4a16(Xd, q, sc, zz, out=Yfull[:, :64])
+    ref = o.w4a16_matmul(full[:, :512].float().numpy(), art["qweight"], art["scales"], art["zeros"])
+    assert np.allclose(Yfull[:, :64].cpu().numpy(), ref, rtol=1e-4, atol=1e-5)
+    assert torch.all(Yfull[:, 64:] == -7.0)  # outside the output view: untouched
+
+
+def test_scaled_inputs_recover_the_layer(awq):
+    """GPU chain: pack S W on the GPU, feed X / s: the W4A16 output approximates X W^T within the
+    quantization error bound |E| <= Delta / (2 s), plus |q - z| times the fp16 rounding of Delta."""
+    rng = np.random.default_rng(9)
+    M, K, N = 16, 1024, 256
+    W = torch.from_numpy((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)).to(torch.bfloat16)
+    s = torch.from_numpy(np.exp(0.3 * rng.standard_normal(K)).astype(np.float32))
+    X = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))
+    q, sc, zz = awq.pack(W.to(DEV), s.to(DEV))
+    Xs = (X / s[None, :]).to(DEV)  # fp32 activations carrying S^-1
+    Y = awq.w4a16(Xs, q, sc, zz).cpu().double()
+    exact = X.double() @ W.double().T
+    # |v - Delta16 (q - z)| <= Delta / 2 + |q - z| Delta 2^-11 <= Delta16 (1/2 + 16 2^-11)
+    dW = sc.cpu().double().repeat_interleave(128, dim=1) * (0.5 + 16 * 2.0 ** -11) / s.double()[None, :]
+    bound = X.double().abs() @ dW.T + 1e-4 * (X.double().abs() @ W.double().abs().T)
+    assert torch.all((Y - exact).abs() <= bound)

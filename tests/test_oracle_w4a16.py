@@ -54,7 +54,7 @@ def test_w4a16_undoes_the_scaling():
     art = o.pack(W, s)
     Y = o.w4a16_matmul(X / s[None, :].astype(np.float64), art["qweight"], art["scales"], art["zeros"])
     # each weight is off by at most Delta/2 / s in the original units (codes in range), plus
-    # the fp16 rounding of Delta
-    dW = (art["scales"].astype(np.float64).repeat(128, axis=1) * 0.5 * (1 + 2.0 ** -10)) / s[None, :]
+    # |q - z| <= 15 times the fp16 rounding of Delta (2^-11 relative)
+    dW = (art["scales"].astype(np.float64).repeat(128, axis=1) * (0.5 + 16 * 2.0 ** -11)) / s[None, :]
     bound = np.abs(X) @ dW.T
     assert np.all(np.abs(Y - X @ W.astype(np.float64).T) <= bound + 1e-12)
