@@ -134,6 +134,35 @@ def clip_search(torch, awq, Xd, Wd, s_best, stride: int = 8, reps: int = 10):
             "note": "whole awq_clip call (range pre-pass, clipped qdq + bf16 MFMA product, select)"}
 
 
+def w4a16_products(torch, awq, dev, reps: int = 10):
+    """The W4A16 product over a packed artefact of the decoder block's fused gate+up weight
+    (N = 28672, K = 4096): decode with one token (HBM-bound: 0.53125 bytes per weight, the
+    last-level cache flushed between calls) and prefill with 4096 tokens (MFMA-bound,
+    2 M K N flop).  The artefact is packed on the GPU from a seeded bf16 weight."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    N, K = 28672, 4096
+    W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
+    s = torch.exp(0.25 * torch.randn(K, generator=g, device=dev, dtype=torch.float32))
+    q, sc, zz = awq.pack(W, s)
+    del W
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    x1 = torch.randn((1, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    ms_d = _time_reps(torch, lambda: awq.w4a16(x1, q, sc, zz, out=y1), reps, flush)
+    bytes_d = N * K * 0.5 + N * (K // 128) * 4.0 + K * 2.0 + N * 4.0
+    M = 4096
+    xp = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    yp = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ms_p = _time_reps(torch, lambda: awq.w4a16(xp, q, sc, zz, out=yp), max(3, reps // 2))
+    flop = 2.0 * M * K * N
+    return {"decode": {"tokens": 1, "shape": [N, K], "ms": ms_d, "bytes": bytes_d,
+                       "gbs": bytes_d / (ms_d * 1e-3) / 1e9, "frac_hbm": bytes_d / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "prefill": {"tokens": M, "shape": [N, K], "ms": ms_p, "flop": flop,
+                        "tflops": flop / (ms_p * 1e-3) / 1e12,
+                        "frac_mfma_peak": flop / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+
+
 def _time_reps(torch, fn, reps, flush=None):
     """Median of reps event-timed calls.  flush, when given, is a buffer larger than the
     last-level cache that is overwritten between calls (outside the timed intervals), so that
@@ -177,6 +206,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096, help="output channels of the oracle sample")
     ap.add_argument("--no-hbm", action="store_true", help="skip the large-input stats / pack timing")
     ap.add_argument("--no-clip", action="store_true", help="skip the clipping-search timing")
+    ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 product timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -293,6 +323,8 @@ def main():
         out["clip"] = clip_search(torch, awq, Xd, Wd, res.s_best)
     if not args.no_hbm:
         out["hbm"] = hbm_kernels(torch, awq, dev)
+    if not args.no_w4a16:
+        out["w4a16"] = w4a16_products(torch, awq, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
     print(json.dumps(out), flush=True)
