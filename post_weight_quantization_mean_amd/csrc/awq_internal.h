@@ -54,6 +54,20 @@ __device__ __forceinline__ float min16(float x) {
   return fminf(x, dpp<kDppMirror>(x));
 }
 
+// sum over the 64 lanes of a wave, the same value in every lane: DPP butterflies within each
+// 16-lane row, then the four row sums read from lanes 0, 16, 32, 48 (no LDS round trip)
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return (a + b) + (c + d);
+}
+
 // ---- search ----------------------------------------------------------------------------
 constexpr int kSearchBM = 512;  // tokens per block tile
 constexpr int kSearchBN = 128;  // output channels per block tile

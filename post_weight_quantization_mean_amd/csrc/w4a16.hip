@@ -24,6 +24,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 // byte c of x as a float (one v_cvt_f32_ubyte<c>)
@@ -53,79 +54,123 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
   for (int64_t c0 = 0; c0 < K; c0 += kc) {
     const int64_t kw = K - c0 < kc ? K - c0 : kc;  // channels in this pass (a multiple of 128)
     __syncthreads();  // the previous pass is done with xs
-    for (int64_t i = threadIdx.x; i < (int64_t)M * kw; i += kGvThreads) {
-      const int64_t m = i / kw, k = i - m * kw;
-      xs[m * kc + k] = XF32 ? static_cast<const float*>(X)[m * ldx + c0 + k]
-                            : __uint_as_float((uint32_t)static_cast<const uint16_t*>(X)[m * ldx + c0 + k] << 16);
+    {  // 16-byte pieces (8 bf16 or 4 fp32 values), four in flight per thread
+      constexpr int PE = XF32 ? 4 : 8;
+      const int64_t pieces = (int64_t)M * kw / PE;
+      for (int64_t i0 = threadIdx.x; i0 < pieces; i0 += 4 * kGvThreads) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t i = i0 + u * kGvThreads;
+          if (i < pieces) {
+            const int64_t m = (i * PE) / kw, k = i * PE - m * kw;
+            v[u] = *reinterpret_cast<const uint4*>(static_cast<const char*>(X) + (m * ldx + c0 + k) * (XF32 ? 4 : 2));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t i = i0 + u * kGvThreads;
+          if (i < pieces) {
+            const int64_t m = (i * PE) / kw, k = i * PE - m * kw;
+            float* dst = xs + m * kc + k;
+            if constexpr (XF32) {
+              *reinterpret_cast<uint4*>(dst) = v[u];
+            } else {
+              const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+              *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                                            __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+              *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                                                __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+            }
+          }
+        }
+      }
     }
     __syncthreads();
     const int64_t pw = kw / 8;                 // words of a row in this pass
     const int64_t segs = (pw + 255) / 256;
-    for (int64_t n0 = wave * kGvRows; n0 < N; n0 += nwaves * kGvRows) {
+    // the weight words, scales and zero points of one row group and segment, loaded one step
+    // ahead of their use so that the next loads are in flight during the current math
+    struct Slab {
+      u32x4 q[kGvRows];
+      float d[kGvRows], z[kGvRows];
+    };
+    auto fetch = [&](int64_t n0, int64_t t, Slab& S) {
+      const int64_t lw = 4 * (64 * t + lane);
+      const int64_t w0 = c0 / 8 + (lw < pw ? lw : 0);
+      const int64_t g = (8 * w0) / kGroup;
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: load row N-1, store nothing
+        S.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qweight + n * words + w0));
+        S.d[r] = h2f(scales[n * G + g]);
+        S.z[r] = h2f(zeros[n * G + g]);
+      }
+    };
+    const int64_t step = nwaves * kGvRows;
+    Slab cur, nxt;
+    int64_t n0 = wave * kGvRows, t = 0;
+    if (n0 < N) fetch(n0, 0, cur);
+    while (n0 < N) {
       float acc[kGvRows][M];
 #pragma unroll
       for (int r = 0; r < kGvRows; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-      for (int64_t t = 0; t < segs; ++t) {
+      for (t = 0; t < segs; ++t) {
+        // next (row group, segment) in this wave's order
+        const bool last_seg = t + 1 == segs;
+        const int64_t nn = last_seg ? n0 + step : n0, tn = last_seg ? 0 : t + 1;
+        if (nn < N) fetch(nn, tn, nxt);
         const int64_t lw = 4 * (64 * t + lane);  // first word of this lane within the pass
-        if (lw >= pw) continue;
-        const int64_t w0 = c0 / 8 + lw;
-        const int64_t g = (8 * w0) / kGroup;
-        uint4 qv[kGvRows];
-        float d[kGvRows], z[kGvRows];
+        if (lw < pw) {
+          const int64_t k0 = 8 * lw;
 #pragma unroll
-        for (int r = 0; r < kGvRows; ++r) {
-          const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: load row N-1, store nothing
-          qv[r] = *reinterpret_cast<const uint4*>(qweight + n * words + w0);
-          d[r] = h2f(scales[n * G + g]);
-          z[r] = h2f(zeros[n * G + g]);
-        }
+          for (int m = 0; m < M; ++m) {
+            const float* xr = xs + (int64_t)m * kc + k0;
+            float sx = 0.0f, sq[kGvRows];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float* xr = xs + (int64_t)m * kc + 8 * lw;
-          float sx = 0.0f, sq[kGvRows];
+            for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
 #pragma unroll
-          for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
+            for (int j = 0; j < 4; ++j) {  // word j: codes 8 j .. 8 j + 7
+              const float4 xa = *reinterpret_cast<const float4*>(xr + 8 * j);
+              const float4 xb = *reinterpret_cast<const float4*>(xr + 8 * j + 4);
+              const float x8[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {  // word j: codes 8 j .. 8 j + 7
-            const float4 xa = *reinterpret_cast<const float4*>(xr + 8 * j);
-            const float4 xb = *reinterpret_cast<const float4*>(xr + 8 * j + 4);
-            const float x8[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+              for (int c = 0; c < 8; ++c) sx += x8[c];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) sx += x8[c];
-#pragma unroll
-            for (int r = 0; r < kGvRows; ++r) {
-              const uint32_t w = j == 0 ? qv[r].x : j == 1 ? qv[r].y : j == 2 ? qv[r].z : qv[r].w;
-              const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;  // codes 0,2,4,6 / 1,3,5,7
-              sq[r] = fmaf(x8[0], ubyte<0>(ev), sq[r]);
-              sq[r] = fmaf(x8[1], ubyte<0>(od), sq[r]);
-              sq[r] = fmaf(x8[2], ubyte<1>(ev), sq[r]);
-              sq[r] = fmaf(x8[3], ubyte<1>(od), sq[r]);
-              sq[r] = fmaf(x8[4], ubyte<2>(ev), sq[r]);
-              sq[r] = fmaf(x8[5], ubyte<2>(od), sq[r]);
-              sq[r] = fmaf(x8[6], ubyte<3>(ev), sq[r]);
-              sq[r] = fmaf(x8[7], ubyte<3>(od), sq[r]);
+              for (int r = 0; r < kGvRows; ++r) {
+                const uint32_t w = j == 0 ? cur.q[r].x : j == 1 ? cur.q[r].y : j == 2 ? cur.q[r].z : cur.q[r].w;
+                const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;  // codes 0,2,4,6 / 1,3,5,7
+                sq[r] = fmaf(x8[0], ubyte<0>(ev), sq[r]);
+                sq[r] = fmaf(x8[1], ubyte<0>(od), sq[r]);
+                sq[r] = fmaf(x8[2], ubyte<1>(ev), sq[r]);
+                sq[r] = fmaf(x8[3], ubyte<1>(od), sq[r]);
+                sq[r] = fmaf(x8[4], ubyte<2>(ev), sq[r]);
+                sq[r] = fmaf(x8[5], ubyte<2>(od), sq[r]);
+                sq[r] = fmaf(x8[6], ubyte<3>(ev), sq[r]);
+                sq[r] = fmaf(x8[7], ubyte<3>(od), sq[r]);
+              }
             }
-          }
-          // Delta (sum x q - z sum x) for this quarter group
+            // Delta (sum x q - z sum x) for this quarter group
 #pragma unroll
-          for (int r = 0; r < kGvRows; ++r) acc[r][m] = fmaf(d[r], fmaf(-z[r], sx, sq[r]), acc[r][m]);
+            for (int r = 0; r < kGvRows; ++r) acc[r][m] = fmaf(cur.d[r], fmaf(-cur.z[r], sx, sq[r]), acc[r][m]);
+          }
         }
+        cur = nxt;
       }
       // sum over the wave's lanes, one row and token at a time
 #pragma unroll
       for (int r = 0; r < kGvRows; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          float v = acc[r][m];
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+          const float v = wave_sum(acc[r][m]);
           if (lane == 0 && n0 + r < N) {
             float* y = Y + (int64_t)m * ldy + n0 + r;
             *y = c0 == 0 ? v : *y + v;
           }
         }
+      n0 += step;
     }
   }
 }
