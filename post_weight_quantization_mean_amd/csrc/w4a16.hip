@@ -6,7 +6,8 @@
 //
 // Two kernels:
 //   * decode, M <= 8 tokens (more with fp32 X, eight per launch): bandwidth-bound on the 4.25
-//     bits per weight.  A wave streams
+//     bits per weight (bf16 activations use the two-products-per-instruction variant below the
+//     fp32 one).  A wave streams
 //     four weight rows at a time with 1 KiB-contiguous loads; every lane keeps 32 channels
 //     (one quarter of a group) and their activations.  A nibble becomes a float through a byte
 //     mask and v_cvt_f32_ubyte (1.4 instructions per code), and the group's scale is applied
@@ -32,7 +33,10 @@ template <int C>
 __device__ __forceinline__ float ubyte(uint32_t x) { return (float)((x >> (8 * C)) & 0xffu); }
 
 // ---- decode ------------------------------------------------------------------------------
-constexpr int kGvRows = 4;     // weight rows per wave step
+#ifndef AWQ_GV_ROWS
+#define AWQ_GV_ROWS 4
+#endif
+constexpr int kGvRows = AWQ_GV_ROWS;  // weight rows per wave step
 constexpr int kGvThreads = 256;
 
 // K is covered in passes of kc channels (4096 for up to two tokens, else 2048): X of the pass
@@ -175,6 +179,138 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
   }
 }
 
+// bf16 activations: the same layout with two products per instruction.  A word's eight codes
+// become four bf16 pairs (q_i, q_{i+4}) biased to 128 + q (bf16 with exponent 2^7 holds the
+// integers 128..255 exactly: bits 0x4300 | q), and v_dot2_f32_bf16 multiplies them with the
+// activation pairs (x_i, x_{i+4}), staged in LDS in that order.  The bias comes off once per
+// quarter group: sum x q - z sum x = sum x (128 + q) - (128 + z) sum x.  Products are exact;
+// the sums carry the bias, so their rounding is relative to sum |x| (128 + q), about 2^7 times
+// the unbiased sum's (still far below the bf16 precision of the activations).
+template <int M>
+__global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
+    float* __restrict__ Y, int64_t ldy, int64_t kc) {
+  extern __shared__ uint32_t xp[];  // [M][kc / 2] bf16 pairs, (x_i, x_{i+4}) per 8 channels
+  typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
+  const int64_t G = K / kGroup;
+  const int64_t words = K / 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kGvThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kGvThreads) >> 6;
+  const int64_t step = nwaves * kGvRows;
+  auto dot = [](uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfx2, a), __builtin_bit_cast(bfx2, b), c, false);
+  };
+  for (int64_t c0 = 0; c0 < K; c0 += kc) {
+    const int64_t kw = K - c0 < kc ? K - c0 : kc;  // a multiple of 128
+    __syncthreads();
+    {  // 8 channels (16 bytes) per piece, four pieces in flight per thread
+      const int64_t pieces = (int64_t)M * kw / 8;
+      for (int64_t i0 = threadIdx.x; i0 < pieces; i0 += 4 * kGvThreads) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t i = i0 + u * kGvThreads;
+          if (i < pieces) {
+            const int64_t m = (i * 8) / kw, k = i * 8 - m * kw;
+            v[u] = *reinterpret_cast<const uint4*>(X + m * ldx + c0 + k);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t i = i0 + u * kGvThreads;
+          if (i < pieces) {
+            const int64_t m = (i * 8) / kw, k = i * 8 - m * kw;
+            // (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+            const uint32_t a = v[u].x, b = v[u].y, c = v[u].z, d = v[u].w;
+            *reinterpret_cast<uint4*>(xp + m * (kc / 2) + k / 2) =
+                make_uint4((a & 0xffffu) | (c << 16), (a >> 16) | (c & 0xffff0000u),
+                           (b & 0xffffu) | (d << 16), (b >> 16) | (d & 0xffff0000u));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int64_t pw = kw / 8;
+    const int64_t segs = (pw + 255) / 256;  // <= kDotSegs
+    struct Slab {
+      u32x4 q[kGvRows];
+      float d[kGvRows], z[kGvRows];
+    };
+    auto fetch = [&](int64_t n0, int64_t t, Slab& S) {
+      const int64_t lw = 4 * (64 * t + lane);
+      const int64_t w0 = c0 / 8 + (lw < pw ? lw : 0);
+      const int64_t g = (8 * w0) / kGroup;
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: load row N-1, store nothing
+        S.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qweight + n * words + w0));
+        S.d[r] = h2f(scales[n * G + g]);
+        S.z[r] = h2f(zeros[n * G + g]);
+      }
+    };
+    Slab cur, nxt;
+    int64_t n0 = wave * kGvRows;
+    if (n0 < N) fetch(n0, 0, cur);
+    while (n0 < N) {
+      float acc[kGvRows][M];
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+      for (int64_t t = 0; t < segs; ++t) {
+        {
+          const bool last_seg = t + 1 == segs;
+          const int64_t nn = last_seg ? n0 + step : n0, tn = last_seg ? 0 : t + 1;
+          if (nn < N) fetch(nn, tn, nxt);
+          const int64_t lw = 4 * (64 * t + lane);
+          if (lw < pw) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              const uint32_t* xr = xp + (int64_t)m * (kc / 2) + 4 * lw;
+              float sq[kGvRows], sxm = 0.0f;  // sxm: sum of the lane's 32 activations
+#pragma unroll
+              for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint4 x4 = *reinterpret_cast<const uint4*>(xr + 4 * j);
+                sxm = dot(x4.x, 0x3f803f80u, sxm);  // (1, 1) in bf16
+                sxm = dot(x4.y, 0x3f803f80u, sxm);
+                sxm = dot(x4.z, 0x3f803f80u, sxm);
+                sxm = dot(x4.w, 0x3f803f80u, sxm);
+#pragma unroll
+                for (int r = 0; r < kGvRows; ++r) {
+                  const uint32_t w = j == 0 ? cur.q[r].x : j == 1 ? cur.q[r].y : j == 2 ? cur.q[r].z : cur.q[r].w;
+                  sq[r] = dot(x4.x, (w & 0x000f000fu) | 0x43004300u, sq[r]);
+                  sq[r] = dot(x4.y, ((w >> 4) & 0x000f000fu) | 0x43004300u, sq[r]);
+                  sq[r] = dot(x4.z, ((w >> 8) & 0x000f000fu) | 0x43004300u, sq[r]);
+                  sq[r] = dot(x4.w, ((w >> 12) & 0x000f000fu) | 0x43004300u, sq[r]);
+                }
+              }
+#pragma unroll
+              for (int r = 0; r < kGvRows; ++r)
+                acc[r][m] = fmaf(cur.d[r], fmaf(-(128.0f + cur.z[r]), sxm, sq[r]), acc[r][m]);
+            }
+          }
+          cur = nxt;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float v = wave_sum(acc[r][m]);
+          if (lane == 0 && n0 + r < N) {
+            float* y = Y + (int64_t)m * ldy + n0 + r;
+            *y = c0 == 0 ? v : *y + v;
+          }
+        }
+      n0 += step;
+    }
+  }
+}
+
 // ---- prefill -------------------------------------------------------------------------------
 constexpr int PBM = 512, PBN = 128, PKC = 32, PPITCH = PKC + 8;
 
@@ -300,10 +436,15 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
     const char* xp = static_cast<const char*>(X) + m0 * ldx * (xf32 ? 4 : 2);
     float* yp = Y + m0 * ldy;
     const int64_t kc = w4a16_gemv_kc(mb);
+    const int64_t kcd = mb <= 2 ? 8192 : 4096;  // bf16 pairs: at most 64 KiB, 4 segments
     const size_t lds = (size_t)mb * (size_t)kc * 4;
 #define AWQ_GV(MV)                                                                                       \
   do {                                                                                                   \
-    if (xf32)                                                                                            \
+    if (!xf32)                                                                                           \
+      w4a16_gemv_dot_kernel<MV><<<(unsigned)blocks, kGvThreads, (size_t)mb * kcd * 2, st>>>(            \
+          static_cast<const uint16_t*>(static_cast<const void*>(xp)), ldx, K, qweight, scales, zeros, N, \
+          yp, ldy, kcd);                                                                                 \
+    else if (xf32)                                                                                       \
       w4a16_gemv_kernel<MV, true><<<(unsigned)blocks, kGvThreads, lds, st>>>(xp, ldx, K, qweight, scales, \
                                                                             zeros, N, yp, ldy, kc);      \
     else                                                                                                 \

@@ -1,7 +1,8 @@
 """GPU parity of the W4A16 product over the packed artefact ("AWQ：为什么 4-bit 权重量化要先观察
 Activation", §7, §8) against the oracle's exact product, on artefacts the oracle packed.
 Decode (<= 8 bf16 tokens, or fp32 tokens): products exact in fp32, fp32 sums, the group scale
-applied to partial sums, so the bound is a few dozen fp32 roundings of sum |x| Delta (q + z + 1).
+applied to partial sums, so the bound is a few dozen fp32 roundings of sum |x| Delta (q + z + 1)
+(with bf16 tokens the sums carry a bias of 128 per code: q + z + 257).
 Prefill (> 8 bf16 tokens): the decoded weight is rounded once to bf16 for the matrix cores,
 so the bound adds 2^-8 sum |x| |W_hat| and K 2^-24 of fp32 accumulation."""
 import numpy as np
@@ -34,7 +35,11 @@ def artefact(N, K, seed):
     return o.pack(W, s)
 
 
-def run(awq, art, X, prefill):
+def run(awq, art, X, prefill, biased=None):
+    """biased: the decode variant for bf16 activations sums x (128 + q) and removes the bias
+    per 32 channels, so its fp32 roundings scale with sum |x| Delta (q + z + 257)."""
+    if biased is None:
+        biased = X.dtype == torch.bfloat16 and not prefill
     q = torch.from_numpy(art["qweight"]).to(DEV)
     sc = torch.from_numpy(art["scales"].view(np.float16)).to(DEV)
     zz = torch.from_numpy(art["zeros"].view(np.float16)).to(DEV)
@@ -46,7 +51,7 @@ def run(awq, art, X, prefill):
     codes = o.unpack_words(art["qweight"]).astype(np.float64)
     d = art["scales"].astype(np.float64).repeat(128, axis=1)
     z = art["zeros"].astype(np.float64).repeat(128, axis=1)
-    mag = np.abs(X64) @ (d * (codes + z + 1.0)).T  # sum |x| Delta (q + z + 1)
+    mag = np.abs(X64) @ (d * (codes + z + (257.0 if biased else 1.0))).T  # sum |x| Delta (q + z + 1 [+ 256])
     tol = 64 * 2.0 ** -24 * mag
     if prefill:
         tol = tol + (2.0 ** -8 + K * 2.0 ** -24) * (np.abs(X64) @ np.abs(Wh).T)
