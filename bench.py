@@ -134,6 +134,36 @@ def clip_search(torch, awq, Xd, Wd, s_best, stride: int = 8, reps: int = 10):
             "note": "whole awq_clip call (range pre-pass, clipped qdq + bf16 MFMA product, select)"}
 
 
+def fold_ops(torch, awq, dev, reps: int = 10):
+    """Applying the scales, at the decoder block's largest shapes: awq_scale_cols in place on the
+    fused gate+up weight bf16 [28672 x 4096] and awq_scaled_act (GELU) from the MLP activation
+    bf16 [16384 x 14336] into a second buffer; 2 bytes read + 2 written per element (plus s).
+    The last-level cache is flushed between calls.  Seeded random values."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    N, K = 28672, 4096
+    W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
+    s = torch.exp(0.25 * torch.randn(K, generator=g, device=dev, dtype=torch.float32))
+    ms = _time_reps(torch, lambda: awq.scale_cols(W, s, flags=fl, check=False), reps, flush)
+    nbytes = 4.0 * N * K + 4.0 * K
+    res["scale_cols"] = {"shape": [N, K], "bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                         "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del W
+    M, K = 16384, 14336
+    X = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    Y = torch.empty_like(X)
+    s = torch.exp(0.25 * torch.randn(K, generator=g, device=dev, dtype=torch.float32))
+    ms = _time_reps(torch, lambda: awq.scaled_act(X, s, "gelu", out=Y, flags=fl, check=False), reps, flush)
+    nbytes = 4.0 * M * K + 4.0 * K
+    res["scaled_act_gelu"] = {"shape": [M, K], "bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                              "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    awq.raise_for_flags(fl)
+    return res
+
+
 def w4a16_products(torch, awq, dev, reps: int = 10):
     """The W4A16 product over a packed artefact of the decoder block's fused gate+up weight
     (N = 28672, K = 4096): decode with one token (HBM-bound: 0.53125 bytes per weight, the
@@ -207,6 +237,7 @@ def main():
     ap.add_argument("--no-hbm", action="store_true", help="skip the large-input stats / pack timing")
     ap.add_argument("--no-clip", action="store_true", help="skip the clipping-search timing")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 product timing")
+    ap.add_argument("--no-fold", action="store_true", help="skip the scale-application timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -325,6 +356,8 @@ def main():
         out["hbm"] = hbm_kernels(torch, awq, dev)
     if not args.no_w4a16:
         out["w4a16"] = w4a16_products(torch, awq, dev)
+    if not args.no_fold:
+        out["fold"] = fold_ops(torch, awq, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -242,6 +242,18 @@ def pack(W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, *, max_val: 
     return qweight, scales, zeros
 
 
+# Linear modules that the clipping search leaves alone, by name ("AWQ：为什么 4-bit 权重量化要先观察
+# Activation", §5): the query and key projections (and a fused QKV weight) keep the full range
+# of their scaled groups.
+CLIP_SKIP_NAME_PARTS = ("q_", "k_", "query", "key", "Wqkv")
+
+
+def clip_skipped(module_name: str) -> bool:
+    """True when a Linear module of this name takes no clipping search (its name contains one of
+    CLIP_SKIP_NAME_PARTS, case-sensitive substrings); pack such a layer with ``max_val=None``."""
+    return any(part in module_name for part in CLIP_SKIP_NAME_PARTS)
+
+
 def clip_workspace_bytes(M: int, K: int, N: int, group: int = GROUP, n_clip: int = N_CLIP) -> int:
     return int(lib().awq_clip_workspace_bytes(M, K, N, group, n_clip))
 

@@ -197,3 +197,18 @@ def test_w4a16_argument_errors(L, kw, status):
     a.update(kw)
     assert L.awq_w4a16(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["q"], a["sc"], a["z"], a["N"], a["group"],
                        a["Y"], a["ldy"], None) == status
+
+
+@pytest.mark.parametrize("name,skipped", [
+    ("model.layers.0.self_attn.q_proj", True), ("model.layers.0.self_attn.k_proj", True),
+    ("transformer.h.3.attn.Wqkv", True), ("encoder.layer.1.attention.self.query", True),
+    ("encoder.layer.1.attention.self.key", True),
+    ("model.layers.0.self_attn.v_proj", False), ("model.layers.0.self_attn.o_proj", False),
+    ("model.layers.0.mlp.gate_proj", False), ("model.layers.0.mlp.down_proj", False),
+    ("encoder.layer.1.attention.self.value", False),
+])
+def test_clip_skips_query_and_key_modules(name, skipped):
+    """The clipping search skips Linear modules whose name contains q_, k_, query, key or Wqkv
+    ("AWQ：为什么 4-bit 权重量化要先观察 Activation", §5); every other projection is clipped."""
+    from post_weight_quantization_mean_amd import awq
+    assert awq.clip_skipped(name) is skipped
