@@ -339,25 +339,30 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
   const int64_t wn = n0 + wr;
   const bool wlive = wn < N;
   const int32_t* wrow = qweight + (wlive ? wn : 0) * words;
-  uint4 xv[8];
-  uint2 qv;
-  float dv, zv;
-  auto load = [&](int64_t c) {
+  // one chunk's global data in registers; two sets alternate, so that the loads of chunk c + 2
+  // are in flight during the whole of step c (one step is shorter than a load's latency)
+  struct Regs {
+    uint4 xv[8];
+    uint2 qv;
+    uint16_t dh, zh;  // fp16 bits, converted at the store so no load result is needed early
+  };
+  auto load = [&](Regs& R, int64_t c) {
     const uint32_t kb = (uint32_t)(c * PKC);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            xrsrc, (int)((xr0 + 64 * i) * ldx * 2 + kb * 2 + xkp * 16), 0, 0));
-    qv = *reinterpret_cast<const uint2*>(wrow + kb / 8 + 2 * wq);
+      R.xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xrsrc, (int)((xr0 + 64 * i) * ldx * 2 + kb * 2 + xkp * 16), 0, 0));
+    R.qv = *reinterpret_cast<const uint2*>(wrow + kb / 8 + 2 * wq);
     const int64_t g = kb / kGroup;
-    dv = wlive ? h2f(scales[(wlive ? wn : 0) * G + g]) : 0.0f;  // rows past N: weight 0
-    zv = h2f(zeros[(wlive ? wn : 0) * G + g]);
+    R.dh = scales[(wlive ? wn : 0) * G + g];  // unconditional: a branch here would drain the loads
+    R.zh = zeros[(wlive ? wn : 0) * G + g];
   };
-  auto store = [&](int b) {
+  auto store = [&](const Regs& R, int b) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&xs[b][xr0 + 64 * i][xkp * 8]) = xv[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&xs[b][xr0 + 64 * i][xkp * 8]) = R.xv[i];
     uint32_t pk[8];
-    const uint32_t wv[2] = {qv.x, qv.y};
+    const uint32_t wv[2] = {R.qv.x, R.qv.y};
+    const float dv = wlive ? h2f(R.dh) : 0.0f, zv = h2f(R.zh);  // rows past N: weight 0
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -377,13 +382,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
   const int frow = lane & 31, fk = (lane >> 5) * 8;
-  const int64_t nch = K / PKC;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int64_t c = 0; c < nch; ++c) {
-    const int b = (int)(c & 1);
-    load(c + 1 < nch ? c + 1 : c);
+  const int64_t nch = K / PKC;  // >= 4 (K is a multiple of 128)
+  auto compute = [&](int b) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 af[4], bfr[4];
@@ -397,8 +397,25 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
         for (int cc = 0; cc < 4; ++cc)
           acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[r], bfr[cc], acc[r][cc], 0, 0, 0);
     }
-    store(b ^ 1);
+  };
+  // step c: LDS buffer c & 1 holds chunk c; `nx` holds chunk c + 1 (landed or in flight) and
+  // `fa` chunk c + 2 (in flight).  After the products, chunk c + 1 goes to the other buffer
+  // (whose readers finished before the previous barrier), and `nx` is reloaded with c + 3.
+  auto step = [&](int64_t c, Regs& nx) {
+    compute((int)(c & 1));
+    if (c + 1 < nch) store(nx, (int)((c + 1) & 1));
     __syncthreads();
+    load(nx, c + 3 < nch ? c + 3 : nch - 1);  // past the end: a harmless in-bounds reload
+  };
+  Regs ra, rb;
+  load(ra, 0);
+  load(rb, 1);
+  store(ra, 0);
+  __syncthreads();
+  load(ra, 2);
+  for (int64_t c = 0; c < nch; c += 2) {  // nch is even
+    step(c, rb);
+    step(c + 1, ra);
   }
   // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
