@@ -26,6 +26,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 // byte c of x as a float (one v_cvt_f32_ubyte<c>)
@@ -37,6 +38,10 @@ __device__ __forceinline__ float ubyte(uint32_t x) { return (float)((x >> (8 * C
 #define AWQ_GV_ROWS 4
 #endif
 constexpr int kGvRows = AWQ_GV_ROWS;  // weight rows per wave step
+#ifndef AWQ_GV_WORD_OUTER
+#define AWQ_GV_WORD_OUTER 2
+#endif
+constexpr int kGvWordOuter = AWQ_GV_WORD_OUTER;  // bf16 decode: up to this many tokens, word-outer order
 constexpr int kGvThreads = 256;
 
 // K is covered in passes of kc channels (4096 for up to two tokens, else 2048): X of the pass
@@ -97,7 +102,8 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
     // ahead of their use so that the next loads are in flight during the current math
     struct Slab {
       u32x4 q[kGvRows];
-      float d[kGvRows], z[kGvRows];
+      uint16_t d[kGvRows], z[kGvRows];  // fp16 bits: converted where used, so that nothing
+                                        // waits for the prefetch before the current math
     };
     auto fetch = [&](int64_t n0, int64_t t, Slab& S) {
       const int64_t lw = 4 * (64 * t + lane);
@@ -107,8 +113,8 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
       for (int r = 0; r < kGvRows; ++r) {
         const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: load row N-1, store nothing
         S.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qweight + n * words + w0));
-        S.d[r] = h2f(scales[n * G + g]);
-        S.z[r] = h2f(zeros[n * G + g]);
+        S.d[r] = scales[n * G + g];
+        S.z[r] = zeros[n * G + g];
       }
     };
     const int64_t step = nwaves * kGvRows;
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
         // next (row group, segment) in this wave's order
         const bool last_seg = t + 1 == segs;
         const int64_t nn = last_seg ? n0 + step : n0, tn = last_seg ? 0 : t + 1;
-        if (nn < N) fetch(nn, tn, nxt);
+        fetch(nn < N ? nn : n0, tn, nxt);  // past the last row group: a harmless reload
         const int64_t lw = 4 * (64 * t + lane);  // first word of this lane within the pass
         if (lw < pw) {
           const int64_t k0 = 8 * lw;
@@ -158,7 +164,8 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
             }
             // Delta (sum x q - z sum x) for this quarter group
 #pragma unroll
-            for (int r = 0; r < kGvRows; ++r) acc[r][m] = fmaf(cur.d[r], fmaf(-cur.z[r], sx, sq[r]), acc[r][m]);
+            for (int r = 0; r < kGvRows; ++r)
+              acc[r][m] = fmaf(h2f(cur.d[r]), fmaf(-h2f(cur.z[r]), sx, sq[r]), acc[r][m]);
           }
         }
         cur = nxt;
@@ -191,122 +198,205 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
     float* __restrict__ Y, int64_t ldy, int64_t kc) {
-  extern __shared__ uint32_t xp[];  // [M][kc / 2] bf16 pairs, (x_i, x_{i+4}) per 8 channels
+  // LDS: [M][kc / 2] bf16 pairs, (x_i, x_{i+4}) per 8 channels, then [M][kc / 8] fp32 sums of
+  // each 8 channels (the bias correction needs sum x per 32 channels, the same for every row)
+  extern __shared__ __attribute__((aligned(16))) uint32_t xp[];
+  float* xsum = reinterpret_cast<float*>(xp + (int64_t)M * (kc / 2));
+  // 16-byte views for the reads (one ds_read_b128 each)
+  const u32x4* xq = reinterpret_cast<const u32x4*>(xp);
+  const f32x4* xs4 = reinterpret_cast<const f32x4*>(xsum);
   typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
   const int64_t G = K / kGroup;
   const int64_t words = K / 8;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * kGvThreads + threadIdx.x) >> 6;
+  // wave-uniform row bookkeeping lives in scalar registers, so row addresses cost no VALU
+  const int64_t wave = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * kGvThreads + threadIdx.x) >> 6));
   const int64_t nwaves = ((int64_t)gridDim.x * kGvThreads) >> 6;
   const int64_t step = nwaves * kGvRows;
   auto dot = [](uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfx2, a), __builtin_bit_cast(bfx2, b), c, false);
   };
+  // the bias 0x43004300 as an opaque vector register: (x & mask) | bias is then one v_and_or_b32
+  // (a VOP3 instruction takes no literal operand here, and at most one scalar one)
+  uint32_t bias;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias));
+  struct Slab {
+    u32x4 q[kGvRows];
+    uint16_t d[kGvRows], z[kGvRows];  // fp16 bits: converted where used, so that nothing
+                                      // waits for the prefetch before the current math
+  };
+  // this wave's row groups n0 = R wave + i step (i < nrg), each in segs segments per pass: the
+  // items (row group, segment) in that order, three slabs in a ring, two items in flight
+  const int64_t first = wave * kGvRows;
+  const int64_t nrg = first < N ? (N - 1 - first) / step + 1 : 0;
   for (int64_t c0 = 0; c0 < K; c0 += kc) {
     const int64_t kw = K - c0 < kc ? K - c0 : kc;  // a multiple of 128
-    __syncthreads();
+    const int64_t pw = kw / 8;                      // words of a row in this pass
+    const int64_t segs = (pw + 255) / 256;
+    const int64_t T = nrg * segs;
+    // cursor of the next item to fetch; rows past N load row N - 1 (in bounds, never stored)
+    int64_t fn0 = first, ft = 0;
+    auto fetch = [&](Slab& S) {
+      const int lw = 4 * (64 * (int)ft + lane);
+      const int w0 = lw < pw ? lw : 0;                      // word within the pass
+      const int g = (int)((c0 + 8 * (int64_t)w0) / kGroup);  // group of those words
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r) {
+        const int64_t n = fn0 + r < N ? fn0 + r : N - 1;
+        const int32_t* rowp = qweight + n * words + c0 / 8;
+        S.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + w0));
+        S.d[r] = (scales + n * G)[g];
+        S.z[r] = (zeros + n * G)[g];
+      }
+      if (++ft == segs) { ft = 0; fn0 += step; }
+    };
+    Slab sa, sb, sc;
+    if (T > 0) {  // the first two items are in flight while X is staged
+      fetch(sa);
+      fetch(sb);
+    }
+    __syncthreads();  // the previous pass is done with xp
     {  // 8 channels (16 bytes) per piece, four pieces in flight per thread
-      const int64_t pieces = (int64_t)M * kw / 8;
-      for (int64_t i0 = threadIdx.x; i0 < pieces; i0 += 4 * kGvThreads) {
+      const int pieces = (int)(M * kw / 8);
+      const int ppr = (int)(kw / 8);  // pieces per token row
+      for (int i0 = threadIdx.x; i0 < pieces; i0 += 4 * kGvThreads) {
         uint4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int64_t i = i0 + u * kGvThreads;
+          const int i = i0 + u * kGvThreads;
           if (i < pieces) {
-            const int64_t m = (i * 8) / kw, k = i * 8 - m * kw;
+            const int m = i / ppr, k = 8 * (i - m * ppr);
             v[u] = *reinterpret_cast<const uint4*>(X + m * ldx + c0 + k);
           }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int64_t i = i0 + u * kGvThreads;
+          const int i = i0 + u * kGvThreads;
           if (i < pieces) {
-            const int64_t m = (i * 8) / kw, k = i * 8 - m * kw;
+            const int m = i / ppr, k = 8 * (i - m * ppr);
             // (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
             const uint32_t a = v[u].x, b = v[u].y, c = v[u].z, d = v[u].w;
-            *reinterpret_cast<uint4*>(xp + m * (kc / 2) + k / 2) =
-                make_uint4((a & 0xffffu) | (c << 16), (a >> 16) | (c & 0xffff0000u),
-                           (b & 0xffffu) | (d << 16), (b >> 16) | (d & 0xffff0000u));
+            const uint4 pr = make_uint4((a & 0xffffu) | (c << 16), (a >> 16) | (c & 0xffff0000u),
+                                        (b & 0xffffu) | (d << 16), (b >> 16) | (d & 0xffff0000u));
+            *reinterpret_cast<uint4*>(xp + (int64_t)m * (kc / 2) + k / 2) = pr;
+            float s8 = 0.0f;
+            s8 = dot(pr.x, 0x3f803f80u, s8);  // (1, 1) in bf16: exact products
+            s8 = dot(pr.y, 0x3f803f80u, s8);
+            s8 = dot(pr.z, 0x3f803f80u, s8);
+            s8 = dot(pr.w, 0x3f803f80u, s8);
+            xsum[(int64_t)m * (kc / 8) + k / 8] = s8;
           }
         }
       }
     }
     __syncthreads();
-    const int64_t pw = kw / 8;
-    const int64_t segs = (pw + 255) / 256;  // <= kDotSegs
-    struct Slab {
-      u32x4 q[kGvRows];
-      float d[kGvRows], z[kGvRows];
-    };
-    auto fetch = [&](int64_t n0, int64_t t, Slab& S) {
-      const int64_t lw = 4 * (64 * t + lane);
-      const int64_t w0 = c0 / 8 + (lw < pw ? lw : 0);
-      const int64_t g = (8 * w0) / kGroup;
+    float acc[kGvRows][M];
+    int64_t pn0 = first, pt = 0;  // cursor of the next item to process
+    auto process = [&](const Slab& S) {
+      if (pt == 0) {
 #pragma unroll
-      for (int r = 0; r < kGvRows; ++r) {
-        const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: load row N-1, store nothing
-        S.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qweight + n * words + w0));
-        S.d[r] = h2f(scales[n * G + g]);
-        S.z[r] = h2f(zeros[n * G + g]);
+        for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+          for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
       }
-    };
-    Slab cur, nxt;
-    int64_t n0 = wave * kGvRows;
-    if (n0 < N) fetch(n0, 0, cur);
-    while (n0 < N) {
-      float acc[kGvRows][M];
+      const int lw = 4 * (64 * (int)pt + lane);
+      if (lw < pw) {
+        // codes as biased bf16 pairs (q_i, q_{i+4}) + 128, i = 0..3, of word j of row r
+        auto pairs = [&](int r, int j, uint32_t* qp) {
+          const uint32_t w = j == 0 ? S.q[r].x : j == 1 ? S.q[r].y : j == 2 ? S.q[r].z : S.q[r].w;
+          qp[0] = (w & 0x000f000fu) | bias;
+          qp[1] = ((w >> 4) & 0x000f000fu) | bias;
+          qp[2] = ((w >> 8) & 0x000f000fu) | bias;
+          qp[3] = ((w >> 12) & 0x000f000fu) | bias;
+        };
+        auto finish = [&](int m, const float* sq) {
+          const f32x4 s4 = xs4[(m * (kc / 8) + lw) / 4];
+          const float sxm = (s4.x + s4.y) + (s4.z + s4.w);  // sum of the lane's 32 activations
 #pragma unroll
-      for (int r = 0; r < kGvRows; ++r)
+          for (int r = 0; r < kGvRows; ++r)
+            acc[r][m] = fmaf(h2f(S.d[r]), fmaf(-(128.0f + h2f(S.z[r])), sxm, sq[r]), acc[r][m]);
+        };
+        if constexpr (M <= kGvWordOuter) {
+          // few tokens: word by word, so that only one word's pairs are live
+          float sq[M][kGvRows];
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-      for (int64_t t = 0; t < segs; ++t) {
-        {
-          const bool last_seg = t + 1 == segs;
-          const int64_t nn = last_seg ? n0 + step : n0, tn = last_seg ? 0 : t + 1;
-          if (nn < N) fetch(nn, tn, nxt);
-          const int64_t lw = 4 * (64 * t + lane);
-          if (lw < pw) {
+          for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < kGvRows; ++r) sq[m][r] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t qp[kGvRows][4];
+#pragma unroll
+            for (int r = 0; r < kGvRows; ++r) pairs(r, j, qp[r]);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-              const uint32_t* xr = xp + (int64_t)m * (kc / 2) + 4 * lw;
-              float sq[kGvRows], sxm = 0.0f;  // sxm: sum of the lane's 32 activations
+              const u32x4 x4 = xq[m * (kc / 8) + lw + j];
 #pragma unroll
-              for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint4 x4 = *reinterpret_cast<const uint4*>(xr + 4 * j);
-                sxm = dot(x4.x, 0x3f803f80u, sxm);  // (1, 1) in bf16
-                sxm = dot(x4.y, 0x3f803f80u, sxm);
-                sxm = dot(x4.z, 0x3f803f80u, sxm);
-                sxm = dot(x4.w, 0x3f803f80u, sxm);
-#pragma unroll
-                for (int r = 0; r < kGvRows; ++r) {
-                  const uint32_t w = j == 0 ? cur.q[r].x : j == 1 ? cur.q[r].y : j == 2 ? cur.q[r].z : cur.q[r].w;
-                  sq[r] = dot(x4.x, (w & 0x000f000fu) | 0x43004300u, sq[r]);
-                  sq[r] = dot(x4.y, ((w >> 4) & 0x000f000fu) | 0x43004300u, sq[r]);
-                  sq[r] = dot(x4.z, ((w >> 8) & 0x000f000fu) | 0x43004300u, sq[r]);
-                  sq[r] = dot(x4.w, ((w >> 12) & 0x000f000fu) | 0x43004300u, sq[r]);
-                }
+              for (int r = 0; r < kGvRows; ++r) {
+                sq[m][r] = dot(x4.x, qp[r][0], sq[m][r]);
+                sq[m][r] = dot(x4.y, qp[r][1], sq[m][r]);
+                sq[m][r] = dot(x4.z, qp[r][2], sq[m][r]);
+                sq[m][r] = dot(x4.w, qp[r][3], sq[m][r]);
               }
-#pragma unroll
-              for (int r = 0; r < kGvRows; ++r)
-                acc[r][m] = fmaf(cur.d[r], fmaf(-(128.0f + cur.z[r]), sxm, sq[r]), acc[r][m]);
             }
           }
-          cur = nxt;
-        }
-      }
 #pragma unroll
-      for (int r = 0; r < kGvRows; ++r)
+          for (int m = 0; m < M; ++m) finish(m, sq[m]);
+        } else {
+          // more tokens: all pairs once, then token by token
+          uint32_t qp[kGvRows][4][4];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float v = wave_sum(acc[r][m]);
-          if (lane == 0 && n0 + r < N) {
-            float* y = Y + (int64_t)m * ldy + n0 + r;
-            *y = c0 == 0 ? v : *y + v;
+          for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pairs(r, j, qp[r][j]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float sq[kGvRows];
+#pragma unroll
+            for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 x4 = xq[m * (kc / 8) + lw + j];
+#pragma unroll
+              for (int r = 0; r < kGvRows; ++r) {
+                sq[r] = dot(x4.x, qp[r][j][0], sq[r]);
+                sq[r] = dot(x4.y, qp[r][j][1], sq[r]);
+                sq[r] = dot(x4.z, qp[r][j][2], sq[r]);
+                sq[r] = dot(x4.w, qp[r][j][3], sq[r]);
+              }
+            }
+            finish(m, sq);
           }
         }
-      n0 += step;
+      }
+      if (pt + 1 == segs) {  // row group done: sum over the wave's lanes, one row and token at a time
+#pragma unroll
+        for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[r][m]);
+            if (lane == 0 && pn0 + r < N) {
+              float* y = Y + (int64_t)m * ldy + pn0 + r;
+              *y = c0 == 0 ? v : *y + v;
+            }
+          }
+        pt = 0;
+        pn0 += step;
+      } else {
+        ++pt;
+      }
+    };
+    for (int64_t it = 0; it < T; it += 3) {  // static slab roles: item it in sa, it+1 in sb, it+2 in sc
+      fetch(sc);
+      process(sa);
+      if (it + 1 < T) {
+        fetch(sa);
+        process(sb);
+      }
+      if (it + 2 < T) {
+        fetch(sb);
+        process(sc);
+      }
     }
   }
 }
@@ -432,6 +522,24 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
 
 }  // namespace
 
+// decode grid: one wave per row group, at most what is resident at once (every wave then
+// starts at the launch and loads its first rows while X is staged)
+template <typename Kern>
+int64_t gemv_blocks(Kern kern, size_t lds, int64_t waves) {
+  int dev = 0, cus = 256, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGvThreads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+#ifdef AWQ_GV_BPC
+  per_cu = AWQ_GV_BPC;
+#endif
+  const int64_t need = (waves + kGvThreads / 64 - 1) / (kGvThreads / 64);
+  const int64_t resident = (int64_t)cus * per_cu;
+  return need < resident ? need : resident;
+}
+
 // channels per decode pass: X of one pass takes at most 64 KiB of LDS (fp32)
 int64_t w4a16_gemv_kc(int64_t M) { return M <= 2 ? 4096 : 2048; }
 
@@ -446,27 +554,26 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
   }
   // decode path, up to 8 tokens per launch (fp32 X always takes it)
   const int64_t waves = (N + kGvRows - 1) / kGvRows;
-  int64_t blocks = (waves + 3) / 4;
-  if (blocks > 1024) blocks = 1024;
   for (int64_t m0 = 0; m0 < M; m0 += kW4a16GemvMax) {
     const int64_t mb = M - m0 < kW4a16GemvMax ? M - m0 : kW4a16GemvMax;
     const char* xp = static_cast<const char*>(X) + m0 * ldx * (xf32 ? 4 : 2);
     float* yp = Y + m0 * ldy;
     const int64_t kc = w4a16_gemv_kc(mb);
-    const int64_t kcd = mb <= 2 ? 8192 : 4096;  // bf16 pairs: at most 64 KiB, 4 segments
+    const int64_t kcd = mb <= 2 ? 8192 : 4096;  // pairs + sums: at most 80 KiB, 4 segments
     const size_t lds = (size_t)mb * (size_t)kc * 4;
 #define AWQ_GV(MV)                                                                                       \
   do {                                                                                                   \
-    if (!xf32)                                                                                           \
-      w4a16_gemv_dot_kernel<MV><<<(unsigned)blocks, kGvThreads, (size_t)mb * kcd * 2, st>>>(            \
+    if (!xf32) {                                                                                         \
+      const size_t ldsd = (size_t)mb * kcd * 5 / 2;                                                      \
+      const int64_t blocks = gemv_blocks(w4a16_gemv_dot_kernel<MV>, ldsd, waves);                        \
+      w4a16_gemv_dot_kernel<MV><<<(unsigned)blocks, kGvThreads, ldsd, st>>>(                             \
           static_cast<const uint16_t*>(static_cast<const void*>(xp)), ldx, K, qweight, scales, zeros, N, \
           yp, ldy, kcd);                                                                                 \
-    else if (xf32)                                                                                       \
+    } else {                                                                                             \
+      const int64_t blocks = gemv_blocks(w4a16_gemv_kernel<MV, true>, lds, waves);                       \
       w4a16_gemv_kernel<MV, true><<<(unsigned)blocks, kGvThreads, lds, st>>>(xp, ldx, K, qweight, scales, \
                                                                             zeros, N, yp, ldy, kc);      \
-    else                                                                                                 \
-      w4a16_gemv_kernel<MV, false><<<(unsigned)blocks, kGvThreads, lds, st>>>(xp, ldx, K, qweight, scales, \
-                                                                             zeros, N, yp, ldy, kc);     \
+    }                                                                                                    \
   } while (0)
     switch (mb) {
       case 1: AWQ_GV(1); break;
