@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 4
+#define AWQ_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -139,6 +139,27 @@ AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, i
                              int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
                              size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
                              awq_event_t fused_begin, awq_event_t fused_end);
+
+/* The same search for projections that read one X and must share one scale vector
+ * ([EXPLAINER §6]: Q, K and V all consume the normalized input, so s applies to all of them
+ * together), given as a list of weights instead of one concatenated W: the layer's output
+ * channels are the rows of Ws[0], then Ws[1], ..., and
+ *   loss_i = sum over all weights and m, n of (X E^T)[m,n]^2 / (M * sum_w N_w).
+ * Each weight's rows are padded to a multiple of 128 inside the search, so with every N_w a
+ * multiple of 128 the losses are bit-identical to awq_search on the concatenated W.
+ *   Ws, Ns, ldws   host arrays of n_weights (1..8) entries: device pointer, rows and row
+ *                  stride of each weight [N_w, K] (all of dtype w_dtype); read during the
+ *                  call only
+ *   ws             workspace of at least awq_search_multi_workspace_bytes(...) bytes
+ * Other arguments, results and errors as awq_search. */
+AWQ_API size_t awq_search_multi_workspace_bytes(int64_t M, int64_t K, const int64_t* Ns,
+                                                int32_t n_weights, int32_t group, int32_t n_grid);
+AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const void* const* Ws, int w_dtype, const int64_t* Ns,
+                             const int64_t* ldws, int32_t n_weights, const float* a,
+                             int32_t group, int32_t n_grid, double* losses_out,
+                             int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
+                             size_t ws_bytes, uint32_t* flags, awq_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Step 5: real quantization and packing of S W ([EXPLAINER §7, §8]; [MODULES §5.3]:

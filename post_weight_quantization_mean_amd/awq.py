@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
                                  i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
         L.awq_search_timed.restype = ctypes.c_int
         L.awq_search_timed.argtypes = L.awq_search.argtypes + [vp, vp]
+        L.awq_search_multi_workspace_bytes.restype = sz
+        L.awq_search_multi_workspace_bytes.argtypes = [i64, i64, vp, i32, i32, i32]
+        L.awq_search_multi.restype = ctypes.c_int
+        L.awq_search_multi.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, vp, vp, i32, vp,
+                                       i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
         L.awq_pack.restype = ctypes.c_int
         L.awq_pack.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, vp, vp, vp]
         L.awq_pack_clipped.restype = ctypes.c_int
@@ -87,7 +92,7 @@ def lib() -> ctypes.CDLL:
         L.awq_scaled_act.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp]
         L.awq_w4a16.restype = ctypes.c_int
         L.awq_w4a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i32, vp, i64, vp]
-        if L.awq_abi_version() != 4:
+        if L.awq_abi_version() != 5:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -132,7 +137,11 @@ def stats_workspace_bytes(M: int, K: int) -> int:
     return int(lib().awq_stats_workspace_bytes(M, K))
 
 
-def search_workspace_bytes(M: int, K: int, N: int, group: int = GROUP, n_grid: int = N_GRID) -> int:
+def search_workspace_bytes(M: int, K: int, N, group: int = GROUP, n_grid: int = N_GRID) -> int:
+    """N: the weight's rows, or a sequence of several weights' rows (awq_search_multi)."""
+    if isinstance(N, (list, tuple)):
+        ns = (ctypes.c_int64 * len(N))(*N)
+        return int(lib().awq_search_multi_workspace_bytes(M, K, ns, len(N), group, n_grid))
     return int(lib().awq_search_workspace_bytes(M, K, N, group, n_grid))
 
 
@@ -166,20 +175,35 @@ class SearchResult:
         return int(self.best.item())
 
 
-def search(X: torch.Tensor, W: torch.Tensor, a: torch.Tensor, group_size: int = GROUP, n_grid: int = N_GRID,
+def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid: int = N_GRID,
            *, return_table: bool = False, workspace: Optional[torch.Tensor] = None,
            flags: Optional[torch.Tensor] = None, check: bool = True,
            fused_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> SearchResult:
-    """The candidate scale search over alpha = i / n_grid for one layer (or several
-    projections sharing one input, concatenated along N).
+    """The candidate scale search over alpha = i / n_grid for one layer.  ``W`` is one weight
+    [N, K], or a list of weights [N_w, K] of projections that read X and share the scales
+    (query/key/value, gate/up): searched as one layer without concatenating them
+    (awq_search_multi), all of one dtype.
 
     ``fused_events``: two timing events that the library records right before and after the
     fused candidate kernel (awq_search_timed), so that ``e0.elapsed_time(e1)`` is that
-    kernel's time alone."""
+    kernel's time alone; single weight only."""
     M, K, ldx = _matrix(X, "X")
-    N, Kw, ldw = _matrix(W, "W")
-    if Kw != K:
-        raise ValueError("X and W disagree on K")
+    Ws = list(W) if isinstance(W, (list, tuple)) else None
+    if Ws is not None:
+        if not Ws:
+            raise ValueError("W is an empty list")
+        if any(w.dtype != Ws[0].dtype for w in Ws):
+            raise ValueError("the weights of one search share a dtype")
+        shapes = [_matrix(w, f"W[{i}]") for i, w in enumerate(Ws)]
+        if any(kw != K for _, kw, _ in shapes):
+            raise ValueError("X and W disagree on K")
+        if fused_events is not None:
+            raise ValueError("fused_events times a single-weight search")
+        N = [n for n, _, _ in shapes]
+    else:
+        N, Kw, ldw = _matrix(W, "W")
+        if Kw != K:
+            raise ValueError("X and W disagree on K")
     if a.shape != (K,) or a.dtype != torch.float32 or not a.is_cuda or not a.is_contiguous():
         raise ValueError("a must be a contiguous fp32 device vector of length K")
     dev = X.device
@@ -190,10 +214,20 @@ def search(X: torch.Tensor, W: torch.Tensor, a: torch.Tensor, group_size: int = 
     need = search_workspace_bytes(M, K, N, group_size, n_grid)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    args = (X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
-            a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(),
-            s_best.data_ptr(), s_table.data_ptr() if s_table is not None else None,
-            ws.data_ptr(), ws.numel(), fl.data_ptr(), _stream(dev))
+    outs = (a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(),
+            s_table.data_ptr() if s_table is not None else None, ws.data_ptr(), ws.numel(), fl.data_ptr(),
+            _stream(dev))
+    if Ws is not None:
+        ptrs = (ctypes.c_void_p * len(Ws))(*[w.data_ptr() for w in Ws])
+        ns = (ctypes.c_int64 * len(Ws))(*N)
+        lds = (ctypes.c_int64 * len(Ws))(*[ld for _, _, ld in shapes])
+        st = lib().awq_search_multi(X.data_ptr(), _dtype_code(X), M, K, ldx, ptrs, _dtype_code(Ws[0]), ns, lds,
+                                    len(Ws), *outs)
+        _check(st, "awq_search_multi")
+        if check:
+            raise_for_flags(fl)
+        return SearchResult(losses, best, s_best, s_table, fl)
+    args = (X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw) + outs
     if fused_events is None:
         st = lib().awq_search(*args)
     else:

@@ -157,30 +157,49 @@ AWQ_API size_t awq_search_workspace_bytes(int64_t M, int64_t K, int64_t N, int32
   return L.total;
 }
 
-AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                             const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
-                             int32_t group, int32_t n_grid, double* losses_out,
-                             int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
-                             size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
-                             awq_event_t fused_begin, awq_event_t fused_end) {
+}  // extern "C"
+
+namespace {
+
+// The search over one layer whose weight is given as n_weights row blocks that share X
+// (a single weight is the case n_weights = 1).  Ws, Ns, ldws: host arrays.
+int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const void* const* Ws,
+                int w_dtype, const int64_t* Ns, const int64_t* ldws, int32_t n_weights, const float* a,
+                int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out, float* s_best_out,
+                float* s_table_out, void* ws, size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
+                awq_event_t fused_begin, awq_event_t fused_end) {
   int st = check_matrix(X, x_dtype, M, K, ldx);
   if (st != AWQ_OK) return st;
-  st = check_matrix(W, w_dtype, N, K, ldw);
-  if (st != AWQ_OK) return st;
+  if (Ws == nullptr || Ns == nullptr || ldws == nullptr || n_weights < 1 || n_weights > awq::kMaxWSegs)
+    return AWQ_ERR_INVALID_ARG;
+  awq::WSegs segs{};
+  segs.count = n_weights;
+  int64_t n_total = 0, tiles = 0;
+  for (int i = 0; i < n_weights; ++i) {
+    st = check_matrix(Ws[i], w_dtype, Ns[i], K, ldws[i]);
+    if (st != AWQ_OK) return st;
+    // block-relative buffer offsets are 32-bit: 128 rows of each weight span less than 2^31 bytes
+    if (mul_ok(mul_ok(awq::kSearchBN, ldws[i]), dsize(w_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+    segs.w[i] = Ws[i];
+    segs.ldw[i] = ldws[i];
+    segs.n[i] = Ns[i];
+    segs.tile0[i] = tiles;
+    tiles += awq::padded_n(Ns[i]) / 128;
+    n_total += Ns[i];
+  }
+  segs.tile0[n_weights] = tiles;
+  const int64_t NP = tiles * 128;  // the padded row space
   if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
   if (n_grid < 1 || n_grid > 64) return AWQ_ERR_INVALID_ARG;
   if (a == nullptr || losses_out == nullptr || best_out == nullptr || s_best_out == nullptr ||
       flags == nullptr)
     return AWQ_ERR_INVALID_ARG;
-  // Block-relative buffer offsets are 32-bit: 512 rows of X and 128 rows of W must span
-  // less than 2^31 bytes.
-  if (mul_ok(mul_ok(awq::kSearchBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX ||
-      mul_ok(mul_ok(awq::kSearchBN, ldw), dsize(w_dtype)) >= (int64_t)INT32_MAX)
-    return AWQ_ERR_SHAPE;
-  // one candidate's group ranges (float2 [K/128][Npad]) are addressed with 32-bit offsets
-  if (mul_ok(mul_ok(K / kGroup, awq::padded_n(N)), 8) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  // 512 rows of X in 32-bit block-relative offsets
+  if (mul_ok(mul_ok(awq::kSearchBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  // one candidate's group ranges (float2 [K/128][NP]) are addressed with 32-bit offsets
+  if (mul_ok(mul_ok(K / kGroup, NP), 8) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
   SearchLayout L;
-  if (!search_layout(M, K, N, n_grid, &L)) return AWQ_ERR_SHAPE;
+  if (!search_layout(M, K, NP, n_grid, &L)) return AWQ_ERR_SHAPE;
   if (ws == nullptr || ws_bytes < L.total) return AWQ_ERR_WORKSPACE;
   if (!aligned16(ws) || !aligned16(a)) return AWQ_ERR_INVALID_ARG;
   if (s_table_out != nullptr && !aligned16(s_table_out)) return AWQ_ERR_INVALID_ARG;
@@ -193,22 +212,38 @@ AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, i
   double* partial = reinterpret_cast<double*>(base + L.partial);
   const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const awq::SearchPlan plan = awq::search_plan(M, K, N, n_grid);
+  const awq::SearchPlan plan = awq::search_plan(M, K, NP, n_grid);
 
   hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
-  if (e == hipSuccess)
-    e = awq::launch_group_range(W, wf32, N, K, ldw, s_tab, n_grid, params, flags, s);
+  for (int i = 0; i < n_weights && e == hipSuccess; ++i)
+    e = awq::launch_group_range(Ws[i], wf32, Ns[i], K, ldws[i], s_tab, n_grid, params, segs.tile0[i] * 128,
+                                NP, flags, s);
   if (e == hipSuccess && fused_begin != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
   if (e == hipSuccess)
-    e = awq::launch_search_fused(X, xf32, M, ldx, W, wf32, N, K, ldw, s_tab, rs_tab, sr_tab,
-                                 params, n_grid, plan, partial, s);
+    e = awq::launch_search_fused(X, xf32, M, ldx, segs, wf32, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
+                                 partial, s);
   if (e == hipSuccess && fused_end != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_end), s);
   if (e == hipSuccess)
-    e = awq::launch_select(partial, plan.tiles, n_grid, M, N, K, s_tab, losses_out, best_out,
+    e = awq::launch_select(partial, plan.tiles, n_grid, M, n_total, K, s_tab, losses_out, best_out,
                            s_best_out, flags, s);
   return map_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                             int32_t group, int32_t n_grid, double* losses_out,
+                             int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
+                             size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
+                             awq_event_t fused_begin, awq_event_t fused_end) {
+  const void* Ws[1] = {W};
+  return search_impl(X, x_dtype, M, K, ldx, Ws, w_dtype, &N, &ldw, 1, a, group, n_grid, losses_out, best_out,
+                     s_best_out, s_table_out, ws, ws_bytes, flags, stream, fused_begin, fused_end);
 }
 
 AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -219,6 +254,31 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
   return awq_search_timed(X, x_dtype, M, K, ldx, W, w_dtype, N, ldw, a, group, n_grid,
                           losses_out, best_out, s_best_out, s_table_out, ws, ws_bytes, flags,
                           stream, nullptr, nullptr);
+}
+
+AWQ_API size_t awq_search_multi_workspace_bytes(int64_t M, int64_t K, const int64_t* Ns, int32_t n_weights,
+                                                int32_t group, int32_t n_grid) {
+  if (M <= 0 || K <= 0 || Ns == nullptr || n_weights < 1 || n_weights > awq::kMaxWSegs || group != kGroup ||
+      K % kGroup != 0 || n_grid < 1 || n_grid > 64)
+    return 0;
+  int64_t NP = 0;
+  for (int i = 0; i < n_weights; ++i) {
+    if (Ns[i] <= 0 || Ns[i] > INT64_MAX / 4) return 0;
+    NP += awq::padded_n(Ns[i]);
+    if (NP < 0 || NP > INT64_MAX / 4) return 0;
+  }
+  SearchLayout L;
+  if (!search_layout(M, K, NP, n_grid, &L)) return 0;
+  return L.total;
+}
+
+AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             const void* const* Ws, int w_dtype, const int64_t* Ns, const int64_t* ldws,
+                             int32_t n_weights, const float* a, int32_t group, int32_t n_grid,
+                             double* losses_out, int32_t* best_out, float* s_best_out, float* s_table_out,
+                             void* ws, size_t ws_bytes, uint32_t* flags, awq_stream_t stream) {
+  return search_impl(X, x_dtype, M, K, ldx, Ws, w_dtype, Ns, ldws, n_weights, a, group, n_grid, losses_out,
+                     best_out, s_best_out, s_table_out, ws, ws_bytes, flags, stream, nullptr, nullptr);
 }
 
 AWQ_API int awq_pack_clipped(const void* W, int w_dtype, int64_t N, int64_t K, int64_t ldw,

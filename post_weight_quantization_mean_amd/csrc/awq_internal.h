@@ -83,24 +83,53 @@ __host__ __device__ inline int64_t range_slot(int64_t n) {
   return (n / 128) * 128 + (r / 32) * 32 + 2 * (r % 16) + (r % 32) / 16;
 }
 
+// Projections that read the same X and share one scale vector (query/key/value, gate/up) are
+// searched as one layer: their weights are segments of one row space, each padded to a whole
+// number of 128-row tiles so that a tile never mixes two weights.  Passed to kernels by value
+// and read with constant indices only (a run-time index into kernel arguments would copy them
+// to scratch memory).
+constexpr int kMaxWSegs = 8;
+struct WSegs {
+  const void* w[kMaxWSegs];
+  int64_t ldw[kMaxWSegs];
+  int64_t n[kMaxWSegs];              // rows of each weight
+  int64_t tile0[kMaxWSegs + 1];      // first 128-row tile of each weight; tile0[count] = all tiles
+  int count;
+};
+struct WSel {
+  const void* w;
+  int64_t ldw, n;  // the tile's weight, its row stride and rows
+  int64_t n0;      // first row of the tile within that weight
+};
+__host__ __device__ inline WSel select_wseg(const WSegs& S, int64_t tile_n) {
+  WSel r{S.w[0], S.ldw[0], S.n[0], tile_n * 128};
+#pragma unroll
+  for (int i = 1; i < kMaxWSegs; ++i)
+    if (i < S.count && tile_n >= S.tile0[i]) r = WSel{S.w[i], S.ldw[i], S.n[i], (tile_n - S.tile0[i]) * 128};
+  return r;
+}
+
 struct SearchPlan {
   int64_t mt, nt;    // tiles along M and N
   int64_t tiles;     // mt * nt
   int64_t blocks;    // launched blocks (multiple of 8)
   int64_t groups;    // K / 128
 };
+// N: rows of the padded row space (the sum of the weights' rows, each rounded up to 128)
 SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid);
 
 // s_tab, rs_tab: fp32 [n_grid, K]; sr_tab: the same pairs interleaved, float2 [n_grid, K]
 hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
                               float2* sr_tab, uint32_t* flags, hipStream_t st);
+// params: float2 [n_grid, K/128, NP] over the padded row space of NP rows; one launch per
+// weight, whose rows start at padded row row_base (a multiple of 128)
 hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
-                              const float* s_tab, int n_grid, float2* params, uint32_t* flags,
-                              hipStream_t st);
-hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const void* W,
-                               bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s_tab,
-                               const float* rs_tab, const float2* sr_tab, const float2* params,
-                               int n_grid, const SearchPlan& plan, double* partial, hipStream_t st);
+                              const float* s_tab, int n_grid, float2* params, int64_t row_base,
+                              int64_t NP, uint32_t* flags, hipStream_t st);
+hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
+                               bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
+                               const float2* sr_tab, const float2* params, int n_grid,
+                               const SearchPlan& plan, double* partial, hipStream_t st);
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
                          float* s_best, uint32_t* flags, hipStream_t st);

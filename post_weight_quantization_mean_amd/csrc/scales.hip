@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kRangeThreads) void group_range_kernel(const void* 
                                                                    int64_t K, int64_t ldw,
                                                                    const float* __restrict__ s_tab,
                                                                    int n_grid, float2* __restrict__ params,
+                                                                   int64_t row_base, int64_t NP,
                                                                    uint32_t* __restrict__ flags) {
   // dynamic LDS: this group's scales for every candidate (n_grid x 128 floats), then the
   // (Delta, z) of every candidate and row (n_grid x 64 float2)
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(kRangeThreads) void group_range_kernel(const void* 
   float4* ss = dyn;
   float2* out = reinterpret_cast<float2*>(dyn + n_grid * (kGroup / 4));
   const int64_t G = K / kGroup;
-  const int64_t NP = padded_n(N);
+  const int64_t NPw = padded_n(N);  // this weight's padded rows (of the NP in the table)
   const int64_t g = blockIdx.y;
   const int64_t nb = (int64_t)blockIdx.x * kRangeRows;   // first row of the block
   const int tid = threadIdx.x;
@@ -174,13 +175,14 @@ __global__ __launch_bounds__(kRangeThreads) void group_range_kernel(const void* 
     }
   }
   __syncthreads();
-  // rows nb .. nb + 63 occupy 64 consecutive slots starting at range_slot(nb)
-  const int64_t slot0 = range_slot(nb);
+  // rows nb .. nb + 63 occupy 64 consecutive slots starting at range_slot(nb), after the
+  // row_base padded rows of the weights before this one
+  const int64_t slot0 = row_base + range_slot(nb);
   for (int t = tid; t < n_grid * kRangeRows; t += kRangeThreads) {
     const int al = t / kRangeRows, j = t % kRangeRows;  // j: slot offset
     // slot offset j = 32 w' + 2 jj + i  <->  row offset 32 w' + 16 i + jj
     const int r = (j & ~31) + 16 * (j & 1) + ((j & 31) >> 1);
-    if (nb + r < NP) params[((int64_t)al * G + g) * NP + slot0 + j] = out[al * kRangeRows + r];
+    if (nb + r < NPw) params[((int64_t)al * G + g) * NP + slot0 + j] = out[al * kRangeRows + r];
   }
   if (live && bad) atomicOr(flags, kFlagNonfiniteW);
 }
@@ -229,14 +231,16 @@ hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_ta
 }
 
 hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
-                              const float* s_tab, int n_grid, float2* params, uint32_t* flags,
-                              hipStream_t st) {
+                              const float* s_tab, int n_grid, float2* params, int64_t row_base,
+                              int64_t NP, uint32_t* flags, hipStream_t st) {
   const dim3 grid((unsigned)((N + kRangeRows - 1) / kRangeRows), (unsigned)(K / kGroup));
   const size_t lds = (size_t)n_grid * (kGroup * 4 + kRangeRows * 8);  // <= 64 KiB (n_grid <= 64)
   if (wf32)
-    group_range_kernel<true><<<grid, kRangeThreads, lds, st>>>(W, N, K, ldw, s_tab, n_grid, params, flags);
+    group_range_kernel<true><<<grid, kRangeThreads, lds, st>>>(W, N, K, ldw, s_tab, n_grid, params, row_base,
+                                                               NP, flags);
   else
-    group_range_kernel<false><<<grid, kRangeThreads, lds, st>>>(W, N, K, ldw, s_tab, n_grid, params, flags);
+    group_range_kernel<false><<<grid, kRangeThreads, lds, st>>>(W, N, K, ldw, s_tab, n_grid, params, row_base,
+                                                                NP, flags);
   return hipGetLastError();
 }
 

@@ -68,8 +68,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 template <bool XF32, bool WF32>
 __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
-    const void* __restrict__ X, int64_t M, int64_t ldx, const void* __restrict__ W, int64_t N,
-    int64_t K, int64_t ldw, const float* __restrict__ s_tab, const float* __restrict__ rs_tab,
+    const void* __restrict__ X, int64_t M, int64_t ldx, const WSegs segs, int64_t K,
+    const float* __restrict__ s_tab, const float* __restrict__ rs_tab,
     const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles,
     int64_t per_xcd, double* __restrict__ partial) {
   using Gm = Geo<XF32, WF32>;
@@ -90,7 +90,11 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
   const int64_t tile = L / n_grid;
   const int al = (int)(L - tile * n_grid);
   const int64_t m0 = (tile / nt_count) * BM;
-  const int64_t n0 = (tile % nt_count) * BN;
+  const int64_t n0 = (tile % nt_count) * BN;  // in the padded row space of all weights
+  // the weight this tile belongs to; n0w: the tile's first row within it
+  const WSel sel = select_wseg(segs, tile % nt_count);
+  const void* __restrict__ W = sel.w;
+  const int64_t N = sel.n, ldw = sel.ldw, n0w = sel.n0;
   const int64_t G = K / kGroup;
   const int64_t nchunks = K / KC;
 
@@ -108,13 +112,13 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
 
   // Buffer resources rebased at this tile: rows past M (or N) fall outside num_records and
   // read as zero, so tail tiles need no branches.  Offsets stay below 2^31 (host-checked).
-  const int64_t xrows = M - m0, wrows = N - n0;
+  const int64_t xrows = M - m0, wrows = N - n0w;
   const int64_t xbytes = xrows * ldx * XSZ, wbytes = wrows * ldw * WSZ;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(static_cast<const char*>(X) + m0 * ldx * XSZ), (short)0,
       (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const char*>(W) + n0 * ldw * WSZ), (short)0,
+      (void*)(static_cast<const char*>(W) + n0w * ldw * WSZ), (short)0,
       (int)(wbytes < 0x7fffffff ? wbytes : 0x7fffffff), 0x00020000);
   const uint32_t xoff0 = (uint32_t)(xrow0 * ldx * XSZ + xkp * 16);
   const uint32_t xstep = (uint32_t)(64 * ldx * XSZ);
@@ -123,15 +127,15 @@ __global__ __launch_bounds__(THREADS, 1) void search_fused_kernel(
 
   const float* srow = s_tab + (int64_t)al * K + wkp * WEL;
   const float* rsrow = rs_tab + (int64_t)al * K + wkp * WEL;
-  // group ranges of this thread's W rows (rows past N read row N-1 and are masked)
-  const int64_t NP = padded_n(N);
+  // group ranges of this thread's W rows (rows past the weight's N are masked)
+  const int64_t NP = nt_count * BN;
   const float2* prow[WP];  // this thread's rows in the range table of candidate al
   bool wlive[WP];
 #pragma unroll
   for (int i = 0; i < WP; ++i) {
-    const int64_t n = n0 + wrow0 + Gm::WROW_STEP * i;  // < NP (tiles never pass NP)
-    wlive[i] = n < N;
-    prow[i] = params + (int64_t)al * G * NP + range_slot(n);
+    const int64_t r = wrow0 + Gm::WROW_STEP * i;
+    wlive[i] = n0w + r < N;
+    prow[i] = params + (int64_t)al * G * NP + range_slot(n0 + r);  // n0 + r < NP
   }
 
   uint4 xr[XP];
@@ -348,10 +352,9 @@ struct RowQ {
 };
 
 __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
-    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const uint16_t* __restrict__ W,
-    int64_t N, int64_t K, int64_t ldw, const float2* __restrict__ sr_tab,
-    const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles,
-    int64_t per_xcd, double* __restrict__ partial) {
+    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const WSegs segs, int64_t K,
+    const float2* __restrict__ sr_tab, const float2* __restrict__ params, int n_grid,
+    int64_t nt_count, int64_t tiles, int64_t per_xcd, double* __restrict__ partial) {
   // X pair stages (pairs 0, 2, 4, ... in xp0; 1, 3, 5, ... in xp1), each split into the first
   // and the last 64 of every wave's 128 rows: distinct LDS objects, so reads of one half never
   // wait for the DMA into the other
@@ -370,9 +373,13 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int64_t tile = L / n_grid;
   const int al = (int)(L - tile * n_grid);
   const int64_t m0 = (tile / nt_count) * BM;
-  const int64_t n0 = (tile % nt_count) * BN;
+  const int64_t n0 = (tile % nt_count) * BN;  // in the padded row space of all weights
+  // the weight this tile belongs to; n0w: the tile's first row within it
+  const WSel sel = select_wseg(segs, tile % nt_count);
+  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(sel.w);
+  const int64_t N = sel.n, ldw = sel.ldw, n0w = sel.n0;
   const int G = (int)(K / kGroup);
-  const int64_t NP = padded_n(N);
+  const int64_t NP = nt_count * BN;
   const int nchunks = (int)(K / PKC);
 
   const int tid = threadIdx.x;
@@ -381,11 +388,11 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
 
   // Buffer resources are rebased at this tile so rows past M (or N) read as zero; offsets
   // stay below 2^31 (host-checked: 512 rows of X, 128 rows of W).
-  const int64_t xbytes = (M - m0) * ldx * 2, wbytes = (N - n0) * ldw * 2;
+  const int64_t xbytes = (M - m0) * ldx * 2, wbytes = (N - n0w) * ldw * 2;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + n0 * ldw), (short)0, (int)(wbytes < 0x7fffffff ? wbytes : 0x7fffffff), 0x00020000);
+      (void*)(W + n0w * ldw), (short)0, (int)(wbytes < 0x7fffffff ? wbytes : 0x7fffffff), 0x00020000);
   // this candidate's (s, 1/s) pairs: K float2 = 8 K bytes (< 2^24: K <= ldx < 2^21 follows
   // from the host check on 512 rows of X)
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const uint32_t woff1 = (uint32_t)(r1 * ldw * 2 + q4 * 16);
   const int eslot0 = r0 * PROW + ((q4 ^ swz(r0)) * 16);
   const int eslot1 = r1 * PROW + ((q4 ^ swz(r1)) * 16);
-  const bool live0 = n0 + r0 < N, live1 = n0 + r1 < N;
+  const bool live0 = n0w + r0 < N, live1 = n0w + r1 < N;
   // ranges of rows r0 and r1 are adjacent (range_slot); rows past N are masked.  A buffer
   // resource over this candidate's ranges (G Npad float2 < 2^31 bytes: host-checked) reads
   // groups past the end as zero.
@@ -727,20 +734,19 @@ SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
   return p;
 }
 
-hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const void* W,
-                               bool wf32, int64_t N, int64_t K, int64_t ldw, const float* s_tab,
-                               const float* rs_tab, const float2* sr_tab, const float2* params,
-                               int n_grid, const SearchPlan& plan, double* partial, hipStream_t st) {
+hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
+                               bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
+                               const float2* sr_tab, const float2* params, int n_grid,
+                               const SearchPlan& plan, double* partial, hipStream_t st) {
   const int64_t per_xcd = plan.blocks / 8;
   const dim3 grid((unsigned)plan.blocks);
-#define AWQ_LAUNCH(XF, WF)                                                                      \
-  search_fused_kernel<XF, WF><<<grid, THREADS, 0, st>>>(X, M, ldx, W, N, K, ldw, s_tab, rs_tab, \
-                                                        params, n_grid, plan.nt, plan.tiles,    \
-                                                        per_xcd, partial)
+#define AWQ_LAUNCH(XF, WF)                                                                  \
+  search_fused_kernel<XF, WF><<<grid, THREADS, 0, st>>>(X, M, ldx, W, K, s_tab, rs_tab, params, \
+                                                        n_grid, plan.nt, plan.tiles, per_xcd,   \
+                                                        partial)
   if (!xf32 && !wf32) {
-    search_pipelined_kernel<<<grid, THREADS, 0, st>>>(
-        static_cast<const uint16_t*>(X), M, ldx, static_cast<const uint16_t*>(W), N, K, ldw, sr_tab,
-        params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
+    search_pipelined_kernel<<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K, sr_tab,
+                                                      params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
     return hipGetLastError();
   }
   if (xf32 && wf32)

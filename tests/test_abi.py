@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
                           "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack",
+                          "awq_search_multi_workspace_bytes", "awq_search_multi",
                           "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip", "awq_fold_rows",
                           "awq_scale_cols", "awq_scaled_act", "awq_w4a16"}
 
@@ -41,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 4
+    assert L.awq_abi_version() == 5
     for st in range(6):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
@@ -112,6 +113,43 @@ def test_search_timed_argument_errors(L, kw, status):
     assert L.awq_search_timed(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["W"], a["wt"], a["N"], a["ldw"],
                               a["a"], a["group"], a["n_grid"], a["losses"], a["best"], a["sb"], a["tab"],
                               a["ws"], a["wsb"], a["fl"], None, None, None) == status
+
+
+def search_multi(L, X=P, xt=BF16, M=64, K=256, ldx=256, Ws=(P, P + 4096), wt=BF16, Ns=(128, 64), ldws=(256, 256),
+                 count=None, a=P, group=128, n_grid=20, losses=P, best=P, sb=P, tab=None, ws=P, wsb=1 << 30, fl=P):
+    n = 2 if count is None else count
+    arr = lambda typ, v: None if v is None else (typ * max(len(v), 1))(*v)
+    return L.awq_search_multi(X, xt, M, K, ldx, arr(ctypes.c_void_p, Ws), wt, arr(ctypes.c_int64, Ns),
+                              arr(ctypes.c_int64, ldws), n, a, group, n_grid, losses, best, sb, tab, ws, wsb, fl,
+                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(Ws=None), INVALID), (dict(Ns=None), INVALID), (dict(ldws=None), INVALID),
+    (dict(count=0), INVALID), (dict(count=9, Ws=(P,) * 9, Ns=(128,) * 9, ldws=(256,) * 9), INVALID),
+    (dict(Ws=(P, None)), INVALID), (dict(Ns=(128, 0)), INVALID), (dict(ldws=(256, 128)), INVALID),
+    (dict(Ws=(P, P + 8)), INVALID),  # the second weight is not 16-byte aligned
+    (dict(ldws=(256, 1 << 24)), SHAPE),  # 128 rows of the second weight span 2^32 bytes
+    (dict(group=64), UNSUP), (dict(wt=2), UNSUP), (dict(n_grid=0), INVALID), (dict(a=None), INVALID),
+    (dict(ws=None), WS), (dict(wsb=1000), WS),
+])
+def test_search_multi_argument_errors(L, kw, status):
+    assert search_multi(L, **kw) == status
+
+
+def test_search_multi_workspace_pads_each_weight(L):
+    ns = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    one = L.awq_search_multi_workspace_bytes(4096, 4096, ns(4096), 1, 128, 20)
+    assert one == L.awq_search_workspace_bytes(4096, 4096, 4096, 128, 20)
+    # three 4096-row weights take the space of one 12288-row weight
+    assert L.awq_search_multi_workspace_bytes(4096, 4096, ns(4096, 4096, 4096), 3, 128, 20) == \
+        L.awq_search_workspace_bytes(4096, 4096, 12288, 128, 20)
+    # 100 + 100 rows pad to two tiles, more than one 200-row weight (also two tiles) never less
+    assert L.awq_search_multi_workspace_bytes(512, 256, ns(100, 100), 2, 128, 20) >= \
+        L.awq_search_workspace_bytes(512, 256, 200, 128, 20)
+    assert L.awq_search_multi_workspace_bytes(512, 256, ns(100, 0), 2, 128, 20) == 0
+    assert L.awq_search_multi_workspace_bytes(512, 256, None, 2, 128, 20) == 0
+    assert L.awq_search_multi_workspace_bytes(512, 256, ns(*([128] * 9)), 9, 128, 20) == 0
 
 
 def pack(L, W=P, wt=BF16, N=128, K=256, ldw=256, s=P, group=128, q=P, sc=P, z=P, fl=P):
