@@ -38,7 +38,9 @@ Readings where the pages are silent (each is listed in the design doc):
   has no fused multiply-add), correctly rounded division, ties-to-even rounding.  The
   scale table is computed in fp64 and rounded once to fp32.  The loss is fp64.
 * The loss of a candidate is the mean over the M x N outputs of (X E)^2 with
-  E = W - S^-1 Q(S W): the module-output MSE of §4 for a single linear layer.
+  E = W - S^-1 Q(S W): the module-output MSE of §4 for a single linear layer.  Its Gram form
+  sum_n E[n] (X^T X) E[n]^T / (M N) (§1: the exact error carries the cross terms of X^T X) is
+  the same number in exact arithmetic.
 * Clipping: the threshold of candidate i is fp32(absmax * fp32(1 - i/20)) of the scaled
   weight v = fp32(W s); the clipped group clamp(v, -c, c) goes through the same asymmetric
   quantizer; the error of (n, g) is the mean over the given tokens of
@@ -230,6 +232,33 @@ def search(X: np.ndarray, W: np.ndarray, a32: np.ndarray, group: int = GROUP, n_
     best = first_argmin(list(losses))
     return {"losses": losses, "best": best, "s_table": s_tab, "rs_table": rs_tab,
             "s_best": s_tab[best].copy(), "alpha_best": alpha_grid(n_grid)[best]}
+
+
+def gram_matrix(X: np.ndarray) -> np.ndarray:
+    """G = X^T X [K x K] in float64 ([EXPLAINER §1]: the cross terms of the inputs that the
+    exact layer-output squared error depends on, beyond the per-channel statistic)."""
+    X64 = np.asarray(X, dtype=np.float64)
+    return X64.T @ X64
+
+
+def gram_loss(G: np.ndarray, M: int, E: np.ndarray) -> float:
+    """mean over the M x N outputs of (X E^T)^2 written through G = X^T X:
+    sum_n E[n,:] G E[n,:]^T / (M N), all in float64 (E [N, K])."""
+    E64 = np.asarray(E, dtype=np.float64)
+    return float(np.einsum("nk,nk->", E64 @ G, E64)) / (M * E64.shape[0])
+
+
+def gram_search_losses(X: np.ndarray, W: np.ndarray, s_table: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Every candidate's loss (the scale table s_table [n_grid, K]) in the Gram form: the same
+    quantities as ``search``'s losses, evaluated through G = X^T X formed once."""
+    X64 = np.asarray(X, dtype=np.float64)
+    W32 = np.asarray(W, dtype=np.float32)
+    G = gram_matrix(X64)
+    out = np.empty(len(s_table))
+    for i, s in enumerate(s_table):
+        q, z, d = quantize(W32, s, group)
+        out[i] = gram_loss(G, X64.shape[0], W32.astype(np.float64) - effective_weight(q, z, d, s, group))
+    return out
 
 
 def search_tiles(X: np.ndarray, W: np.ndarray, s32: np.ndarray, rows: Tuple[int, int],
