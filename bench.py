@@ -134,6 +134,39 @@ def clip_search(torch, awq, Xd, Wd, s_best, stride: int = 8, reps: int = 10):
             "note": "whole awq_clip call (range pre-pass, clipped qdq + bf16 MFMA product, select)"}
 
 
+def gram_form(torch, awq, dev, reps: int = 3):
+    """The scale search in both loss forms on the decoder block's qkv layer (M = 16384 tokens,
+    K = 4096, N = 6144, bf16): the direct form (20 x 2 M K N flop on the matrix cores) and the
+    Gram form (G = X^T X once, 2 M K^2 flop, then 20 x 2 (2K) K N flop for the [G_hi; G_lo]
+    stack).  Whole calls, event-timed; seeded random values with the workload's shapes."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    M, K, N = 16384, 4096, 6144
+    c = torch.exp(0.5 * torch.randn(K, generator=g, device=dev))
+    X = (torch.randn((M, K), generator=g, device=dev) * c).to(torch.bfloat16)
+    W = torch.randn((N, K), generator=g, device=dev).mul_(K ** -0.5).to(torch.bfloat16)
+    a = awq.stats(X)
+    ws = torch.empty(max(awq.search_workspace_bytes(M, K, N), awq.search_workspace_bytes(M, K, N, gram=True)),
+                     dtype=torch.uint8, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    out = {}
+    for name, gram in (("direct", False), ("gram", True)):
+        out[name] = awq.search(X, W, a, workspace=ws, flags=fl, check=False, gram=gram)
+        ms = _time_reps(torch, lambda: awq.search(X, W, a, workspace=ws, flags=fl, check=False, gram=gram), reps)
+        flop = 20 * 2.0 * (2 * K if gram else M) * K * N + (2.0 * M * K * K if gram else 0.0)
+        res[name] = {"ms": ms, "flop": flop, "tflops": flop / (ms * 1e-3) / 1e12,
+                     "best": out[name].best_index}
+    awq.raise_for_flags(fl)
+    Ld, Lg = out["direct"].losses.double(), out["gram"].losses.double()
+    res["shape"] = [M, K, N]
+    res["speedup"] = res["direct"]["ms"] / res["gram"]["ms"]
+    res["max_rel_loss_diff"] = float(((Lg - Ld).abs() / Ld).max())
+    res["direct_equiv_tflops"] = res["direct"]["flop"] / (res["gram"]["ms"] * 1e-3) / 1e12
+    res["note"] = "whole awq_search / awq_search_gram calls; direct_equiv_tflops = direct-form flop / gram time"
+    return res
+
+
 def fold_ops(torch, awq, dev, reps: int = 10):
     """Applying the scales, at the decoder block's largest shapes: awq_scale_cols in place on the
     fused gate+up weight bf16 [28672 x 4096] and awq_scaled_act (GELU) from the MLP activation
@@ -238,6 +271,7 @@ def main():
     ap.add_argument("--no-clip", action="store_true", help="skip the clipping-search timing")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 product timing")
     ap.add_argument("--no-fold", action="store_true", help="skip the scale-application timing")
+    ap.add_argument("--no-gram", action="store_true", help="skip the Gram-form search timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -358,6 +392,8 @@ def main():
         out["w4a16"] = w4a16_products(torch, awq, dev)
     if not args.no_fold:
         out["fold"] = fold_ops(torch, awq, dev)
+    if not args.no_gram:
+        out["gram"] = gram_form(torch, awq, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
     print(json.dumps(out), flush=True)

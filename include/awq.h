@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 5
+#define AWQ_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -160,6 +160,29 @@ AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, i
                              int32_t group, int32_t n_grid, double* losses_out,
                              int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
                              size_t ws_bytes, uint32_t* flags, awq_stream_t stream);
+
+/* The same search with the loss in its Gram form ([EXPLAINER §1]: the exact layer-output
+ * squared error carries the cross terms of X^T X):
+ *   sum_{m,n} (X E^T)[m,n]^2 = sum_n E[n,:] G E[n,:]^T,   G = X^T X,
+ * with G formed once on the matrix cores (fp32 sums per 1024 tokens, then across blocks) and
+ * kept as G_hi + G_lo, two bf16 matrices (16 significand bits of G).  Every candidate then
+ * multiplies the [2K, K] stack [G_hi; G_lo] with E^T (2 * 2 K^2 N flop instead of 2 M K N:
+ * less work when M > 2K) and dots each output with E[n, k'].  The losses differ from
+ * awq_search's only by rounding: G's representation (2^-16 relative per entry) and its sums,
+ * and the sums over k of products that cancel (the quadratic form), where the direct form
+ * sums squares.  Candidates, codes, tie rule and outputs as awq_search.
+ *   X, W   AWQ_DTYPE_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); 512 x K bf16 must span less
+ *          than 2^31 bytes
+ *   ws     workspace of at least awq_search_gram_workspace_bytes(...) bytes: the search
+ *          workspace for 2K rows plus Gs (2K x K bf16)
+ * Other arguments, results and errors as awq_search. */
+AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
+                                               int32_t n_grid);
+AWQ_API int awq_search_gram(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                            const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                            int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
+                            float* s_best_out, float* s_table_out, void* ws, size_t ws_bytes,
+                            uint32_t* flags, awq_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Step 5: real quantization and packing of S W ([EXPLAINER §7, §8]; [MODULES §5.3]:

@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
                                  i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
         L.awq_search_timed.restype = ctypes.c_int
         L.awq_search_timed.argtypes = L.awq_search.argtypes + [vp, vp]
+        L.awq_search_gram_workspace_bytes.restype = sz
+        L.awq_search_gram_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+        L.awq_search_gram.restype = ctypes.c_int
+        L.awq_search_gram.argtypes = L.awq_search.argtypes
         L.awq_search_multi_workspace_bytes.restype = sz
         L.awq_search_multi_workspace_bytes.argtypes = [i64, i64, vp, i32, i32, i32]
         L.awq_search_multi.restype = ctypes.c_int
@@ -92,7 +96,7 @@ def lib() -> ctypes.CDLL:
         L.awq_scaled_act.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp]
         L.awq_w4a16.restype = ctypes.c_int
         L.awq_w4a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i32, vp, i64, vp]
-        if L.awq_abi_version() != 5:
+        if L.awq_abi_version() != 6:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -137,8 +141,10 @@ def stats_workspace_bytes(M: int, K: int) -> int:
     return int(lib().awq_stats_workspace_bytes(M, K))
 
 
-def search_workspace_bytes(M: int, K: int, N, group: int = GROUP, n_grid: int = N_GRID) -> int:
+def search_workspace_bytes(M: int, K: int, N, group: int = GROUP, n_grid: int = N_GRID, gram: bool = False) -> int:
     """N: the weight's rows, or a sequence of several weights' rows (awq_search_multi)."""
+    if gram:
+        return int(lib().awq_search_gram_workspace_bytes(M, K, N, group, n_grid))
     if isinstance(N, (list, tuple)):
         ns = (ctypes.c_int64 * len(N))(*N)
         return int(lib().awq_search_multi_workspace_bytes(M, K, ns, len(N), group, n_grid))
@@ -177,12 +183,15 @@ class SearchResult:
 
 def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid: int = N_GRID,
            *, return_table: bool = False, workspace: Optional[torch.Tensor] = None,
-           flags: Optional[torch.Tensor] = None, check: bool = True,
+           flags: Optional[torch.Tensor] = None, check: bool = True, gram: bool = False,
            fused_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> SearchResult:
     """The candidate scale search over alpha = i / n_grid for one layer.  ``W`` is one weight
     [N, K], or a list of weights [N_w, K] of projections that read X and share the scales
     (query/key/value, gate/up): searched as one layer without concatenating them
     (awq_search_multi), all of one dtype.
+
+    ``gram``: evaluate the losses in the Gram form sum_n E[n] (X^T X) E[n]^T (awq_search_gram;
+    bf16 X and a single bf16 W): cheaper when M > 2K, equal up to rounding.
 
     ``fused_events``: two timing events that the library records right before and after the
     fused candidate kernel (awq_search_timed), so that ``e0.elapsed_time(e1)`` is that
@@ -197,8 +206,8 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
         shapes = [_matrix(w, f"W[{i}]") for i, w in enumerate(Ws)]
         if any(kw != K for _, kw, _ in shapes):
             raise ValueError("X and W disagree on K")
-        if fused_events is not None:
-            raise ValueError("fused_events times a single-weight search")
+        if fused_events is not None or gram:
+            raise ValueError("fused_events and the Gram form take a single weight")
         N = [n for n, _, _ in shapes]
     else:
         N, Kw, ldw = _matrix(W, "W")
@@ -211,7 +220,9 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
     best = torch.empty(1, dtype=torch.int32, device=dev)
     s_best = torch.empty(K, dtype=torch.float32, device=dev)
     s_table = torch.empty((n_grid, K), dtype=torch.float32, device=dev) if return_table else None
-    need = search_workspace_bytes(M, K, N, group_size, n_grid)
+    if gram and fused_events is not None:
+        raise ValueError("fused_events times the direct form")
+    need = search_workspace_bytes(M, K, N, group_size, n_grid, gram=gram)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
     outs = (a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(),
@@ -228,7 +239,9 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
             raise_for_flags(fl)
         return SearchResult(losses, best, s_best, s_table, fl)
     args = (X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw) + outs
-    if fused_events is None:
+    if gram:
+        st = lib().awq_search_gram(*args)
+    elif fused_events is None:
         st = lib().awq_search(*args)
     else:
         evs = []

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libawq.so")
 
-SOURCES = ["stats.hip", "scales.hip", "search.hip", "pack.hip", "clip.hip", "fold.hip", "w4a16.hip", "awq_api.cpp"]
+SOURCES = ["stats.hip", "scales.hip", "search.hip", "gram.hip", "pack.hip", "clip.hip", "fold.hip", "w4a16.hip",
+           "awq_api.cpp"]
 
 # -ffp-contract=off: every fp32 operation of the quantizer contract is rounded on its own
 #   (fused multiply-adds are written explicitly where the search wants them).

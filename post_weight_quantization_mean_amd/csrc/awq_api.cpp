@@ -167,7 +167,7 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
                 int w_dtype, const int64_t* Ns, const int64_t* ldws, int32_t n_weights, const float* a,
                 int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out, float* s_best_out,
                 float* s_table_out, void* ws, size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
-                awq_event_t fused_begin, awq_event_t fused_end) {
+                awq_event_t fused_begin, awq_event_t fused_end, bool gram = false) {
   int st = check_matrix(X, x_dtype, M, K, ldx);
   if (st != AWQ_OK) return st;
   if (Ws == nullptr || Ns == nullptr || ldws == nullptr || n_weights < 1 || n_weights > awq::kMaxWSegs)
@@ -198,9 +198,20 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   if (mul_ok(mul_ok(awq::kSearchBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
   // one candidate's group ranges (float2 [K/128][NP]) are addressed with 32-bit offsets
   if (mul_ok(mul_ok(K / kGroup, NP), 8) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  // Gram form: the product's left operand is Gs [2K, K] bf16 (rows of G_hi, then G_lo)
+  if (gram && (x_dtype != AWQ_DTYPE_BF16 || w_dtype != AWQ_DTYPE_BF16)) return AWQ_ERR_UNSUPPORTED;
+  if (gram && mul_ok(mul_ok(awq::kSearchBM, K), 2) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  const int64_t rows = gram ? 2 * K : M;  // rows of the product's left operand
   SearchLayout L;
-  if (!search_layout(M, K, NP, n_grid, &L)) return AWQ_ERR_SHAPE;
-  if (ws == nullptr || ws_bytes < L.total) return AWQ_ERR_WORKSPACE;
+  if (!search_layout(rows, K, NP, n_grid, &L)) return AWQ_ERR_SHAPE;
+  size_t total = L.total, gs_off = 0;
+  if (gram) {
+    const int64_t gsb = mul_ok(mul_ok(2 * K, K), 2);
+    if (gsb < 0) return AWQ_ERR_SHAPE;
+    gs_off = total;
+    total += align_up((size_t)gsb);
+  }
+  if (ws == nullptr || ws_bytes < total) return AWQ_ERR_WORKSPACE;
   if (!aligned16(ws) || !aligned16(a)) return AWQ_ERR_INVALID_ARG;
   if (s_table_out != nullptr && !aligned16(s_table_out)) return AWQ_ERR_INVALID_ARG;
 
@@ -212,15 +223,20 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   double* partial = reinterpret_cast<double*>(base + L.partial);
   const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const awq::SearchPlan plan = awq::search_plan(M, K, NP, n_grid);
+  const awq::SearchPlan plan = awq::search_plan(rows, K, NP, n_grid);
+  uint16_t* Gs = gram ? reinterpret_cast<uint16_t*>(base + gs_off) : nullptr;
 
   hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
+  if (e == hipSuccess && gram) e = awq::launch_gram(static_cast<const uint16_t*>(X), M, K, ldx, Gs, s);
   for (int i = 0; i < n_weights && e == hipSuccess; ++i)
     e = awq::launch_group_range(Ws[i], wf32, Ns[i], K, ldws[i], s_tab, n_grid, params, segs.tile0[i] * 128,
                                 NP, flags, s);
   if (e == hipSuccess && fused_begin != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
-  if (e == hipSuccess)
+  if (e == hipSuccess && gram)
+    e = awq::launch_search_fused(Gs, false, rows, K, segs, false, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
+                                 partial, s, true);
+  else if (e == hipSuccess)
     e = awq::launch_search_fused(X, xf32, M, ldx, segs, wf32, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
                                  partial, s);
   if (e == hipSuccess && fused_end != nullptr)
@@ -254,6 +270,26 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
   return awq_search_timed(X, x_dtype, M, K, ldx, W, w_dtype, N, ldw, a, group, n_grid,
                           losses_out, best_out, s_best_out, s_table_out, ws, ws_bytes, flags,
                           stream, nullptr, nullptr);
+}
+
+AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group, int32_t n_grid) {
+  if (M <= 0 || K <= 0 || N <= 0 || group != kGroup || K % kGroup != 0 || n_grid < 1 || n_grid > 64 ||
+      K > INT64_MAX / 8)
+    return 0;
+  SearchLayout L;
+  if (!search_layout(2 * K, K, N, n_grid, &L)) return 0;
+  const int64_t gsb = mul_ok(mul_ok(2 * K, K), 2);
+  if (gsb < 0) return 0;
+  return L.total + align_up((size_t)gsb);
+}
+
+AWQ_API int awq_search_gram(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const void* W,
+                            int w_dtype, int64_t N, int64_t ldw, const float* a, int32_t group, int32_t n_grid,
+                            double* losses_out, int32_t* best_out, float* s_best_out, float* s_table_out,
+                            void* ws, size_t ws_bytes, uint32_t* flags, awq_stream_t stream) {
+  const void* Ws[1] = {W};
+  return search_impl(X, x_dtype, M, K, ldx, Ws, w_dtype, &N, &ldw, 1, a, group, n_grid, losses_out, best_out,
+                     s_best_out, s_table_out, ws, ws_bytes, flags, stream, nullptr, nullptr, true);
 }
 
 AWQ_API size_t awq_search_multi_workspace_bytes(int64_t M, int64_t K, const int64_t* Ns, int32_t n_weights,

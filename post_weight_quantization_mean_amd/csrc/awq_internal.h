@@ -129,7 +129,9 @@ hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, in
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
                                bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
                                const float2* sr_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st);
+                               const SearchPlan& plan, double* partial, hipStream_t st, bool gram = false);
+// Gram form: Gs bf16 [2K, K] = [bf16(G); bf16(G - bf16(G))], G = X^T X for bf16 X [M, K]
+hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, hipStream_t st);
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
                          float* s_best, uint32_t* flags, hipStream_t st);

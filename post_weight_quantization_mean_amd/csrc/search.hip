@@ -351,6 +351,9 @@ struct RowQ {
   float delta, inv, lo, hi;
 };
 
+// GRAM: X is the stacked [G_hi; G_lo] (2K rows, gram.hip) and the block's result is
+// sum over its outputs of (Gs E^T)[k', n] E[n, k' mod K] instead of the squares.
+template <bool GRAM>
 __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const WSegs segs, int64_t K,
     const float2* __restrict__ sr_tab, const float2* __restrict__ params, int n_grid,
@@ -702,15 +705,71 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   }
 
   double ss = 0.0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
+  if constexpr (GRAM) {
+    // This wave's 128 rows are rows k' = (m0 + 128 wave + ...) mod K of G (the first K rows
+    // of X hold G_hi, the next K G_lo): one whole group gq of K.  Lane l's outputs sit at
+    // k' = kb + 32 r + 8 (i / 4) + 4 (l / 32) + i % 4 and n = n0 + 32 c + l % 32, where it
+    // recomputes e = E[n, k'] exactly as the K loop formed it (before the bf16 rounding).
+    const int kb = (int)((m0 + (int64_t)WAVE_ROWS * wave) % K);
+    const int gq = kb / kGroup;
+    RowQ rq[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float t = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t = fmaf(acc[r][c][i], acc[r][c][i], t);
-      ss += (double)t;
+      const int nl = 32 * c + (lane & 31);
+      const float2 P = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      prsrc, (int)(((int64_t)gq * NP + range_slot(n0 + nl)) * 8), 0, 0));
+      const bool live = n0w + nl < N;
+      rq[c].delta = live ? P.x : 1.0f;  // rows past N: Delta 1, z 0, w 0 (read as zero): e = 0
+      const float z = live ? P.y : 0.0f;
+      rq[c].inv = __builtin_amdgcn_rcpf(rq[c].delta);
+      rq[c].lo = -z;
+      rq[c].hi = 15.0f - z;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4 sv[4][2];  // (s, 1/s) of the four consecutive channels of each i / 4
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int kk = kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          sv[i4][h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, kk * 8 + 16 * h, 0, 0));
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int nl = 32 * c + (lane & 31);
+        float t = 0.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int kk = kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
+          const uint2 w4 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                         wrsrc, (int)(nl * ldw * 2 + kk * 2), 0, 0));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t u = j < 2 ? w4.x : w4.y;
+            const float w = (j & 1) ? bf16_hi(u) : bf16_lo(u);
+            const float4& sp = sv[i4][j >> 1];
+            const float s = (j & 1) ? sp.z : sp.x, rs = (j & 1) ? sp.w : sp.y;
+            const float v = w * s;
+            const float q = __builtin_amdgcn_fmed3f(rintf(v * rq[c].inv), rq[c].lo, rq[c].hi);
+            const float e = fmaf(-(q * rq[c].delta), rs, w);
+            t = fmaf(acc[r][c][4 * i4 + j], e, t);
+          }
+        }
+        ss += (double)t;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t = fmaf(acc[r][c][i], acc[r][c][i], t);
+        ss += (double)t;
+      }
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   // every wave is past its last LDS access (the barrier ending the last step), so the first
@@ -737,16 +796,23 @@ SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
                                bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
                                const float2* sr_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st) {
+                               const SearchPlan& plan, double* partial, hipStream_t st, bool gram) {
   const int64_t per_xcd = plan.blocks / 8;
   const dim3 grid((unsigned)plan.blocks);
 #define AWQ_LAUNCH(XF, WF)                                                                  \
   search_fused_kernel<XF, WF><<<grid, THREADS, 0, st>>>(X, M, ldx, W, K, s_tab, rs_tab, params, \
                                                         n_grid, plan.nt, plan.tiles, per_xcd,   \
                                                         partial)
+  if (gram) {  // bf16 operands only (host-checked)
+    search_pipelined_kernel<true><<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K,
+                                                            sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd,
+                                                            partial);
+    return hipGetLastError();
+  }
   if (!xf32 && !wf32) {
-    search_pipelined_kernel<<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K, sr_tab,
-                                                      params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
+    search_pipelined_kernel<false><<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K,
+                                                             sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd,
+                                                             partial);
     return hipGetLastError();
   }
   if (xf32 && wf32)

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     assert set(names) == {"awq_abi_version", "awq_status_string", "awq_stats_workspace_bytes", "awq_stats",
                           "awq_search_workspace_bytes", "awq_search", "awq_search_timed", "awq_pack",
                           "awq_search_multi_workspace_bytes", "awq_search_multi",
+                          "awq_search_gram_workspace_bytes", "awq_search_gram",
                           "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip", "awq_fold_rows",
                           "awq_scale_cols", "awq_scaled_act", "awq_w4a16"}
 
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 5
+    assert L.awq_abi_version() == 6
     for st in range(6):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
@@ -150,6 +151,29 @@ def test_search_multi_workspace_pads_each_weight(L):
     assert L.awq_search_multi_workspace_bytes(512, 256, ns(100, 0), 2, 128, 20) == 0
     assert L.awq_search_multi_workspace_bytes(512, 256, None, 2, 128, 20) == 0
     assert L.awq_search_multi_workspace_bytes(512, 256, ns(*([128] * 9)), 9, 128, 20) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(W=None), INVALID), (dict(xt=F32), UNSUP), (dict(wt=F32), UNSUP),
+    (dict(group=64), UNSUP), (dict(n_grid=0), INVALID), (dict(a=None), INVALID), (dict(ws=None), WS),
+    (dict(wsb=1000), WS), (dict(K=1 << 21, ldx=1 << 21, ldw=1 << 21), SHAPE),  # 512 rows of G span 2^31
+])
+def test_search_gram_argument_errors(L, kw, status):
+    a = dict(X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, a=P, group=128, n_grid=20,
+             losses=P, best=P, sb=P, tab=None, ws=P, wsb=1 << 30, fl=P)
+    a.update(kw)
+    assert L.awq_search_gram(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["W"], a["wt"], a["N"], a["ldw"],
+                             a["a"], a["group"], a["n_grid"], a["losses"], a["best"], a["sb"], a["tab"],
+                             a["ws"], a["wsb"], a["fl"], None) == status
+
+
+def test_search_gram_workspace(L):
+    # the search workspace for 2K rows of the left operand plus the 2K x K bf16 stack of G
+    K, N = 4096, 4096
+    assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= \
+        L.awq_search_workspace_bytes(2 * K, K, N, 128, 20) + 2 * K * K * 2
+    assert L.awq_search_gram_workspace_bytes(16384, 4000, N, 128, 20) == 0
+    assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 65) == 0
 
 
 def pack(L, W=P, wt=BF16, N=128, K=256, ldw=256, s=P, group=128, q=P, sc=P, z=P, fl=P):

@@ -1,0 +1,108 @@
+"""GPU parity of the Gram-form search (awq_search_gram: "AWQ：为什么 4-bit 权重量化要先观察
+Activation", §1, the exact output error through X^T X) against the oracle's exact losses.
+
+Tolerance, from the arithmetic.  The kernel forms Y' = G~ E~^T with E~ = E rounded to bf16
+and G~ = G_hi + G_lo, then sums Y'[k', n] e[n, k'] with the unrounded e:
+  * bf16 E: sum_n e G (E~ - E)^T = sum_{m,n} y (X dE^T), at most 2^-8 sum |y| (|X| |E|^T): the
+    first-order term of the direct form with coefficient 1 instead of 2;
+  * G: 2^-16 relative per entry (G_lo's rounding) plus fp32 sums over 1024-token blocks and
+    across the M / 1024 blocks, each bounded by its count times 2^-24 of |X|^T |X|;
+  * fp32 accumulation over the K products of the matrix cores and the epilogue's 16-term sums.
+The last three are bounded by c sum_{m,n} (|X| |E|^T)^2.  Per candidate the test allows
+max(1e-3 relative, that bound).  The chosen candidate follows the single-weight rule."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import awq_oracle as o
+from post_weight_quantization_mean_amd import synth
+from tests.test_gpu_parity import DEV, banner, check_choice, loss_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_weight_quantization_mean_amd import awq as _awq
+    _awq.lib()
+    return _awq
+
+
+def gram_tolerance(X64, W32, s_table, ref_losses):
+    M, K = X64.shape
+    N = W32.shape[0]
+    cG = 2.0 ** -16 + (1024 + M / 1024 + 1 + K + 16) * 2.0 ** -24
+    absX = np.abs(X64)
+    tol = np.empty(len(s_table))
+    for i, s in enumerate(s_table):
+        q, z, d = o.quantize(W32, s, 128)
+        E = W32.astype(np.float64) - o.effective_weight(q, z, d, s, 128)
+        Y = X64 @ E.T
+        A = absX @ np.abs(E).T
+        bound = (2.0 ** -8 * np.sum(np.abs(Y) * A) + cG * np.sum(A * A)) / (M * N)
+        tol[i] = max(1e-3 * ref_losses[i], bound + 1e-5 * ref_losses[i])
+    return tol
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (2000, 256, 200),   # M > 2K: the case the Gram form is for; N ragged (two tiles)
+    (700, 384, 130),    # 2K = 768 rows of [G_hi; G_lo]: a 512-row tile holds rows of both
+    (64, 128, 1),       # degenerate: one group, one output
+    (4096, 512, 256),
+])
+def test_gram_search_vs_oracle(awq, M, K, N):
+    banner(f"search gram M={M} K={K} N={N}")
+    _, X, W = synth.custom_layer(M, K, N, dtype="bf16", seed=21)
+    X64, W32 = synth.to_f64(X), synth.to_f32(W)
+    a32 = o.activation_stat(X64).astype(np.float32)
+    ref = o.search(X64, W32, a32)
+    res = awq.search(X.to(DEV), W.to(DEV), torch.from_numpy(a32).to(DEV), return_table=True, gram=True)
+    assert np.array_equal(res.s_table.cpu().numpy().view(np.int32), ref["s_table"].view(np.int32))
+    L = res.losses.cpu().numpy()
+    tol = gram_tolerance(X64, W32, ref["s_table"], ref["losses"])
+    err = np.abs(L - ref["losses"])
+    bad = np.nonzero(err > tol)[0]
+    assert bad.size == 0, f"gram loss error {err[bad] / ref['losses'][bad]} (rel) above tolerance at {bad}"
+    check_choice(res.best_index, ref["losses"], ref["best"], tol)
+    assert np.array_equal(res.s_best.cpu().numpy(), ref["s_table"][res.best_index])
+    print(f"[gpu-case] gram max rel err {np.max(err / ref['losses']):.2e}", flush=True)
+
+
+def test_gram_and_direct_agree(awq):
+    """Both forms on the GPU, a block-shaped layer (M = 4 K): each is within its own tolerance
+    of the oracle's exact losses, so they agree to the sum of the two tolerances, and their
+    first minima are the same candidate or candidates those tolerances cannot separate."""
+    banner("search gram vs direct")
+    M, K, N = 2048, 512, 384
+    _, X, W = synth.custom_layer(M, K, N, dtype="bf16", seed=22)
+    X64, W32 = synth.to_f64(X), synth.to_f32(W)
+    a32 = o.activation_stat(X64).astype(np.float32)
+    ref = o.search(X64, W32, a32)
+    Xd, Wd, a = X.to(DEV), W.to(DEV), torch.from_numpy(a32).to(DEV)
+    rd = awq.search(Xd, Wd, a)
+    rg = awq.search(Xd, Wd, a, gram=True)
+    Ld, Lg = rd.losses.cpu().numpy(), rg.losses.cpu().numpy()
+    tol = loss_tolerance(X64, W32, ref["s_table"], ref["losses"], False) + \
+        gram_tolerance(X64, W32, ref["s_table"], ref["losses"])
+    assert np.all(np.abs(Lg - Ld) <= tol)
+    if rg.best_index != rd.best_index:
+        assert abs(ref["losses"][rg.best_index] - ref["losses"][rd.best_index]) <= \
+            tol[rg.best_index] + tol[rd.best_index]
+
+
+def test_gram_is_deterministic(awq):
+    _, X, W = synth.custom_layer(1500, 256, 300, dtype="bf16", seed=23)
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    a = awq.stats(Xd)
+    r1 = awq.search(Xd, Wd, a, gram=True)
+    r2 = awq.search(Xd, Wd, a, gram=True)
+    assert torch.equal(r1.losses, r2.losses) and torch.equal(r1.best, r2.best)
+
+
+def test_gram_rejects_fp32(awq):
+    X = torch.zeros((64, 128), device=DEV)
+    W = torch.zeros((128, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(Exception, match="unsupported"):
+        awq.search(X, W, torch.ones(128, device=DEV), gram=True)
