@@ -171,19 +171,27 @@ __global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(
   load_scales(s, g * kGroup + 32 * q, sc, bad);
 
   // the four slots this lane loads: unit j = 4 t + lane / 16 of the wave, piece lane % 16
-  int64_t soff[4], srow[4];
+  // W through a buffer resource of N ldw 2 bytes (< 2^31, host-checked): 32-bit byte offsets
+  // that advance by a scalar row step, and slots past the last row read zero in hardware, so
+  // the loads need neither a per-slot row test nor a branch (a guarded load compiles to a
+  // branch, after which the wait counts could no longer keep both iterations in flight).
+  // Slots of units that do not exist start at the end of W and stay past it.
+  const uint32_t wbytes = (uint32_t)(N * ldw * 2);
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)wbytes, 0x00020000);
+  uint32_t boff[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t uj = uw + 4 * t + (lane >> 4);
-    srow[t] = uj < U ? uj / G : N;  // spare units never load
-    soff[t] = (uj < U ? uj / G : 0) * ldw + (uj % G) * kGroup + 8 * (lane & 15);
+    boff[t] = uj < U ? (uint32_t)(((uj / G) * ldw + (uj % G) * kGroup + 8 * (lane & 15)) * 2) : wbytes;
   }
+  const uint32_t rowb = (uint32_t)(ldw * 2);
   auto phys = [](int slot) { return slot ^ ((slot >> 4) & 15); };
-  auto issue = [&](u32x4* raw, int64_t kk) {  // loads of iteration kk (rows + kk)
+  auto issue = [&](u32x4* raw, int64_t kk) {  // loads of iteration kk (rows + kk), non-temporal
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      raw[t] = srow[t] + kk < N ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + soff[t] + kk * ldw))
-                                : u32x4{0u, 0u, 0u, 0u};
+      raw[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wrsrc, (int)(boff[t] + (uint32_t)kk * rowb), 0, 2));
   };
   auto process = [&](u32x4* raw, int64_t kk) {
     // slot order -> unit order through LDS (a wave's LDS operations complete in issue order)
@@ -214,10 +222,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_bf16_kernel(
   const int64_t wrow = uw / G;
   u32x4 ra[4], rb[4];
   issue(ra, 0);
+  __builtin_amdgcn_sched_barrier(0);  // ra's loads strictly before rb's, as in the loop
   issue(rb, R);
   for (int64_t kk = 0; wrow + kk < N; kk += 2 * R) {
     process(ra, kk);
-    if (wrow + kk + R < N) process(rb, kk + R);
+    process(rb, kk + R);  // unconditional (its units past N encode nothing): a branch here would
+                          // leave the wait counts at the loop head unable to keep rb in flight
   }
   if (bad) atomicOr(flags, bad);
 }
@@ -274,10 +284,26 @@ hipError_t launch_pack(const void* W, bool wf32, int64_t N, int64_t K, int64_t l
     pack_f32_kernel<true><<<blocks, kPackThreads, 0, st>>>(Wf, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
   else if (wf32)
     pack_f32_kernel<false><<<blocks, kPackThreads, 0, st>>>(Wf, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
-  else if (clip)
-    pack_bf16_kernel<true><<<blocks, kPackThreads, 0, st>>>(Wh, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
-  else
-    pack_bf16_kernel<false><<<blocks, kPackThreads, 0, st>>>(Wh, N, K, ldw, s, clip, R, qweight, scales, zeros, flags);
+  else {
+    // the bf16 kernel addresses W with 32-bit offsets: row slabs of at most 2^30 bytes, so that
+    // offsets two iterations past a slab's end stay below 2^31
+    int64_t slab = ((int64_t)1 << 30) / (ldw * 2);
+    if (slab < 1) slab = 1;
+    for (int64_t r0 = 0; r0 < N; r0 += slab) {
+      const int64_t n = N - r0 < slab ? N - r0 : slab;
+      const int64_t Rs = R < n ? R : n;
+      const unsigned bs = (unsigned)((Rs * G + kPackUnits - 1) / kPackUnits);
+      const float* cs = clip ? clip + r0 * G : nullptr;
+      if (clip)
+        pack_bf16_kernel<true><<<bs, kPackThreads, 0, st>>>(Wh + r0 * ldw, n, K, ldw, s, cs, Rs, qweight + r0 * (K / 8),
+                                                            scales + r0 * G, zeros + r0 * G, flags);
+      else
+        pack_bf16_kernel<false><<<bs, kPackThreads, 0, st>>>(Wh + r0 * ldw, n, K, ldw, s, cs, Rs, qweight + r0 * (K / 8),
+                                                             scales + r0 * G, zeros + r0 * G, flags);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   return hipGetLastError();
 }
 

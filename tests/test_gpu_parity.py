@@ -253,6 +253,27 @@ def test_pack_bf16_many_rows_strided(awq):
     assert np.array_equal(zz.cpu().numpy(), art["zeros"])
 
 
+def test_pack_bf16_row_slabs(awq):
+    """A bf16 W of more than 2^30 bytes (131073 rows of 4096): the pack runs in row slabs of
+    2^30 bytes (32-bit offsets inside each), here one full slab and a one-row slab.  Rows on
+    both sides of the slab boundary, the first and the last, bit-exact against the oracle
+    (the pack is row-independent)."""
+    banner("pack bf16 row slabs N=131073 K=4096")
+    N, K = 131073, 4096
+    g = torch.Generator(device=DEV).manual_seed(22)
+    Wd = (torch.randn((N, K), generator=g, device=DEV) / 64).to(torch.bfloat16)
+    s = (torch.rand(K, generator=torch.Generator().manual_seed(23)) + 0.5).to(torch.float32)
+    qw, sc, zz = awq.pack(Wd, s.to(DEV))
+    rows = [0, 1, 65536, 131070, 131071, 131072]
+    Ws = synth.to_f32(Wd[rows].cpu())
+    art = o.pack(Ws, s.numpy())
+    assert np.array_equal(qw[rows].cpu().numpy(), art["qweight"])
+    assert np.array_equal(sc[rows].cpu().numpy(), art["scales"])
+    assert np.array_equal(zz[rows].cpu().numpy(), art["zeros"])
+    del Wd, qw, sc, zz
+    torch.cuda.empty_cache()
+
+
 def test_pack_hand_vectors(awq):
     # groups built from the oracle's hand-derived fp32 vectors, padded to 128 with copies of
     # their own values (min, max and so Delta, z unchanged)
