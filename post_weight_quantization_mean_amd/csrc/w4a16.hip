@@ -16,6 +16,8 @@
 //   * prefill, M > 8: the bf16 matrix cores.  A 128-row tile of W_hat is decoded per 32-channel
 //     chunk into LDS as bf16 (Delta (q - z) rounded once to bf16), X' is staged as bf16, and
 //     each of four waves accumulates 128 tokens x 128 outputs in fp32.
+#include <type_traits>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -402,67 +404,96 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
 }
 
 // ---- prefill -------------------------------------------------------------------------------
-constexpr int PBM = 512, PBN = 128, PKC = 32, PPITCH = PKC + 8;
+// Each wave multiplies its own 128 tokens of the 512-token tile, so X never needs sharing: the
+// wave copies its rows of every 32-channel chunk from global memory straight into LDS (buffer
+// load with LDS destination, 1 KiB per instruction), three chunks deep, and nothing of X passes
+// through registers or waits for a barrier.  The decoded weight tile is shared by the four
+// waves: its codes are loaded two chunks ahead, decoded after the chunk's matrix instructions
+// and stored for the next chunk, which one barrier per chunk publishes.  The three X stages and
+// the three W stages are distinct LDS objects with a fixed role in each of three unrolled steps,
+// so the compiler's wait counts for the copies stay exact.  LDS rows are 64 bytes, unpadded,
+// their four 16-byte slots permuted by (row >> 2) & 3 (conflict-free 32-row fragment reads).
+#define AWQ_LDS __attribute__((address_space(3)))
+constexpr int PBM = 512, PBN = 128, PKC = 32;
+constexpr int XSTAGE = PBM * PKC * 2;  // 32 KiB
+constexpr int WSTAGE = PBN * PKC * 2;  // 8 KiB
 
 __device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
   const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
   return __builtin_bit_cast(uint32_t, h);
 }
+__device__ __forceinline__ int pslot(int row, int s) { return (s ^ ((row >> 2) & 3)) * 16; }  // bytes
+
+struct WRegs {
+  uint2 qv;  // two words: the row's 16 codes of this chunk for this thread
+};
 
 __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
     float* __restrict__ Y, int64_t ldy, int64_t ntiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][PBM][PPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][PBN][PPITCH];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs0[XSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs1[XSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs2[XSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ws0[WSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ws1[WSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ws2[WSTAGE];
   const int64_t G = K / kGroup, words = K / 8;
   const int64_t mt = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
   const int64_t m0 = mt * PBM, n0 = nt * PBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // X chunk: 512 rows x 64 bytes, thread: rows tid / 4 + 64 i, piece tid % 4 (16 bytes)
-  const int xkp = tid & 3, xr0 = tid >> 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // X rows of this tile through a buffer resource: rows past M read as zero (host: 512 rows of
+  // X span less than 2^31 bytes)
   const int64_t xbytes = (M - m0) * ldx * 2;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
+  // copy instruction i (0..7) of this wave fills its rows 16 i + lane / 4 with 16 bytes each:
+  // physical slot lane % 4 receives logical slot (lane % 4) ^ swizzle(row)
+  uint32_t xoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = wave * 128 + 16 * i + (lane >> 2);
+    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
+  }
+  auto dma_x = [&](uint8_t* stage, int64_t c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(stage + (wave * 128 + 16 * i) * 64), 16,
+                                               (int)xoff[i], (int)(c * PKC * 2), 0, 0);
+  };
   // W chunk: 128 rows x 4 words (32 channels); thread: row tid / 2, words 2 (tid % 2) .. + 1
   const int wr = tid >> 1, wq = tid & 1;
   const int64_t wn = n0 + wr;
   const bool wlive = wn < N;
   const int32_t* wrow = qweight + (wlive ? wn : 0) * words;
-  // one chunk's global data in registers; two sets alternate, so that the loads of chunk c + 2
-  // are in flight during the whole of step c (one step is shorter than a load's latency)
-  struct Regs {
-    uint4 xv[8];
-    uint2 qv;
-    uint16_t dh, zh;  // fp16 bits, converted at the store so no load result is needed early
+  const int64_t nch = K / PKC;  // a multiple of 4: a group is four chunks
+  auto load_codes = [&](WRegs& R, int64_t c) {
+    const int64_t cc = c < nch ? c : nch - 1;  // past the end: an in-bounds reload, never stored
+    R.qv = *reinterpret_cast<const uint2*>(wrow + cc * (PKC / 8) + 2 * wq);
   };
-  auto load = [&](Regs& R, int64_t c) {
-    const uint32_t kb = (uint32_t)(c * PKC);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      R.xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xrsrc, (int)((xr0 + 64 * i) * ldx * 2 + kb * 2 + xkp * 16), 0, 0));
-    R.qv = *reinterpret_cast<const uint2*>(wrow + kb / 8 + 2 * wq);
-    const int64_t g = kb / kGroup;
-    R.dh = scales[(wlive ? wn : 0) * G + g];  // unconditional: a branch here would drain the loads
-    R.zh = zeros[(wlive ? wn : 0) * G + g];
+  // The row's fp16 scale and zero are loaded once per group, with the group's first chunk, into
+  // register pair g mod 3; they stay fp16 bits until the decode, which comes two chunks later.
+  uint32_t sd[3] = {0, 0, 0}, sz[3] = {0, 0, 0};
+  auto load_group = [&](uint32_t& d, uint32_t& z, int64_t c) {
+    const int64_t g = (c < nch ? c : nch - 1) / 4;
+    d = scales[(wlive ? wn : 0) * G + g];
+    z = zeros[(wlive ? wn : 0) * G + g];
   };
-  auto store = [&](const Regs& R, int b) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&xs[b][xr0 + 64 * i][xkp * 8]) = R.xv[i];
+  auto store_w = [&](const WRegs& R, uint32_t dh, uint32_t zh, uint8_t* stage) {
     uint32_t pk[8];
     const uint32_t wv[2] = {R.qv.x, R.qv.y};
-    const float dv = wlive ? h2f(R.dh) : 0.0f, zv = h2f(R.zh);  // rows past N: weight 0
+    const float dv = wlive ? h2f((uint16_t)dh) : 0.0f, zv = h2f((uint16_t)zh);  // rows past N: weight 0
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float a = dv * ((float)((wv[j] >> (8 * c)) & 15u) - zv);      // exact in fp32
+        const float a = dv * ((float)((wv[j] >> (8 * c)) & 15u) - zv);  // exact in fp32
         const float bq = dv * ((float)((wv[j] >> (8 * c + 4)) & 15u) - zv);
         pk[4 * j + c] = bf16x2_of(a, bq);
       }
-    *reinterpret_cast<uint4*>(&ws[b][wr][wq * 16]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    *reinterpret_cast<uint4*>(&ws[b][wr][wq * 16 + 8]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    *reinterpret_cast<uint4*>(stage + wr * 64 + pslot(wr, 2 * wq)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(stage + wr * 64 + pslot(wr, 2 * wq + 1)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
   };
   f32x16 acc[4][4];
 #pragma unroll
@@ -471,16 +502,21 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  const int64_t nch = K / PKC;  // >= 4 (K is a multiple of 128)
-  auto compute = [&](int b) {
+  const int frow = lane & 31, fs = lane >> 5;
+  auto compute = [&](const uint8_t* xst, const uint8_t* wst) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 af[4], bfr[4];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) bfr[cc] = *reinterpret_cast<const bf16x8*>(&ws[b][cc * 32 + frow][h * 16 + fk]);
+      for (int cc = 0; cc < 4; ++cc) {
+        const int row = cc * 32 + frow;
+        bfr[cc] = *reinterpret_cast<const bf16x8*>(wst + row * 64 + pslot(row, 2 * h + fs));
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) af[r] = *reinterpret_cast<const bf16x8*>(&xs[b][wave * 128 + r * 32 + frow][h * 16 + fk]);
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 128 + r * 32 + frow;
+        af[r] = *reinterpret_cast<const bf16x8*>(xst + row * 64 + pslot(row, 2 * h + fs));
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -488,24 +524,73 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
           acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[r], bfr[cc], acc[r][cc], 0, 0, 0);
     }
   };
-  // step c: LDS buffer c & 1 holds chunk c; `nx` holds chunk c + 1 (landed or in flight) and
-  // `fa` chunk c + 2 (in flight).  After the products, chunk c + 1 goes to the other buffer
-  // (whose readers finished before the previous barrier), and `nx` is reloaded with c + 3.
-  auto step = [&](int64_t c, Regs& nx) {
-    compute((int)(c & 1));
-    if (c + 1 < nch) store(nx, (int)((c + 1) & 1));
-    __syncthreads();
-    load(nx, c + 3 < nch ? c + 3 : nch - 1);  // past the end: a harmless in-bounds reload
+  // stage i as the shared object itself (not through a pointer table), so that the compiler
+  // knows which copy writes which stage and its wait counts stay exact
+  auto xst = [&](auto I) -> uint8_t* {
+    constexpr int i = decltype(I)::value % 3;
+    if constexpr (i == 0) return xs0; else if constexpr (i == 1) return xs1; else return xs2;
   };
-  Regs ra, rb;
-  load(ra, 0);
-  load(rb, 1);
-  store(ra, 0);
+  auto wst = [&](auto I) -> uint8_t* {
+    constexpr int i = decltype(I)::value % 3;
+    if constexpr (i == 0) return ws0; else if constexpr (i == 1) return ws1; else return ws2;
+  };
+  // The barrier that publishes a W stage: this wave's LDS stores done (lgkmcnt 0), then
+  // s_barrier.  No workgroup fence: a fence would also wait for every X copy still in flight
+  // (they write LDS), though only the issuing wave reads those rows and its reads wait for
+  // their own copies.  The signal fences keep the compiler from moving LDS accesses across.
+  auto publish_w = [] {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63, expcnt 7 (no wait), lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  WRegs rg[3];  // W codes of chunk c in set c % 3
+  // Step c, with S = c mod 12 known at compile time (so that every stage, register set and
+  // group pair is fixed and the step has no branch, which would cost the exact wait counts):
+  // copy X chunk c + 2 into the X stage read two steps ago (past the end: a harmless re-copy
+  // into a stage no later step reads), load W chunk c + 2's codes (and, at a group's first chunk,
+  // its scale and zero), multiply chunk c, decode and store W chunk c + 1 into the W stage read
+  // two steps ago, then the barrier that publishes it.
+  auto step = [&](int64_t c, auto Sc) {
+    constexpr int S = decltype(Sc)::value;
+    dma_x(xst(std::integral_constant<int, S + 2>{}), c + 2 < nch ? c + 2 : nch - 1);
+    load_codes(rg[(S + 2) % 3], c + 2);
+    if constexpr ((S + 2) % 4 == 0) load_group(sd[((S + 2) / 4) % 3], sz[((S + 2) / 4) % 3], c + 2);
+    __builtin_amdgcn_sched_barrier(0);  // the copies and loads ahead of the products they hide behind
+    compute(xst(std::integral_constant<int, S>{}), wst(std::integral_constant<int, S>{}));
+    store_w(rg[(S + 1) % 3], sd[((S + 1) / 4) % 3], sz[((S + 1) / 4) % 3], wst(std::integral_constant<int, S + 1>{}));
+    publish_w();
+  };
+  dma_x(xs0, 0);
+  dma_x(xs1, 1);
+  load_codes(rg[0], 0);
+  load_codes(rg[1], 1);
+  load_group(sd[0], sz[0], 0);
+  store_w(rg[0], sd[0], sz[0], ws0);
   __syncthreads();
-  load(ra, 2);
-  for (int64_t c = 0; c < nch; c += 2) {  // nch is even
-    step(c, rb);
-    step(c + 1, ra);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+  using I8 = std::integral_constant<int, 8>;
+  using I9 = std::integral_constant<int, 9>;
+  using I10 = std::integral_constant<int, 10>;
+  using I11 = std::integral_constant<int, 11>;
+  int64_t c = 0;
+  for (; c + 12 <= nch; c += 12) {
+    step(c, I0{}); step(c + 1, I1{}); step(c + 2, I2{}); step(c + 3, I3{});
+    step(c + 4, I4{}); step(c + 5, I5{}); step(c + 6, I6{}); step(c + 7, I7{});
+    step(c + 8, I8{}); step(c + 9, I9{}); step(c + 10, I10{}); step(c + 11, I11{});
+  }
+  if (c < nch) {  // 4 or 8 chunks remain (nch is a multiple of 4)
+    step(c, I0{}); step(c + 1, I1{}); step(c + 2, I2{}); step(c + 3, I3{});
+    if (c + 4 < nch) {
+      step(c + 4, I4{}); step(c + 5, I5{}); step(c + 6, I6{}); step(c + 7, I7{});
+    }
   }
   // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
