@@ -412,7 +412,8 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
 // and stored for the next chunk, which one barrier per chunk publishes.  The three X stages and
 // the three W stages are distinct LDS objects with a fixed role in each of three unrolled steps,
 // so the compiler's wait counts for the copies stay exact.  LDS rows are 64 bytes, unpadded,
-// their four 16-byte slots permuted by (row >> 2) & 3 (conflict-free 32-row fragment reads).
+// their four 16-byte slots permuted per row (X by (row >> 2) & 3, W by wslot below) so that
+// neither the fragment reads nor the stores meet a bank conflict.
 #define AWQ_LDS __attribute__((address_space(3)))
 constexpr int PBM = 512, PBN = 128, PKC = 32;
 constexpr int XSTAGE = PBM * PKC * 2;  // 32 KiB
@@ -423,6 +424,14 @@ __device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 __device__ __forceinline__ int pslot(int row, int s) { return (s ^ ((row >> 2) & 3)) * 16; }  // bytes
+// W stage slots: f(row) = ((row >> 1) & 3) ^ 3 ((row >> 3) & 1).  LDS serves a 16-byte read for
+// 16 lanes at a time over 64 four-byte banks and a 16-byte write for 8 lanes at a time over 32
+// banks (measured with the bank-conflict counter); under this f both the 32-row fragment reads
+// (16 consecutive rows, one slot) and the decode's stores (8 lanes: 4 rows x 2 slots) are
+// conflict-free, where (row >> 2) & 3 doubled the stores' time.
+__device__ __forceinline__ int wslot(int row, int s) {
+  return (s ^ ((row >> 1) & 3) ^ (((row >> 3) & 1) * 3)) * 16;
+}
 
 struct WRegs {
   uint2 qv;  // two words: the row's 16 codes of this chunk for this thread
@@ -492,8 +501,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
         const float bq = dv * ((float)((wv[j] >> (8 * c + 4)) & 15u) - zv);
         pk[4 * j + c] = bf16x2_of(a, bq);
       }
-    *reinterpret_cast<uint4*>(stage + wr * 64 + pslot(wr, 2 * wq)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    *reinterpret_cast<uint4*>(stage + wr * 64 + pslot(wr, 2 * wq + 1)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    *reinterpret_cast<uint4*>(stage + wr * 64 + wslot(wr, 2 * wq)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(stage + wr * 64 + wslot(wr, 2 * wq + 1)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
   };
   f32x16 acc[4][4];
 #pragma unroll
@@ -510,7 +519,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const int row = cc * 32 + frow;
-        bfr[cc] = *reinterpret_cast<const bf16x8*>(wst + row * 64 + pslot(row, 2 * h + fs));
+        bfr[cc] = *reinterpret_cast<const bf16x8*>(wst + row * 64 + wslot(row, 2 * h + fs));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
