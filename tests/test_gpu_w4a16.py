@@ -44,7 +44,11 @@ def run(awq, art, X, prefill, biased=None):
     sc = torch.from_numpy(art["scales"].view(np.float16)).to(DEV)
     zz = torch.from_numpy(art["zeros"].view(np.float16)).to(DEV)
     Y = awq.w4a16(X.to(DEV), q, sc, zz).cpu().numpy().astype(np.float64)
-    X64 = X.float().numpy().astype(np.float64)
+    return check(Y, X.float().numpy().astype(np.float64), art, prefill, biased)
+
+
+def check(Y, X64, art, prefill, biased):
+    """Y [m, n] against the oracle's exact product of X64 [m, K] and the artefact's n rows."""
     ref = o.w4a16_matmul(X64, art["qweight"], art["scales"], art["zeros"])
     Wh = o.dequant_artefact(art["qweight"], art["scales"], art["zeros"])
     K = X64.shape[1]
@@ -58,7 +62,7 @@ def run(awq, art, X, prefill, biased=None):
     err = np.abs(Y - ref)
     bad = np.argwhere(err > tol + 1e-30)
     assert bad.size == 0, f"{len(bad)} outputs outside tolerance, first {bad[:4].tolist()}"
-    return float(np.max(err / np.maximum(np.abs(ref), 1e-30)))
+    return float(np.max(err / (tol + 1e-30)))  # the largest error as a fraction of its tolerance
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 256), (3, 14336, 130), (8, 384, 64), (2, 5120, 4)])
@@ -76,7 +80,10 @@ def test_decode_fp32_many_tokens(awq):
     run(awq, art, X, prefill=False)
 
 
-@pytest.mark.parametrize("M,K,N", [(9, 512, 128), (600, 4096, 200), (1024, 1024, 384)])
+# K / 32 chunks: 16 (one unrolled run of 12, tail 4), 128 (tail 8), 32 (tail 8), 4 (tail only),
+# 12 and 48 (no tail), 64 (tail 4); M and N ragged against the 512 x 128 tile
+@pytest.mark.parametrize("M,K,N", [(9, 512, 128), (600, 4096, 200), (1024, 1024, 384), (520, 128, 130),
+                                   (513, 384, 64), (700, 1536, 256), (40, 2048, 129)])
 def test_prefill_bf16(awq, M, K, N):
     banner(f"w4a16 prefill M={M} K={K} N={N}")
     art = artefact(N, K, 5)
@@ -114,3 +121,28 @@ def test_scaled_inputs_recover_the_layer(awq):
     dW = sc.cpu().double().repeat_interleave(128, dim=1) * (0.5 + 16 * 2.0 ** -11) / s.double()[None, :]
     bound = X.double().abs() @ dW.T + 1e-4 * (X.double().abs() @ W.double().abs().T)
     assert torch.all((Y - exact).abs() <= bound)
+
+
+def test_prefill_full_size_sampled(awq):
+    """The prefill in the shape the benchmark times: 4096 bf16 tokens against a 28672 x 4096
+    artefact (synthetic: uniformly random code words, positive fp16 scales, integer zeros), all
+    outputs computed on the GPU, a 24 x 96 sample of them (tokens and outputs from every tile
+    row and column, the last of each included) checked against the oracle."""
+    banner("w4a16 prefill full size 4096 x 28672 x 4096, sampled")
+    M, K, N = 4096, 4096, 28672
+    rng = np.random.default_rng(10)
+    art = {"qweight": rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint32).view(np.int32),
+           "scales": (np.abs(rng.standard_normal((N, K // 128))) * 0.01 + 1e-3).astype(np.float16),
+           "zeros": rng.integers(0, 16, size=(N, K // 128)).astype(np.float16)}
+    X = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    sc = torch.from_numpy(art["scales"]).to(DEV)
+    zz = torch.from_numpy(art["zeros"]).to(DEV)
+    Y = awq.w4a16(X.to(DEV), q, sc, zz)
+    rows = np.unique(np.concatenate([rng.choice(M, 23, replace=False), [M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, 95, replace=False), [N - 1]]))
+    Ys = Y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu().numpy().astype(np.float64)
+    sub = {k: v[cols] for k, v in art.items()}
+    X64 = X.float().numpy().astype(np.float64)[rows]
+    frac = check(Ys, X64, sub, prefill=True, biased=False)
+    print(f"[gpu-case] full-size prefill sample: largest error {frac:.3f} of its tolerance", flush=True)
