@@ -404,16 +404,19 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
 }
 
 // ---- prefill -------------------------------------------------------------------------------
-// Each wave multiplies its own 128 tokens of the 512-token tile, so X never needs sharing: the
-// wave copies its rows of every 32-channel chunk from global memory straight into LDS (buffer
-// load with LDS destination, 1 KiB per instruction), three chunks deep, and nothing of X passes
-// through registers or waits for a barrier.  The decoded weight tile is shared by the four
-// waves: its codes are loaded two chunks ahead, decoded after the chunk's matrix instructions
-// and stored for the next chunk, which one barrier per chunk publishes.  The three X stages and
-// the three W stages are distinct LDS objects with a fixed role in each of three unrolled steps,
-// so the compiler's wait counts for the copies stay exact.  LDS rows are 64 bytes, unpadded,
-// their four 16-byte slots permuted per row (X by (row >> 2) & 3, W by wslot below) so that
-// neither the fragment reads nor the stores meet a bank conflict.
+// A block of 8 waves (two per SIMD, at most 256 registers each) computes a 512-token x
+// 128-output tile.  Each wave multiplies its own 64 tokens, so X never needs sharing: the wave
+// copies its rows of every 32-channel chunk from global memory straight into LDS (buffer load
+// with LDS destination, 1 KiB per instruction), three chunks deep, and nothing of X passes
+// through registers or waits for a barrier.  The decoded weight tile is shared by all waves:
+// its codes are loaded two chunks ahead, decoded after the chunk's matrix instructions and
+// stored for the next chunk, which one barrier per chunk publishes.  The three X stages and
+// the three W stages are distinct LDS objects with a fixed role in each step of the unrolled
+// loop, so the compiler's wait counts for the copies stay exact.  LDS rows are 64 bytes,
+// unpadded, their four 16-byte slots permuted per row (X by (row >> 2) & 3, W by wslot below)
+// so that neither the fragment reads nor the stores meet a bank conflict.  (A 4-wave block,
+// 128 tokens a wave at 512 registers, is the other instance of the template; it measured the
+// same at 4096 tokens and slower at 512 and 16384.)
 #define AWQ_LDS __attribute__((address_space(3)))
 constexpr int PBM = 512, PBN = 128, PKC = 32;
 constexpr int XSTAGE = PBM * PKC * 2;  // 32 KiB
@@ -433,14 +436,18 @@ __device__ __forceinline__ int wslot(int row, int s) {
   return (s ^ ((row >> 1) & 3) ^ (((row >> 3) & 1) * 3)) * 16;
 }
 
+// NW waves per block: wave w multiplies tokens RW w .. RW w + RW - 1 of the tile (RW = 512 / NW);
+// a W row's four words of a chunk are decoded by TPR = NW / 2 threads, WPT = 4 / TPR words each.
+template <int NW>
 struct WRegs {
-  uint2 qv;  // two words: the row's 16 codes of this chunk for this thread
+  uint32_t qv[8 / NW];  // this thread's words of its row: 8 codes each
 };
 
-__global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void w4a16_gemm_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
-    float* __restrict__ Y, int64_t ldy, int64_t ntiles) {
+    float* __restrict__ Y, int64_t ldy, int64_t ntiles, int64_t tiles, int64_t per_xcd) {
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs1[XSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t xs2[XSTAGE];
@@ -448,7 +455,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t ws1[WSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t ws2[WSTAGE];
   const int64_t G = K / kGroup, words = K / 8;
-  const int64_t mt = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
+  // Blocks go to the 8 XCDs round robin (block b to XCD b % 8); XCD x takes the tiles
+  // x per_xcd .. (x + 1) per_xcd - 1 in order, so its blocks share token tiles and the tile's X
+  // stays in that XCD's L2.  Blocks past the last tile (grid rounded up to 8) return at once.
+  const int64_t L = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (L >= tiles) return;
+  const int64_t mt = L / ntiles, nt = L % ntiles;
   const int64_t m0 = mt * PBM, n0 = nt * PBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -457,29 +469,36 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
   const int64_t xbytes = (M - m0) * ldx * 2;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
-  // copy instruction i (0..7) of this wave fills its rows 16 i + lane / 4 with 16 bytes each:
-  // physical slot lane % 4 receives logical slot (lane % 4) ^ swizzle(row)
-  uint32_t xoff[8];
+  constexpr int RW = PBM / NW, RT = RW / 32, NDMA = RW / 16, TPR = NW / 2, WPT = 4 / TPR;
+  // copy instruction i (0 .. NDMA - 1) of this wave fills its rows 16 i + lane / 4 with 16 bytes
+  // each: physical slot lane % 4 receives logical slot (lane % 4) ^ swizzle(row)
+  uint32_t xoff[NDMA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = wave * 128 + 16 * i + (lane >> 2);
+  for (int i = 0; i < NDMA; ++i) {
+    const int row = wave * RW + 16 * i + (lane >> 2);
     xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
   }
   auto dma_x = [&](uint8_t* stage, int64_t c) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(stage + (wave * 128 + 16 * i) * 64), 16,
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(stage + (wave * RW + 16 * i) * 64), 16,
                                                (int)xoff[i], (int)(c * PKC * 2), 0, 0);
   };
-  // W chunk: 128 rows x 4 words (32 channels); thread: row tid / 2, words 2 (tid % 2) .. + 1
-  const int wr = tid >> 1, wq = tid & 1;
+  // W chunk: 128 rows x 4 words (32 channels); thread: row tid / TPR, words WPT (tid % TPR) ..
+  const int wr = tid / TPR, wq = tid % TPR;
   const int64_t wn = n0 + wr;
   const bool wlive = wn < N;
   const int32_t* wrow = qweight + (wlive ? wn : 0) * words;
   const int64_t nch = K / PKC;  // a multiple of 4: a group is four chunks
-  auto load_codes = [&](WRegs& R, int64_t c) {
+  auto load_codes = [&](WRegs<NW>& R, int64_t c) {
     const int64_t cc = c < nch ? c : nch - 1;  // past the end: an in-bounds reload, never stored
-    R.qv = *reinterpret_cast<const uint2*>(wrow + cc * (PKC / 8) + 2 * wq);
+    if constexpr (WPT == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(wrow + cc * (PKC / 8) + 2 * wq);
+      R.qv[0] = v.x;
+      R.qv[1] = v.y;
+    } else {
+      R.qv[0] = wrow[cc * (PKC / 8) + wq];
+    }
   };
   // The row's fp16 scale and zero are loaded once per group, with the group's first chunk, into
   // register pair g mod 3; they stay fp16 bits until the decode, which comes two chunks later.
@@ -489,24 +508,23 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
     d = scales[(wlive ? wn : 0) * G + g];
     z = zeros[(wlive ? wn : 0) * G + g];
   };
-  auto store_w = [&](const WRegs& R, uint32_t dh, uint32_t zh, uint8_t* stage) {
-    uint32_t pk[8];
-    const uint32_t wv[2] = {R.qv.x, R.qv.y};
+  auto store_w = [&](const WRegs<NW>& R, uint32_t dh, uint32_t zh, uint8_t* stage) {
     const float dv = wlive ? h2f((uint16_t)dh) : 0.0f, zv = h2f((uint16_t)zh);  // rows past N: weight 0
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WPT; ++j) {
+      uint32_t pk[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float a = dv * ((float)((wv[j] >> (8 * c)) & 15u) - zv);  // exact in fp32
-        const float bq = dv * ((float)((wv[j] >> (8 * c + 4)) & 15u) - zv);
-        pk[4 * j + c] = bf16x2_of(a, bq);
+        const float a = dv * ((float)((R.qv[j] >> (8 * c)) & 15u) - zv);  // exact in fp32
+        const float bq = dv * ((float)((R.qv[j] >> (8 * c + 4)) & 15u) - zv);
+        pk[c] = bf16x2_of(a, bq);
       }
-    *reinterpret_cast<uint4*>(stage + wr * 64 + wslot(wr, 2 * wq)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    *reinterpret_cast<uint4*>(stage + wr * 64 + wslot(wr, 2 * wq + 1)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      *reinterpret_cast<uint4*>(stage + wr * 64 + wslot(wr, WPT * wq + j)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
   };
-  f32x16 acc[4][4];
+  f32x16 acc[RT][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -515,19 +533,19 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
   auto compute = [&](const uint8_t* xst, const uint8_t* wst) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      bf16x8 af[4], bfr[4];
+      bf16x8 af[RT], bfr[4];
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const int row = cc * 32 + frow;
         bfr[cc] = *reinterpret_cast<const bf16x8*>(wst + row * 64 + wslot(row, 2 * h + fs));
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wave * 128 + r * 32 + frow;
+      for (int r = 0; r < RT; ++r) {
+        const int row = wave * RW + r * 32 + frow;
         af[r] = *reinterpret_cast<const bf16x8*>(xst + row * 64 + pslot(row, 2 * h + fs));
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
           acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[r], bfr[cc], acc[r][cc], 0, 0, 0);
@@ -553,7 +571,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
-  WRegs rg[3];  // W codes of chunk c in set c % 3
+  WRegs<NW> rg[3];  // W codes of chunk c in set c % 3
   // Step c, with S = c mod 12 known at compile time (so that every stage, register set and
   // group pair is fixed and the step has no branch, which would cost the exact wait counts):
   // copy X chunk c + 2 into the X stage read two steps ago (past the end: a harmless re-copy
@@ -603,12 +621,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_kernel(
   }
   // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t m = m0 + wave * 128 + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+        const int64_t m = m0 + wave * RW + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
         const int64_t n = n0 + cc * 32 + (lane % 32);
         if (m < M && n < N) Y[m * ldy + n] = acc[r][cc][i];
       }
@@ -642,8 +660,10 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
                         hipStream_t st) {
   if (!xf32 && M > kW4a16GemvMax) {
     const int64_t mtiles = (M + PBM - 1) / PBM, ntiles = (N + PBN - 1) / PBN;
-    w4a16_gemm_kernel<<<(unsigned)(mtiles * ntiles), 256, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, K,
-                                                                   qweight, scales, zeros, N, Y, ldy, ntiles);
+    const int64_t tiles = mtiles * ntiles, per_xcd = (tiles + 7) / 8;
+    constexpr int kGemmWaves = 8;
+    w4a16_gemm_kernel<kGemmWaves><<<(unsigned)(8 * per_xcd), 64 * kGemmWaves, 0, st>>>(
+        static_cast<const uint16_t*>(X), M, ldx, K, qweight, scales, zeros, N, Y, ldy, ntiles, tiles, per_xcd);
     return hipGetLastError();
   }
   // decode path, up to 8 tokens per launch (fp32 X always takes it)
