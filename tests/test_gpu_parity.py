@@ -317,6 +317,49 @@ def test_pack_near_tie_quotients(awq):
 
 
 # ------------------------------------------------------------------------------ data errors
+def test_pack_bf16_group_categories(awq):
+    """bf16 groups of every kind the quantizer distinguishes, with random per-channel scales:
+    ranges containing 0 (z from the rounding alone), groups of one sign far from 0 (z clamped to
+    0 or 15, codes clamped), groups that touch 0 (min or max exactly 0), constant groups (the
+    1e-5 range floor) and narrow ones; codes, scales and zeros bit-exact against the oracle."""
+    rng = np.random.default_rng(12)
+    N, K = 512, 512
+    W = np.empty((N, K), np.float32)
+    kinds = ("mixed", "positive", "negative", "touch_lo", "touch_hi", "constant", "narrow")
+    for n in range(N):
+        for g in range(K // 128):
+            kind = kinds[rng.integers(len(kinds))]
+            sl = slice(128 * g, 128 * g + 128)
+            if kind == "mixed":
+                W[n, sl] = rng.uniform(-rng.uniform(0.01, 2), rng.uniform(0.01, 2), 128)
+            elif kind == "positive":
+                lo = rng.uniform(0.05, 1.0)
+                W[n, sl] = rng.uniform(lo, lo * rng.uniform(1.01, 8.0), 128)
+            elif kind == "negative":
+                hi = -rng.uniform(0.05, 1.0)
+                W[n, sl] = rng.uniform(hi * rng.uniform(1.01, 8.0), hi, 128)
+            elif kind == "touch_lo":
+                W[n, sl] = rng.uniform(0, 1, 128)
+                W[n, 128 * g + rng.integers(128)] = 0.0
+            elif kind == "touch_hi":
+                W[n, sl] = rng.uniform(-1, 0, 128)
+                W[n, 128 * g + rng.integers(128)] = 0.0
+            elif kind == "constant":
+                W[n, sl] = rng.uniform(-1, 1)
+            else:
+                c = rng.uniform(-1, 1)
+                W[n, sl] = c + rng.uniform(-1e-3, 1e-3, 128)
+    Wb = torch.from_numpy(W).to(torch.bfloat16)
+    s = np.exp(0.5 * rng.standard_normal(K)).astype(np.float32)
+    qw, sc, zz = awq.pack(Wb.to(DEV), torch.from_numpy(s).to(DEV))
+    art = o.pack(synth.to_f32(Wb), s)
+    assert np.array_equal(qw.cpu().numpy(), art["qweight"])
+    assert np.array_equal(zz.cpu().numpy(), art["zeros"])
+    assert np.array_equal(sc.cpu().numpy(), art["scales"])
+    zeros = art["zeros"].astype(np.float32)
+    assert np.any(zeros == 0) and np.any(zeros == 15) and np.any((zeros > 0) & (zeros < 15))
+
+
 def test_flags_nonfinite(awq):
     _, X, W = synth.custom_layer(64, 256, 64, seed=6)
     Xn = X.clone()
