@@ -41,7 +41,12 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xffffu);
 }
 
-__global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+// At most 256 registers a lane (two blocks per CU, 2 x 72 KiB of LDS): while one block waits for
+// its next step's loads the other multiplies.  At one block per CU (264 registers) the one step
+// of prefetch could not cover the load latency and G took 1.7x as long (measured; a second
+// register set for two steps of prefetch instead gained half as much and does not fit with two
+// blocks).
+__global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                    int64_t ldx, uint16_t* __restrict__ Gs) {
   __shared__ __attribute__((aligned(16))) uint16_t t1[2][GT][GPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t t2[2][GT][GPITCH];
