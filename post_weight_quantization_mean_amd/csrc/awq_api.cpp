@@ -204,12 +204,14 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   const int64_t rows = gram ? 2 * K : M;  // rows of the product's left operand
   SearchLayout L;
   if (!search_layout(rows, K, NP, n_grid, &L)) return AWQ_ERR_SHAPE;
-  size_t total = L.total, gs_off = 0;
+  size_t total = L.total, gs_off = 0, gp_off = 0;
   if (gram) {
     const int64_t gsb = mul_ok(mul_ok(2 * K, K), 2);
     if (gsb < 0) return AWQ_ERR_SHAPE;
     gs_off = total;
     total += align_up((size_t)gsb);
+    gp_off = total;  // fp32 sums of the G tiles split along the tokens
+    total += align_up(awq::gram_partial_bytes(M, K));
   }
   if (ws == nullptr || ws_bytes < total) return AWQ_ERR_WORKSPACE;
   if (!aligned16(ws) || !aligned16(a)) return AWQ_ERR_INVALID_ARG;
@@ -225,9 +227,10 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const awq::SearchPlan plan = awq::search_plan(rows, K, NP, n_grid);
   uint16_t* Gs = gram ? reinterpret_cast<uint16_t*>(base + gs_off) : nullptr;
+  float* gpart = gram ? reinterpret_cast<float*>(base + gp_off) : nullptr;
 
   hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
-  if (e == hipSuccess && gram) e = awq::launch_gram(static_cast<const uint16_t*>(X), M, K, ldx, Gs, s);
+  if (e == hipSuccess && gram) e = awq::launch_gram(static_cast<const uint16_t*>(X), M, K, ldx, Gs, gpart, s);
   for (int i = 0; i < n_weights && e == hipSuccess; ++i)
     e = awq::launch_group_range(Ws[i], wf32, Ns[i], K, ldws[i], s_tab, n_grid, params, segs.tile0[i] * 128,
                                 NP, flags, s);
@@ -280,7 +283,7 @@ AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, 
   if (!search_layout(2 * K, K, N, n_grid, &L)) return 0;
   const int64_t gsb = mul_ok(mul_ok(2 * K, K), 2);
   if (gsb < 0) return 0;
-  return L.total + align_up((size_t)gsb);
+  return L.total + align_up((size_t)gsb) + align_up(awq::gram_partial_bytes(M, K));
 }
 
 AWQ_API int awq_search_gram(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const void* W,

@@ -131,7 +131,10 @@ hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx,
                                const float2* sr_tab, const float2* params, int n_grid,
                                const SearchPlan& plan, double* partial, hipStream_t st, bool gram = false);
 // Gram form: Gs bf16 [2K, K] = [bf16(G); bf16(G - bf16(G))], G = X^T X for bf16 X [M, K]
-hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, hipStream_t st);
+// bytes of fp32 slice sums that launch_gram needs beside Gs (0 when no tile is split)
+size_t gram_partial_bytes(int64_t M, int64_t K);
+hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,
+                       hipStream_t st);
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
                          float* s_best, uint32_t* flags, hipStream_t st);

@@ -47,12 +47,21 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // register set for two steps of prefetch instead gained half as much and does not fit with two
 // blocks).
 __global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                   int64_t ldx, uint16_t* __restrict__ Gs) {
+                                                   int64_t ldx, uint16_t* __restrict__ Gs, int64_t full, int S,
+                                                   int64_t slice_tokens, float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t t1[2][GT][GPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t t2[2][GT][GPITCH];
-  // upper-triangle tile (i, j), i <= j, of T x T tiles: blockIdx = i T - i (i - 1) / 2 + (j - i)
+  // Block b < full computes tile b over all M tokens and writes it to Gs.  Block full + u S + s
+  // computes tile full + u over tokens [s slice_tokens, (s + 1) slice_tokens) (whole 1024-token
+  // blocks) and writes the fp32 sum to partial[u S + s]; gram_fixup_kernel adds the slices.
+  const bool whole = blockIdx.x < full;
+  const int64_t item = whole ? 0 : blockIdx.x - full;
+  const int64_t tile = whole ? blockIdx.x : full + item / S;
+  const int64_t mbeg = whole ? 0 : (item % S) * slice_tokens;
+  const int64_t mend = whole ? M : (mbeg + slice_tokens < M ? mbeg + slice_tokens : M);
+  // upper-triangle tile (i, j), i <= j, of T x T tiles: tile = i T - i (i - 1) / 2 + (j - i)
   const int64_t T = K / GT;
-  int64_t i = 0, rem = blockIdx.x;
+  int64_t i = 0, rem = tile;
   while (rem >= T - i) {
     rem -= T - i;
     ++i;
@@ -65,14 +74,14 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict
   const uint16_t* src = X + (second ? k2b : k1b) + 8 * cg;
   uint16_t (*dst)[GT][GPITCH] = second ? t2 : t1;
   u32x4 rows[8];
-  int valid = 0;  // rows past M: loaded from row M - 1 (no branch, so no wait on the prefetch), zeroed at the store
+  int valid = 0;  // rows past mend: loaded from row mend - 1 (no branch, so no wait on the prefetch), zeroed at the store
   auto load = [&](int64_t m0) {
     valid = 0;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int64_t m = m0 + 8 * tg + r;
-      rows[r] = *reinterpret_cast<const u32x4*>(src + (m < M ? m : M - 1) * ldx);
-      valid |= (m < M ? 1 : 0) << r;
+      rows[r] = *reinterpret_cast<const u32x4*>(src + (m < mend ? m : mend - 1) * ldx);
+      valid |= (m < mend ? 1 : 0) << r;
     }
   };
   auto store = [&](int b) {
@@ -102,13 +111,15 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict
       for (int e = 0; e < 16; ++e) acc[a][c][e] = tot[a][c][e] = 0.0f;
   const int r1 = 64 * (wave >> 1), c2 = 64 * (wave & 1);  // this wave's rows (k1) and columns (k2)
   const int fr = lane & 31, fk = 8 * (lane >> 5);
-  const int64_t steps = (M + GS - 1) / GS;
-  load(0);
+  // a slice starts on a 1024-token boundary, so the block sums below are the same blocks of
+  // tokens as in a whole tile
+  const int64_t steps = (mend - mbeg + GS - 1) / GS;
+  load(mbeg);
   store(0);
   __syncthreads();
   for (int64_t st = 0; st < steps; ++st) {
     const int b = (int)(st & 1);
-    if (st + 1 < steps) load((st + 1) * GS);
+    if (st + 1 < steps) load(mbeg + (st + 1) * GS);
 #pragma unroll
     for (int h = 0; h < GS / 16; ++h) {
       bf16x8 fa[2], fb[2];
@@ -136,6 +147,20 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict
     __syncthreads();
   }
   // 32x32 result layout: lane l holds column l % 32, rows 8 (e / 4) + 4 (l / 32) + e % 4.
+  if (!whole) {  // a slice: its fp32 sum, tile-local [k1][k2]
+    float* P = partial + item * (GT * GT);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int k1 = r1 + 32 * a + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+          const int k2 = c2 + 32 * c + (lane & 31);
+          P[k1 * GT + k2] = tot[a][c][e] + acc[a][c][e];
+        }
+    return;
+  }
   // G[k1][k2] and, off the diagonal tiles, G[k2][k1]: rows of G_hi, then rows of G_lo.
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -157,11 +182,81 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict
       }
 }
 
+// The split tiles: element (k1, k2) of tile full + u is the sum of its S slices in slice order,
+// starting from 0 -- the order in which a whole tile adds its 1024-token block sums, so with one
+// block per slice the result is the same bits as the whole-tile kernel's.
+__global__ __launch_bounds__(256) void gram_fixup_kernel(const float* __restrict__ partial, int64_t K,
+                                                          int64_t full, int S, uint16_t* __restrict__ Gs) {
+  const int64_t u = blockIdx.y;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // k1 GT + k2, tile-local
+  const int k1l = (int)(idx / GT), k2l = (int)(idx % GT);
+  const int64_t T = K / GT;
+  int64_t i = 0, rem = full + u;
+  while (rem >= T - i) {
+    rem -= T - i;
+    ++i;
+  }
+  const int64_t k1b = i * GT, k2b = (i + rem) * GT;
+  float g = 0.0f;
+  for (int s = 0; s < S; ++s) g += partial[(u * S + s) * (GT * GT) + idx];
+  const int64_t k1 = k1b + k1l, k2 = k2b + k2l;
+  const uint16_t hi = bf16_bits(g);
+  const uint16_t lo = bf16_bits(g - __uint_as_float((uint32_t)hi << 16));
+  Gs[k1 * K + k2] = hi;
+  Gs[(K + k1) * K + k2] = lo;
+  if (k1b != k2b) {
+    Gs[k2 * K + k1] = hi;
+    Gs[(K + k2) * K + k1] = lo;
+  }
+}
+
+// Two blocks per CU on 256 CUs.  With tiles = q 512 + r, the first q 512 tiles run whole; the r
+// tiles of the last, partial round are cut into S token slices of whole 1024-token blocks, so
+// that r S is about one round (K = 4096: 528 tiles, 16 of them in 16 slices each).
+constexpr int64_t kGramSlots = 512;
+constexpr int64_t kGramBlockTokens = GS * kGramBlockSteps;
+
+struct GramPlan {
+  int64_t tiles, full, r, slice_tokens;
+  int S;
+};
+
+GramPlan gram_plan(int64_t M, int64_t K) {
+  GramPlan p;
+  const int64_t T = K / GT;
+  p.tiles = T * (T + 1) / 2;
+  p.r = p.tiles % kGramSlots;
+  p.full = p.tiles - p.r;
+  const int64_t nblk = (M + kGramBlockTokens - 1) / kGramBlockTokens;
+  int64_t S = p.r > 0 ? kGramSlots / p.r : 1;
+  if (S > nblk) S = nblk;
+  if (S < 1) S = 1;
+  const int64_t bps = (nblk + S - 1) / S;  // 1024-token blocks per slice
+  p.slice_tokens = bps * kGramBlockTokens;
+  p.S = (int)((nblk + bps - 1) / bps);
+  if (p.S <= 1) {  // one slice: the leftover tiles run whole
+    p.full = p.tiles;
+    p.r = 0;
+    p.S = 1;
+  }
+  return p;
+}
+
 }  // namespace
 
-hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, hipStream_t st) {
-  const int64_t T = K / GT;
-  gram_kernel<<<(unsigned)(T * (T + 1) / 2), 256, 0, st>>>(X, M, K, ldx, Gs);
+size_t gram_partial_bytes(int64_t M, int64_t K) {
+  const GramPlan p = gram_plan(M, K);
+  return (size_t)(p.r * p.S) * GT * GT * sizeof(float);
+}
+
+hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,
+                       hipStream_t st) {
+  const GramPlan p = gram_plan(M, K);
+  gram_kernel<<<(unsigned)(p.full + p.r * p.S), 256, 0, st>>>(X, M, K, ldx, Gs, p.full, p.S, p.slice_tokens,
+                                                             partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.r == 0) return e;
+  gram_fixup_kernel<<<dim3((unsigned)(GT * GT / 256), (unsigned)p.r), 256, 0, st>>>(partial, K, p.full, p.S, Gs);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ def gram_tolerance(X64, W32, s_table, ref_losses):
     (700, 384, 130),    # 2K = 768 rows of [G_hi; G_lo]: a 512-row tile holds rows of both
     (64, 128, 1),       # degenerate: one group, one output
     (4096, 512, 256),
+    (2048, 4096, 128),  # 528 G tiles: 512 whole, the other 16 in two token slices each
 ])
 def test_gram_search_vs_oracle(awq, M, K, N):
     banner(f"search gram M={M} K={K} N={N}")
