@@ -105,6 +105,25 @@ def test_strided_activations_and_output(awq):
     assert torch.all(Yfull[:, 64:] == -7.0)  # outside the output view: untouched
 
 
+def test_prefill_strided_activations_and_output(awq):
+    """The prefill (more than 8 bf16 tokens) on an X view with row stride K + 72 and an output
+    view with row stride N + 40: the X copies address rows by their stride, and nothing outside
+    the output view is written."""
+    banner("w4a16 prefill strided")
+    M, K, N = 600, 1024, 200
+    art = artefact(N, K, 11)
+    full = torch.from_numpy(np.random.default_rng(12).standard_normal((M, K + 72)).astype(np.float32)).to(torch.bfloat16)
+    Xd = full.to(DEV)[:, :K]
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    sc = torch.from_numpy(art["scales"].view(np.float16)).to(DEV)
+    zz = torch.from_numpy(art["zeros"].view(np.float16)).to(DEV)
+    Yfull = torch.full((M, N + 40), -7.0, device=DEV)
+    awq.w4a16(Xd, q, sc, zz, out=Yfull[:, :N])
+    check(Yfull[:, :N].cpu().numpy().astype(np.float64), full[:, :K].float().numpy().astype(np.float64), art,
+          prefill=True, biased=False)
+    assert torch.all(Yfull[:, N:] == -7.0)
+
+
 def test_scaled_inputs_recover_the_layer(awq):
     """GPU chain: pack S W on the GPU, feed X / s: the W4A16 output approximates X W^T within the
     quantization error bound |E| <= Delta / (2 s), plus |q - z| times the fp16 rounding of Delta."""
