@@ -360,6 +360,28 @@ def test_pack_bf16_group_categories(awq):
     assert np.any(zeros == 0) and np.any(zeros == 15) and np.any((zeros > 0) & (zeros < 15))
 
 
+def test_strided_inputs_match_contiguous(awq):
+    """Row strides larger than K (X: K + 64, W: K + 128): stats, the direct search and the Gram
+    search read rows by their stride and give the same bits as on contiguous copies."""
+    banner("stats / search / gram on strided views")
+    M, K, N = 1500, 512, 300
+    _, X, W = synth.custom_layer(M, K, N, dtype="bf16", seed=24)
+    Xbig = torch.zeros((M, K + 64), dtype=X.dtype)
+    Xbig[:, :K] = X
+    Wbig = torch.zeros((N, K + 128), dtype=W.dtype)
+    Wbig[:, :K] = W
+    Xv, Wv = Xbig.to(DEV)[:, :K], Wbig.to(DEV)[:, :K]
+    Xc, Wc = X.to(DEV), W.to(DEV)
+    assert Xv.stride(0) == K + 64 and Wv.stride(0) == K + 128
+    a_v, a_c = awq.stats(Xv), awq.stats(Xc)
+    assert torch.equal(a_v, a_c)
+    for gram in (False, True):
+        r_v = awq.search(Xv, Wv, a_c, gram=gram)
+        r_c = awq.search(Xc, Wc, a_c, gram=gram)
+        assert torch.equal(r_v.losses, r_c.losses) and r_v.best_index == r_c.best_index, gram
+        assert torch.equal(r_v.s_best, r_c.s_best)
+
+
 def test_flags_nonfinite(awq):
     _, X, W = synth.custom_layer(64, 256, 64, seed=6)
     Xn = X.clone()
