@@ -174,6 +174,13 @@ def test_search_gram_workspace(L):
         L.awq_search_workspace_bytes(2 * K, K, N, 128, 20) + 2 * K * K * 2
     assert L.awq_search_gram_workspace_bytes(16384, 4000, N, 128, 20) == 0
     assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 65) == 0
+    # plus the fp32 sums of the G tiles split along the tokens: at K = 4096, 528 upper-triangle
+    # tiles of 128 x 128, the 16 past the first 512 split into 16 slices of 1024 tokens
+    base = L.awq_search_workspace_bytes(2 * K, K, N, 128, 20) + 2 * K * K * 2
+    assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= base + 16 * 16 * 128 * 128 * 4
+    # K = 5120: 820 tiles; the 308 past the first 512 would get one slice each, so none is split
+    base = L.awq_search_workspace_bytes(2 * 5120, 5120, N, 128, 20) + 2 * 5120 * 5120 * 2
+    assert base <= L.awq_search_gram_workspace_bytes(16384, 5120, N, 128, 20) < base + 4096
 
 
 def pack(L, W=P, wt=BF16, N=128, K=256, ldw=256, s=P, group=128, q=P, sc=P, z=P, fl=P):
