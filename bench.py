@@ -276,7 +276,7 @@ def main():
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the library runs the path on one GPU; --gpus must be 1 "
                                    "(the path would shard along N with one 160-byte loss all-reduce)"}))
         sys.exit(2)
 
