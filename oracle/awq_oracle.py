@@ -57,7 +57,7 @@ invariants, brute force on tiny inputs).  Nothing here is "parity unpinned".
 """
 from __future__ import annotations
 
-from math import isfinite, sqrt
+from math import fsum, isfinite, sqrt
 from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
@@ -320,69 +320,77 @@ def artefact_bits_per_weight(N: int, K: int, group: int = GROUP) -> float:
 
 # ---------------------------------------------------------------------------------------
 # Teaching mode: the symmetric [-7, 7] quantizer and scaled forward  [EXPLAINER §2, §3]
+# Written from the definitions (vectorised, float64); it exists only to reproduce the numbers
+# the page prints for its two-channel example.
 # ---------------------------------------------------------------------------------------
+TEACH_QMAX = 7  # [EXPLAINER §2] symmetric codes -7 .. 7
+
+
+def _finite_vector(values, what: str) -> np.ndarray:
+    v = np.asarray(values, dtype=np.float64).reshape(-1)
+    if v.size == 0 or not np.all(np.isfinite(v)):
+        raise ValueError(f"{what} needs finite values")
+    return v
+
+
 def teaching_qdq(values: Sequence[float]) -> Tuple[List[int], List[float], float]:
-    """Symmetric absmax quantizer of [EXPLAINER §2]: one step Delta = max|v| / 7 per group,
-    integer codes in [-7, 7] by nearest rounding with ties to even; an all-zero group uses
-    Delta = 1.  Only finite values are accepted."""
-    vals = [float(v) for v in values]
-    if not vals or any(not isfinite(v) for v in vals):
-        raise ValueError("a group needs finite values")
-    peak = max(abs(v) for v in vals)
-    step = 1.0 if peak == 0 else peak / 7.0
-    if not (isfinite(step) and step > 0):
-        raise ValueError("step outside the float range")
-    codes = []
-    for v in vals:
-        c = round(v / step)  # Python round: nearest, ties to even
-        codes.append(int(min(7, max(-7, c))))
-    restored = [step * c for c in codes]
-    if any(not isfinite(r) for r in restored):
-        raise ValueError("reconstruction is not finite")
-    return codes, restored, step
+    """The symmetric absmax quantizer of [EXPLAINER §2] on one group: step = max|v| / 7 (the
+    page uses step 1 for an all-zero group), code = v / step rounded to the nearest integer
+    with ties to even and limited to [-7, 7], reconstruction = step * code.
+    Returns (codes, reconstruction, step)."""
+    v = _finite_vector(values, "a group")
+    peak = float(np.max(np.abs(v)))
+    step = peak / TEACH_QMAX if peak > 0.0 else 1.0
+    if not 0.0 < step < np.inf:
+        raise ValueError("the step is outside the float range")
+    codes = np.clip(np.rint(v / step), -TEACH_QMAX, TEACH_QMAX)
+    return [int(c) for c in codes], [float(r) for r in codes * step], step
+
+
+def _kept_in_range(original: np.ndarray, scaled: np.ndarray) -> bool:
+    """A scaled copy is usable when every value stays finite and no non-zero value vanishes."""
+    return bool(np.all(np.isfinite(scaled)) and not np.any((original != 0) & (scaled == 0)))
 
 
 def teaching_forward(x: Sequence[float], w: Sequence[float], scales: Sequence[float]
                      ) -> Tuple[float, List[int], float]:
-    """One output of the scaled layer of [EXPLAINER §3]: y = sum_j (x_j / s_j) * Q(w_j s_j),
-    with all channels in one teaching group.  Rejects mismatched lengths, non-finite input,
-    non-positive scales and any transform or product that leaves the float range."""
-    if not (len(x) == len(w) == len(scales)) or len(x) == 0:
-        raise ValueError("x, w and scales need the same non-zero length")
-    if any(not isfinite(v) for v in list(x) + list(w)):
+    """One output of the scaled layer of [EXPLAINER §3], all channels in one teaching group:
+    y = sum_j (x_j / s_j) * Q(w_j * s_j), the sum rounded once (math.fsum of the products).
+    Without quantization this is x.w exactly (XW = (XS^-1)(SW)).  Rejects mismatched or empty
+    vectors, non-finite values, non-positive scales, and scalings that overflow or flush a
+    value to zero.  Returns (y, codes, step)."""
+    xv = np.asarray(x, dtype=np.float64).reshape(-1)
+    wv = np.asarray(w, dtype=np.float64).reshape(-1)
+    sv = np.asarray(scales, dtype=np.float64).reshape(-1)
+    if xv.size == 0 or xv.shape != wv.shape or xv.shape != sv.shape:
+        raise ValueError("x, w and the scales need the same non-zero length")
+    if not (np.all(np.isfinite(xv)) and np.all(np.isfinite(wv))):
         raise ValueError("inputs must be finite")
-    if any(not (isfinite(s) and s > 0) for s in scales):
+    if not np.all(np.isfinite(sv) & (sv > 0)):
         raise ValueError("scales must be finite and positive")
-    xs = [xi / si for xi, si in zip(x, scales)]
-    ws = [wi * si for wi, si in zip(w, scales)]
-    for orig, new in ((x, xs), (w, ws)):
-        for o, n in zip(orig, new):
-            if not isfinite(n) or (o != 0 and n == 0):
-                raise ValueError("scaling left the float range")
+    xs, ws = xv / sv, wv * sv
+    if not (_kept_in_range(xv, xs) and _kept_in_range(wv, ws)):
+        raise ValueError("the scaling left the float range")
     codes, restored, step = teaching_qdq(ws)
-    terms = [a * b for a, b in zip(xs, restored)]
-    for a, b, t in zip(xs, restored, terms):
-        if not isfinite(t) or (a != 0 and b != 0 and t == 0):
-            raise ValueError("product left the float range")
-    y = sum(terms)
+    y = fsum(xs * np.asarray(restored))
     if not isfinite(y):
-        raise ValueError("output is not finite")
+        raise ValueError("the output is not finite")
     return y, codes, step
 
 
-def teaching_search(x: Sequence[float], w: Sequence[float], n_grid: int = N_GRID
-                    ) -> Tuple[List[Tuple[float, float, float]], int]:
-    """The candidate search of [EXPLAINER §3/§4] on one token with the teaching quantizer:
-    a = |x| (one calibration row), scales from ``candidate_scales``, loss (y - x.w)^2.
-    Returns the history [(loss, alpha, y)] and the index of the first minimum."""
-    target = sum(xi * wi for xi, wi in zip(x, w))
-    a = [abs(v) for v in x]
-    history = []
-    for alpha in alpha_grid(n_grid):
-        s = [float(v) for v in candidate_scales(a, alpha)]
-        y, _, _ = teaching_forward(x, w, s)
-        history.append(((y - target) ** 2, alpha, y))
-    return history, first_argmin([h[0] for h in history])
+def teaching_search(x: Sequence[float], w: Sequence[float], n_grid: int = N_GRID) -> Dict[str, object]:
+    """The candidate search of [EXPLAINER §3, §4] on a single token with the teaching quantizer:
+    the statistic of one calibration row is |x|, candidate i uses candidate_scales(|x|, i/n),
+    and its loss is (y_i - x.w)^2.  Returns the arrays alpha, y and loss over the candidates and
+    ``best``, the first index of the least loss."""
+    xv = _finite_vector(x, "x")
+    wv = _finite_vector(w, "w")
+    target = fsum(xv * wv)
+    alphas = alpha_grid(n_grid)
+    ys = np.array([teaching_forward(xv, wv, candidate_scales(np.abs(xv), al))[0] for al in alphas])
+    losses = (ys - target) ** 2
+    return {"alpha": np.array(alphas), "y": ys, "loss": losses, "best": first_argmin(list(losses)),
+            "target": target}
 
 
 # ---------------------------------------------------------------------------------------
@@ -400,46 +408,38 @@ def clip_factors(n_clip: int = CLIP_CANDIDATES) -> np.ndarray:
 
 
 def teaching_clip_qdq(values: Sequence[float], factor: float) -> List[float]:
-    """The symmetric teaching quantizer with a clipping threshold ([EXPLAINER §5]): the
-    threshold is factor * max|v|, the step is threshold / 7, values are clamped to
-    +-threshold and then rounded to the nearest step (ties to even), codes limited to
-    [-7, 7].  An all-zero group stays zero.  Finite values and 0 < factor <= 1 only."""
-    vals = [float(v) for v in values]
-    if not vals or any(not isfinite(v) for v in vals):
-        raise ValueError("a group needs finite values")
+    """The teaching quantizer of [EXPLAINER §5] with a clipping threshold: t = factor * max|v|,
+    step = t / 7, each value clamped to [-t, t] and then reconstructed as step times its code
+    (nearest, ties to even, limited to [-7, 7]).  An all-zero group stays zero.  Finite values
+    and 0 < factor <= 1 only.  Returns the reconstruction."""
+    v = _finite_vector(values, "a group")
     if not (isfinite(factor) and 0.0 < factor <= 1.0):
         raise ValueError("the clipping factor must lie in (0, 1]")
-    peak = max(abs(v) for v in vals)
+    peak = float(np.max(np.abs(v)))
     if peak == 0.0:
-        return [0.0] * len(vals)
+        return [0.0] * v.size
     thr = peak * factor
-    step = thr / 7.0
-    if not (isfinite(step) and step > 0.0):
-        raise ValueError("threshold outside the float range")
-    out = []
-    for v in vals:
-        c = round(min(thr, max(-thr, v)) / step)  # Python round: ties to even
-        out.append(step * min(7, max(-7, c)))
-    return out
+    step = thr / TEACH_QMAX
+    if not 0.0 < step < np.inf:
+        raise ValueError("the threshold is outside the float range")
+    codes = np.clip(np.rint(np.clip(v, -thr, thr) / step), -TEACH_QMAX, TEACH_QMAX)
+    return [float(r) for r in codes * step]
 
 
 def teaching_clip_search(groups: Sequence[Tuple[Sequence[float], Sequence[float]]],
                          n_clip: int = CLIP_CANDIDATES) -> List[Tuple[float, float, float]]:
-    """Independent per-group clipping choice of [EXPLAINER §5] on one token: for each group
-    (x, w) the reference partial output x.w is compared with x.Q_c(w) for every factor, and
-    the first factor with the least squared difference wins.  Returns, per group,
-    (factor, prediction, reference)."""
+    """The per-group threshold choice of [EXPLAINER §5] on one token: group g's partial output
+    x_g.w_g is the reference, candidate i predicts x_g.Q_i(w_g) with factor 1 - i/20, and the
+    first factor with the least squared difference wins, independently per group.  Sums are
+    rounded once (math.fsum).  Returns, per group, (factor, prediction, reference)."""
+    factors = [1.0 - i / 20.0 for i in range(n_clip)]
     out = []
     for x, w in groups:
-        ref = sum(float(a) * float(b) for a, b in zip(x, w))
-        best = None
-        for i in range(n_clip):
-            f = 1.0 - i / 20.0
-            pred = sum(float(a) * b for a, b in zip(x, teaching_clip_qdq(w, f)))
-            loss = (pred - ref) ** 2
-            if best is None or loss < best[0]:
-                best = (loss, f, pred)
-        out.append((best[1], best[2], ref))
+        xv = _finite_vector(x, "x")
+        ref = fsum(xv * _finite_vector(w, "w"))
+        preds = np.array([fsum(xv * np.asarray(teaching_clip_qdq(w, f))) for f in factors])
+        i = first_argmin(list((preds - ref) ** 2))
+        out.append((factors[i], float(preds[i]), ref))
     return out
 
 

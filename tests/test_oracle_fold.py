@@ -95,3 +95,42 @@ def test_activation_odd_part(act):
     x = np.linspace(-6, 6, 41)
     assert np.allclose(f(x) - f(-x), x, rtol=0, atol=1e-14)
     assert f(np.array([0.0]))[0] == 0.0
+
+
+# Value pins for the two activations, fixed by mathematics rather than by the oracle's formula.
+# The standard normal CDF gives Phi(1.6448536269514722) = 0.95 (the 95% quantile) and
+# Phi(1) = 0.8413447460685429, and GELU(x) = x Phi(x).  The logistic function gives
+# sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4, and SiLU(x) = x sigmoid(x).  A dropped sqrt(2)
+# in the erfc argument, or a sign flip in the SiLU exponent, fails these.
+@pytest.mark.parametrize("x,phi", [(1.6448536269514722, 0.95), (1.0, 0.8413447460685429),
+                                   (-1.0, 1.0 - 0.8413447460685429), (-1.6448536269514722, 0.05)])
+def test_gelu_normal_cdf_values(x, phi):
+    got = float(o.gelu(np.array([x]))[0])
+    assert got == pytest.approx(x * phi, rel=1e-14, abs=0)
+
+
+def test_gelu_matches_library_normal_cdf():
+    """GELU(x) = x Phi(x) against scipy's own normal CDF (scipy.special.ndtr) on [-10, 10]."""
+    ndtr = pytest.importorskip("scipy.special").ndtr
+    x = np.linspace(-10.0, 10.0, 2001)
+    want = x * ndtr(x)
+    got = o.gelu(x)
+    nz = want != 0
+    assert np.all(np.abs(got[nz] - want[nz]) <= 1e-13 * np.abs(want[nz]))
+
+
+def test_silu_logistic_values():
+    ln3 = np.log(3.0)
+    got = o.silu(np.array([ln3, -ln3]))
+    assert got[0] == pytest.approx(0.75 * ln3, rel=1e-15, abs=0)
+    assert got[1] == pytest.approx(-0.25 * ln3, rel=1e-15, abs=0)
+
+
+def test_silu_matches_library_logistic():
+    """SiLU(x) = x sigmoid(x) against scipy's logistic function (scipy.special.expit)."""
+    expit = pytest.importorskip("scipy.special").expit
+    x = np.linspace(-30.0, 30.0, 1201)
+    want = x * expit(x)
+    got = o.silu(x)
+    nz = want != 0
+    assert np.all(np.abs(got[nz] - want[nz]) <= 1e-14 * np.abs(want[nz]))

@@ -29,16 +29,19 @@ def test_hand_picked_scales(case):
 
 
 def test_twenty_candidate_search_matches_page():
-    hist, best = o.teaching_search(G["x"], G["w"])
+    r = o.teaching_search(G["x"], G["w"])
+    best = r["best"]
     s = G["search"]
-    assert len(hist) == s["n_candidates"]
-    assert hist[-1][1] == s["last_alpha"]
-    assert hist[best][1] == s["alpha_best"]
-    assert round(hist[best][2], s["printed_decimals"]) == s["y_best_printed"]
+    assert len(r["y"]) == len(r["loss"]) == len(r["alpha"]) == s["n_candidates"]
+    assert r["target"] == G["target"]["value"]
+    assert r["alpha"][-1] == s["last_alpha"]
+    assert r["alpha"][best] == s["alpha_best"]
+    assert round(r["y"][best], s["printed_decimals"]) == s["y_best_printed"]
     # the chosen candidate beats the unscaled one (alpha = 0)
-    assert hist[best][0] < hist[0][0]
+    assert r["loss"][best] < r["loss"][0]
     # alpha = 0 is the unscaled layer: y = 17/7, loss (17/7 - 2)^2 = 9/49
-    assert math.isclose(hist[0][0], 9 / 49, rel_tol=1e-12)
+    assert math.isclose(r["loss"][0], 9 / 49, rel_tol=1e-12)
+    assert math.isclose(r["y"][0], 17 / 7, rel_tol=1e-15)
 
 
 def test_alpha_grid_excludes_one():
@@ -83,8 +86,8 @@ def test_teaching_forward_range_checks(x, w, s):
 def test_exact_rational_y_for_chosen_candidate():
     # y at the chosen alpha recomputed in exact rationals from the quantizer's definition
     # (codes from nearest rounding, step = max|v|/7) agrees with the float search.
-    hist, best = o.teaching_search(G["x"], G["w"])
-    alpha = hist[best][1]
+    r = o.teaching_search(G["x"], G["w"])
+    alpha = float(r["alpha"][r["best"]])
     s = [Fraction(float(v)) for v in o.candidate_scales([abs(v) for v in G["x"]], alpha)]
     x = [Fraction(v) for v in G["x"]]
     w = [Fraction(v) for v in G["w"]]
@@ -92,7 +95,7 @@ def test_exact_rational_y_for_chosen_candidate():
     step = max(abs(v) for v in ws) / 7
     codes = [min(7, max(-7, round(v / step))) for v in ws]
     y = sum(xi / si * step * c for xi, si, c in zip(x, s, codes))
-    assert abs(float(y) - hist[best][2]) < 1e-12
+    assert abs(float(y) - r["y"][r["best"]]) < 1e-12
 
 
 def test_bits_per_weight_budget():
