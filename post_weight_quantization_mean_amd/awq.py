@@ -120,6 +120,39 @@ def _matrix(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
     return t.shape[0], t.shape[1], t.stride(0)
 
 
+def _same_device(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+
+
+def _out(t: torch.Tensor, shape: Tuple[int, ...], dtype: torch.dtype, dev: torch.device, name: str) -> torch.Tensor:
+    """A caller-supplied output buffer: the kernels write shape x dtype bytes through its pointer,
+    so anything else (a smaller, strided or mistyped tensor, or one on another device) is refused."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)}")
+    _same_device(t, dev, name)
+    return t
+
+
+def _workspace(t: Optional[torch.Tensor], need: int, dev: torch.device) -> Tuple[torch.Tensor, int]:
+    """The workspace tensor and its size in bytes (the library refuses one below ``need``)."""
+    if t is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev), max(need, 1)
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _same_device(t, dev, "workspace")
+    return t, t.numel() * t.element_size()
+
+
+def _flags(t: Optional[torch.Tensor], dev: torch.device) -> torch.Tensor:
+    if t is None:
+        return torch.zeros(1, dtype=torch.int32, device=dev)
+    if t.dtype != torch.int32 or t.numel() < 1 or not t.is_contiguous():
+        raise ValueError("flags must be a contiguous int32 tensor with at least one element")
+    _same_device(t, dev, "flags")
+    return t
+
+
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -156,12 +189,12 @@ def stats(X: torch.Tensor, *, out: Optional[torch.Tensor] = None, workspace: Opt
     """a[j] = mean_m |X[m, j]| as fp32 [K]."""
     M, K, ldx = _matrix(X, "X")
     dev = X.device
-    a = out if out is not None else torch.empty(K, dtype=torch.float32, device=dev)
-    need = stats_workspace_bytes(M, K)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    a = _out(out, (K,), torch.float32, dev, "out") if out is not None else \
+        torch.empty(K, dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(workspace, stats_workspace_bytes(M, K), dev)
+    fl = _flags(flags, dev)
     st = lib().awq_stats(X.data_ptr(), _dtype_code(X), M, K, ldx, a.data_ptr(), ws.data_ptr(),
-                         ws.numel(), fl.data_ptr(), _stream(dev))
+                         ws_bytes, fl.data_ptr(), _stream(dev))
     _check(st, "awq_stats")
     if check:
         raise_for_flags(fl)
@@ -204,6 +237,8 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
         if any(w.dtype != Ws[0].dtype for w in Ws):
             raise ValueError("the weights of one search share a dtype")
         shapes = [_matrix(w, f"W[{i}]") for i, w in enumerate(Ws)]
+        for i, w in enumerate(Ws):
+            _same_device(w, X.device, f"W[{i}]")
         if any(kw != K for _, kw, _ in shapes):
             raise ValueError("X and W disagree on K")
         if fused_events is not None or gram:
@@ -213,20 +248,21 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
         N, Kw, ldw = _matrix(W, "W")
         if Kw != K:
             raise ValueError("X and W disagree on K")
+        _same_device(W, X.device, "W")
     if a.shape != (K,) or a.dtype != torch.float32 or not a.is_cuda or not a.is_contiguous():
         raise ValueError("a must be a contiguous fp32 device vector of length K")
     dev = X.device
+    _same_device(a, dev, "a")
     losses = torch.empty(n_grid, dtype=torch.float64, device=dev)
     best = torch.empty(1, dtype=torch.int32, device=dev)
     s_best = torch.empty(K, dtype=torch.float32, device=dev)
     s_table = torch.empty((n_grid, K), dtype=torch.float32, device=dev) if return_table else None
     if gram and fused_events is not None:
         raise ValueError("fused_events times the direct form")
-    need = search_workspace_bytes(M, K, N, group_size, n_grid, gram=gram)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    ws, ws_bytes = _workspace(workspace, search_workspace_bytes(M, K, N, group_size, n_grid, gram=gram), dev)
+    fl = _flags(flags, dev)
     outs = (a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(),
-            s_table.data_ptr() if s_table is not None else None, ws.data_ptr(), ws.numel(), fl.data_ptr(),
+            s_table.data_ptr() if s_table is not None else None, ws.data_ptr(), ws_bytes, fl.data_ptr(),
             _stream(dev))
     if Ws is not None:
         ptrs = (ctypes.c_void_p * len(Ws))(*[w.data_ptr() for w in Ws])
@@ -269,13 +305,20 @@ def pack(W: torch.Tensor, s: torch.Tensor, group_size: int = GROUP, *, max_val: 
                                 or not max_val.is_cuda or not max_val.is_contiguous()):
         raise ValueError("max_val must be a contiguous fp32 device tensor [N, K/group]")
     dev = W.device
+    _same_device(s, dev, "s")
+    if max_val is not None:
+        _same_device(max_val, dev, "max_val")
+    G = K // group_size if group_size > 0 else 0
     if out is None:
         qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
-        scales = torch.empty((N, K // group_size if group_size > 0 else 0), dtype=torch.float16, device=dev)
+        scales = torch.empty((N, G), dtype=torch.float16, device=dev)
         zeros = torch.empty_like(scales)
     else:
         qweight, scales, zeros = out
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        _out(qweight, (N, K // 8), torch.int32, dev, "qweight")
+        _out(scales, (N, G), torch.float16, dev, "scales")
+        _out(zeros, (N, G), torch.float16, dev, "zeros")
+    fl = _flags(flags, dev)
     if max_val is None:
         st = lib().awq_pack(W.data_ptr(), _dtype_code(W), N, K, ldw, s.data_ptr(), group_size,
                             qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), fl.data_ptr(), _stream(dev))
@@ -327,16 +370,17 @@ def clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, group_size: int = GR
     if s.shape != (K,) or s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous():
         raise ValueError("s must be a contiguous fp32 device vector of length K")
     dev = X.device
+    _same_device(W, dev, "W")
+    _same_device(s, dev, "s")
     G = K // group_size if group_size > 0 else 0
     max_val = torch.empty((N, G), dtype=torch.float32, device=dev)
     best = torch.empty((N, G), dtype=torch.int32, device=dev)
     err = torch.empty((n_clip, N, G), dtype=torch.float64, device=dev) if return_err else None
-    need = clip_workspace_bytes(M, K, N, group_size, n_clip)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    ws, ws_bytes = _workspace(workspace, clip_workspace_bytes(M, K, N, group_size, n_clip), dev)
+    fl = _flags(flags, dev)
     st = lib().awq_clip(X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
                         s.data_ptr(), group_size, n_clip, max_val.data_ptr(), best.data_ptr(),
-                        err.data_ptr() if err is not None else None, ws.data_ptr(), ws.numel(),
+                        err.data_ptr() if err is not None else None, ws.data_ptr(), ws_bytes,
                         fl.data_ptr(), _stream(dev))
     _check(st, "awq_clip")
     if check:
@@ -368,7 +412,8 @@ def fold_rows(A: torch.Tensor, s: torch.Tensor, *, flags: Optional[torch.Tensor]
     Linear's weight [K, K_in] and bias [K] absorb the inverse scaling.  Returns A."""
     rows, cols, ld = _rows2d(A, "A")
     _scales_vec(s, rows)
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=A.device)
+    _same_device(s, A.device, "s")
+    fl = _flags(flags, A.device)
     _check(lib().awq_fold_rows(A.data_ptr(), _dtype_code(A), rows, cols, ld, s.data_ptr(), fl.data_ptr(),
                                _stream(A.device)), "awq_fold_rows")
     if check:
@@ -381,7 +426,8 @@ def scale_cols(W: torch.Tensor, s: torch.Tensor, *, flags: Optional[torch.Tensor
     """In place: column k of a consuming Linear weight W [N, K] multiplied by s[k].  Returns W."""
     N, K, ld = _matrix(W, "W")
     _scales_vec(s, K)
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=W.device)
+    _same_device(s, W.device, "s")
+    fl = _flags(flags, W.device)
     _check(lib().awq_scale_cols(W.data_ptr(), _dtype_code(W), N, K, ld, s.data_ptr(), fl.data_ptr(),
                                 _stream(W.device)), "awq_scale_cols")
     if check:
@@ -398,7 +444,9 @@ def scaled_act(X: torch.Tensor, s: torch.Tensor, act: str = "gelu", *, out: Opti
     Y = out if out is not None else torch.empty_strided(X.shape, X.stride(), dtype=X.dtype, device=X.device)
     if Y.shape != X.shape or Y.stride() != X.stride() or Y.dtype != X.dtype:
         raise ValueError("out must match X in shape, strides and dtype")
-    fl = flags if flags is not None else torch.zeros(1, dtype=torch.int32, device=X.device)
+    _same_device(Y, X.device, "out")
+    _same_device(s, X.device, "s")
+    fl = _flags(flags, X.device)
     _check(lib().awq_scaled_act(X.data_ptr(), Y.data_ptr(), _dtype_code(X), M, K, ld, code, s.data_ptr(),
                                 fl.data_ptr(), _stream(X.device)), "awq_scaled_act")
     if check:
@@ -417,9 +465,12 @@ def w4a16(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: t
     for t, name in ((scales, "scales"), (zeros, "zeros")):
         if t.shape != (N, K // group_size) or t.dtype != torch.float16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous fp16 [N, K/group] tensor")
+    for t, name in ((qweight, "qweight"), (scales, "scales"), (zeros, "zeros")):
+        _same_device(t, X.device, name)
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=X.device)
     if Y.shape != (M, N) or Y.dtype != torch.float32 or Y.stride(1) != 1:
         raise ValueError("out must be fp32 [M, N] with unit stride along N")
+    _same_device(Y, X.device, "out")
     _check(lib().awq_w4a16(X.data_ptr(), _dtype_code(X), M, K, ldx, qweight.data_ptr(), scales.data_ptr(),
                            zeros.data_ptr(), N, group_size, Y.data_ptr(), Y.stride(0), _stream(X.device)),
            "awq_w4a16")

@@ -27,10 +27,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPackThreads = 256;
 constexpr int kPackUnits = kPackThreads / 4;  // units per block per iteration
 constexpr int kWaveUnits = 16;                // units per wave per iteration
-#ifndef AWQ_PACK_WINDOW
-#define AWQ_PACK_WINDOW 32768
-#endif
-constexpr int64_t kPackWindow = AWQ_PACK_WINDOW;  // target units per grid iteration
+constexpr int64_t kPackWindow = 32768;  // target units per grid iteration
 
 // Correctly rounded quotients a / b from a reciprocal y = RN(1 / b) and FMA corrections:
 // q1 = RN(q0 + RN(a - b q0) y) with q0 = RN(a y) is within one ulp of a / b, so

@@ -26,10 +26,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStatsWaves = 4;
 constexpr int kStatsThreads = kStatsWaves * 64;
-#ifndef AWQ_STATS_ROWS
-#define AWQ_STATS_ROWS 4
-#endif
-constexpr int kStatsRows = AWQ_STATS_ROWS;  // consecutive rows per wave per iteration
+constexpr int kStatsRows = 4;  // consecutive rows per wave per iteration
 
 template <bool F32>
 __global__ __launch_bounds__(kStatsThreads) void stats_partial_kernel(

@@ -16,6 +16,7 @@
 //   * prefill, M > 8: the bf16 matrix cores.  A 128-row tile of W_hat is decoded per 32-channel
 //     chunk into LDS as bf16 (Delta (q - z) rounded once to bf16), X' is staged as bf16, and
 //     each of four waves accumulates 128 tokens x 128 outputs in fp32.
+#include <atomic>
 #include <type_traits>
 
 #include "awq_internal.h"
@@ -635,20 +636,30 @@ __global__ __launch_bounds__(64 * NW, 1) void w4a16_gemm_kernel(
 }  // namespace
 
 // decode grid: one wave per row group, at most what is resident at once (every wave then
-// starts at the launch and loads its first rows while X is staged)
+// starts at the launch and loads its first rows while X is staged).  The resident count is a
+// property of the device and of the kernel instantiation (its LDS size is fixed by its token
+// count), so it is queried once per device and kept: a decode launch costs ~20 us and the
+// occupancy query is not free.  The cache packs (LDS bytes, resident blocks) in one word; two
+// threads that race on the first call store the same value.
 template <typename Kern>
 int64_t gemv_blocks(Kern kern, size_t lds, int64_t waves) {
-  int dev = 0, cus = 256, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGvThreads, lds) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-#ifdef AWQ_GV_BPC
-  per_cu = AWQ_GV_BPC;
-#endif
+  constexpr int kMaxDevices = 64;
+  static std::atomic<uint64_t> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<uint64_t>* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
+  uint64_t packed = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (packed == 0 || (packed >> 32) != (uint64_t)lds) {
+    int cus = 256, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGvThreads, lds) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    packed = ((uint64_t)lds << 32) | (uint64_t)((int64_t)cus * per_cu);
+    if (slot) slot->store(packed, std::memory_order_relaxed);
+  }
+  const int64_t resident = (int64_t)(packed & 0xffffffffu);
   const int64_t need = (waves + kGvThreads / 64 - 1) / (kGvThreads / 64);
-  const int64_t resident = (int64_t)cus * per_cu;
   return need < resident ? need : resident;
 }
 
