@@ -18,7 +18,8 @@
  *   - Every pointer argument is DEVICE memory owned by the caller; buffers must stay alive
  *     until the work queued on `stream` has finished.  The library allocates no device
  *     memory, keeps no mutable global state and is reentrant; every call is asynchronous on
- *     `stream` (a hipStream_t; NULL is the default stream).
+ *     `stream` (a hipStream_t; NULL is the default stream).  The one exception is
+ *     awq_search_static, whose workspace is a static device array (see there).
  *   - Argument errors are returned synchronously as an awq_status before anything is
  *     queued; no kernel is launched in that case.
  *   - Data errors can only be seen on the device: kernels OR AWQ_FLAG_* bits into *flags.
@@ -38,7 +39,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 6
+#define AWQ_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -57,7 +58,9 @@ typedef enum {
                               (8 N K / 128 bytes) do */
   AWQ_ERR_UNSUPPORTED = 3, /* dtype other than F32/BF16, group other than 128 */
   AWQ_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than the size function says */
-  AWQ_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+  AWQ_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
+  AWQ_ERR_SCRATCH = 6      /* awq_search_static: the call needs more workspace than
+                              AWQ_STATIC_SCRATCH_BYTES */
 } awq_status;
 
 /* Element types of X and W. */
@@ -139,6 +142,27 @@ AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, i
                              int32_t* best_out, float* s_best_out, float* s_table_out, void* ws,
                              size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
                              awq_event_t fused_begin, awq_event_t fused_end);
+
+/* The same search without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It calls no hipMalloc, hipFree or allocating library routine: its workspace
+ * is a static device array of AWQ_STATIC_SCRATCH_BYTES (128 MiB) inside the library, one
+ * copy on each GPU the library runs on, held until the process ends.  The current device
+ * must be the device of `stream`.
+ *   Limit: a call whose workspace (awq_search_workspace_bytes) exceeds
+ *          AWQ_STATIC_SCRATCH_BYTES returns AWQ_ERR_SCRATCH before any HIP call (for n_grid =
+ *          20 the workspace is about 1.25 N K bytes: K = N = 4096 needs 21 MB, K = 14336 with
+ *          N = 4096 needs 74 MB; N = 28672 with K = 4096 does not fit).
+ *   Sharing: every call on one GPU uses that GPU's single copy and leaves its contents
+ *          behind; nothing in it has to start at zero.  Calls that overlap on one GPU (two
+ *          streams, or two host threads) race on it and must be serialised by the caller.
+ * Arguments, results and other errors as awq_search (no ws, ws_bytes). */
+#define AWQ_STATIC_SCRATCH_BYTES (128u * 1024u * 1024u)
+AWQ_API int awq_search_static(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                              const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                              int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
+                              float* s_best_out, float* s_table_out, uint32_t* flags,
+                              awq_stream_t stream);
 
 /* The same search for projections that read one X and must share one scale vector
  * ([EXPLAINER §6]: Q, K and V all consume the normalized input, so s applies to all of them

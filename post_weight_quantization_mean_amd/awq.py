@@ -24,6 +24,7 @@ FLAG_NONFINITE_W = 0x2
 FLAG_SCALE_RANGE = 0x4
 FLAG_F16_RANGE = 0x8
 FLAG_NONFINITE_LOSS = 0x10
+STATIC_SCRATCH_BYTES = 128 * 1024 * 1024  # awq_search_static's workspace (AWQ_STATIC_SCRATCH_BYTES)
 _FLAG_TEXT = {
     FLAG_NONFINITE_X: "activations must be finite",
     FLAG_NONFINITE_W: "weights (and weights times scales) must be finite",
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
                                  i32, i32, vp, vp, vp, vp, vp, sz, vp, vp]
         L.awq_search_timed.restype = ctypes.c_int
         L.awq_search_timed.argtypes = L.awq_search.argtypes + [vp, vp]
+        L.awq_search_static.restype = ctypes.c_int
+        L.awq_search_static.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, i64, i64, vp,
+                                        i32, i32, vp, vp, vp, vp, vp, vp]
         L.awq_search_gram_workspace_bytes.restype = sz
         L.awq_search_gram_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
         L.awq_search_gram.restype = ctypes.c_int
@@ -96,7 +100,7 @@ def lib() -> ctypes.CDLL:
         L.awq_scaled_act.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp]
         L.awq_w4a16.restype = ctypes.c_int
         L.awq_w4a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i32, vp, i64, vp]
-        if L.awq_abi_version() != 6:
+        if L.awq_abi_version() != 7:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -217,7 +221,8 @@ class SearchResult:
 def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid: int = N_GRID,
            *, return_table: bool = False, workspace: Optional[torch.Tensor] = None,
            flags: Optional[torch.Tensor] = None, check: bool = True, gram: bool = False,
-           fused_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> SearchResult:
+           fused_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
+           no_alloc: bool = False) -> SearchResult:
     """The candidate scale search over alpha = i / n_grid for one layer.  ``W`` is one weight
     [N, K], or a list of weights [N_w, K] of projections that read X and share the scales
     (query/key/value, gate/up): searched as one layer without concatenating them
@@ -228,7 +233,11 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
 
     ``fused_events``: two timing events that the library records right before and after the
     fused candidate kernel (awq_search_timed), so that ``e0.elapsed_time(e1)`` is that
-    kernel's time alone; single weight only."""
+    kernel's time alone; single weight only.
+
+    ``no_alloc``: run awq_search_static, whose workspace is the library's static device array
+    (STATIC_SCRATCH_BYTES per GPU) instead of ``workspace``; single weight, direct form.  Calls
+    that overlap on one GPU race on that array."""
     M, K, ldx = _matrix(X, "X")
     Ws = list(W) if isinstance(W, (list, tuple)) else None
     if Ws is not None:
@@ -259,6 +268,18 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
     s_table = torch.empty((n_grid, K), dtype=torch.float32, device=dev) if return_table else None
     if gram and fused_events is not None:
         raise ValueError("fused_events times the direct form")
+    if no_alloc:
+        if Ws is not None or gram or fused_events is not None or workspace is not None:
+            raise ValueError("no_alloc runs a single weight in the direct form, without workspace or events")
+        fl = _flags(flags, dev)
+        st = lib().awq_search_static(X.data_ptr(), _dtype_code(X), M, K, ldx, W.data_ptr(), _dtype_code(W), N, ldw,
+                                     a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(),
+                                     s_best.data_ptr(), s_table.data_ptr() if s_table is not None else None,
+                                     fl.data_ptr(), _stream(dev))
+        _check(st, "awq_search_static")
+        if check:
+            raise_for_flags(fl)
+        return SearchResult(losses, best, s_best, s_table, fl)
     ws, ws_bytes = _workspace(workspace, search_workspace_bytes(M, K, N, group_size, n_grid, gram=gram), dev)
     fl = _flags(flags, dev)
     outs = (a.data_ptr(), group_size, n_grid, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(),

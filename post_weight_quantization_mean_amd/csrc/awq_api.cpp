@@ -5,6 +5,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "awq.h"
 #include "awq_internal.h"
@@ -107,6 +108,36 @@ bool clip_layout(int64_t M, int64_t K, int64_t N, int n_clip, ClipLayout* out) {
   return true;
 }
 
+// ---- the allocation-free search: its workspace in a static device array -------------------
+// awq_search_static is for callers that cannot allocate device memory.  Its workspace is this
+// array: AWQ_STATIC_SCRATCH_BYTES on every GPU the library is used on, held from its module
+// load on that GPU until the process ends.  Every call on one GPU shares that GPU's copy.
+__device__ __align__(256) unsigned char scratch[AWQ_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // the device address of `scratch` on each device, once known
+
+// The device address of `scratch` on the current device.  In host code the array's name is a
+// host-side stand-in, not a device address, so it is looked up once per device, with that
+// device current, and only this pointer is ever handed to kernels.
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,6 +152,9 @@ AWQ_API const char* awq_status_string(int status) {
     case AWQ_ERR_UNSUPPORTED: return "unsupported dtype or group size";
     case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
     case AWQ_ERR_HIP: return "HIP runtime or launch error";
+    case AWQ_ERR_SCRATCH:
+      return "the call needs more workspace than the static scratch of awq_search_static holds "
+             "(AWQ_STATIC_SCRATCH_BYTES); use awq_search with a workspace";
     default: return "unknown status";
   }
 }
@@ -167,7 +201,8 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
                 int w_dtype, const int64_t* Ns, const int64_t* ldws, int32_t n_weights, const float* a,
                 int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out, float* s_best_out,
                 float* s_table_out, void* ws, size_t ws_bytes, uint32_t* flags, awq_stream_t stream,
-                awq_event_t fused_begin, awq_event_t fused_end, bool gram = false) {
+                awq_event_t fused_begin, awq_event_t fused_end, bool gram = false,
+                bool static_ws = false) {
   int st = check_matrix(X, x_dtype, M, K, ldx);
   if (st != AWQ_OK) return st;
   if (Ws == nullptr || Ns == nullptr || ldws == nullptr || n_weights < 1 || n_weights > awq::kMaxWSegs)
@@ -212,6 +247,14 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
     total += align_up((size_t)gsb);
     gp_off = total;  // fp32 sums of the G tiles split along the tokens
     total += align_up(awq::gram_partial_bytes(M, K));
+  }
+  if (static_ws) {
+    // every argument is checked above; the first HIP call of this path comes after them
+    if (total > (size_t)AWQ_STATIC_SCRATCH_BYTES) return AWQ_ERR_SCRATCH;
+    if (!aligned16(a) || (s_table_out != nullptr && !aligned16(s_table_out))) return AWQ_ERR_INVALID_ARG;
+    const hipError_t se = static_scratch(&ws);
+    if (se != hipSuccess) return AWQ_ERR_HIP;
+    ws_bytes = (size_t)AWQ_STATIC_SCRATCH_BYTES;
   }
   if (ws == nullptr || ws_bytes < total) return AWQ_ERR_WORKSPACE;
   if (!aligned16(ws) || !aligned16(a)) return AWQ_ERR_INVALID_ARG;
@@ -273,6 +316,15 @@ AWQ_API int awq_search(const void* X, int x_dtype, int64_t M, int64_t K, int64_t
   return awq_search_timed(X, x_dtype, M, K, ldx, W, w_dtype, N, ldw, a, group, n_grid,
                           losses_out, best_out, s_best_out, s_table_out, ws, ws_bytes, flags,
                           stream, nullptr, nullptr);
+}
+
+AWQ_API int awq_search_static(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                              const void* W, int w_dtype, int64_t N, int64_t ldw, const float* a,
+                              int32_t group, int32_t n_grid, double* losses_out, int32_t* best_out,
+                              float* s_best_out, float* s_table_out, uint32_t* flags, awq_stream_t stream) {
+  const void* Ws[1] = {W};
+  return search_impl(X, x_dtype, M, K, ldx, Ws, w_dtype, &N, &ldw, 1, a, group, n_grid, losses_out, best_out,
+                     s_best_out, s_table_out, nullptr, 0, flags, stream, nullptr, nullptr, false, true);
 }
 
 AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group, int32_t n_grid) {

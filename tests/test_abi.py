@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
                           "awq_search_multi_workspace_bytes", "awq_search_multi",
                           "awq_search_gram_workspace_bytes", "awq_search_gram",
                           "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip", "awq_fold_rows",
-                          "awq_scale_cols", "awq_scaled_act", "awq_w4a16"}
+                          "awq_scale_cols", "awq_scaled_act", "awq_w4a16", "awq_search_static"}
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -43,13 +43,13 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 6
-    for st in range(6):
+    assert L.awq_abi_version() == 7
+    for st in range(7):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
 
 
-OK, INVALID, SHAPE, UNSUP, WS, HIP = 0, 1, 2, 3, 4, 5
+OK, INVALID, SHAPE, UNSUP, WS, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6
 BF16, F32 = 1, 0
 P = 1 << 20  # a fake, 16-byte aligned device address: never dereferenced on these paths
 
@@ -114,6 +114,33 @@ def test_search_timed_argument_errors(L, kw, status):
     assert L.awq_search_timed(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["W"], a["wt"], a["N"], a["ldw"],
                               a["a"], a["group"], a["n_grid"], a["losses"], a["best"], a["sb"], a["tab"],
                               a["ws"], a["wsb"], a["fl"], None, None, None) == status
+
+
+def search_static(L, X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, a=P, group=128,
+                  n_grid=20, losses=P, best=P, sb=P, tab=None, fl=P):
+    return L.awq_search_static(X, xt, M, K, ldx, W, wt, N, ldw, a, group, n_grid, losses, best, sb, tab, fl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID), (dict(W=None), INVALID), (dict(a=None), INVALID), (dict(losses=None), INVALID),
+    (dict(fl=None), INVALID), (dict(N=0), INVALID), (dict(K=192, ldx=192, ldw=192), SHAPE),
+    (dict(group=64), UNSUP), (dict(n_grid=65), INVALID), (dict(xt=3), UNSUP), (dict(a=P + 4), INVALID),
+    # the workspace of a 4096 x 28672 weight (147 MB of group ranges) exceeds the 128 MiB array
+    (dict(K=4096, ldx=4096, ldw=4096, N=28672), SCRATCH),
+    (dict(K=14336, ldx=14336, ldw=14336, N=8192), SCRATCH),
+])
+def test_search_static_argument_errors(L, kw, status):
+    """The allocation-free search validates every argument and its size limit before its first
+    HIP call (the lookup of the static array), so all of these return on the CPU."""
+    assert search_static(L, **kw) == status
+
+
+def test_search_static_limit_matches_the_workspace_size(L):
+    from post_weight_quantization_mean_amd import awq
+    assert awq.STATIC_SCRATCH_BYTES == 128 * 1024 * 1024
+    # the decoder block's down projection (K = 14336, N = 4096) fits, its fused gate+up does not
+    assert L.awq_search_workspace_bytes(16384, 14336, 4096, 128, 20) <= awq.STATIC_SCRATCH_BYTES
+    assert L.awq_search_workspace_bytes(16384, 4096, 28672, 128, 20) > awq.STATIC_SCRATCH_BYTES
 
 
 def search_multi(L, X=P, xt=BF16, M=64, K=256, ldx=256, Ws=(P, P + 4096), wt=BF16, Ns=(128, 64), ldws=(256, 256),
