@@ -8,15 +8,22 @@ and G~ = G_hi + G_lo, then sums Y'[k', n] e[n, k'] with the unrounded e:
   * G: 2^-16 relative per entry (G_lo's rounding) plus fp32 sums over 1024-token blocks and
     across the M / 1024 blocks, each bounded by its count times 2^-24 of |X|^T |X|;
   * fp32 accumulation over the K products of the matrix cores and the epilogue's 16-term sums.
-The last three are bounded by c sum_{m,n} (|X| |E|^T)^2.  Per candidate the test allows
-max(1e-3 relative, that bound).  The chosen candidate follows the single-weight rule."""
+The last three are bounded by c sum_{m,n} (|X| |E|^T)^2.  Per candidate the tests allow 1e-3
+relative; only layers with fewer than TINY_OUTPUTS outputs (where no averaging hides the bf16
+rounding of E) take max(1e-3 relative, that bound).  The chosen candidate follows the
+single-weight rule."""
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 from oracle import awq_oracle as o
 from post_weight_quantization_mean_amd import synth
-from tests.test_gpu_parity import DEV, banner, check_choice, loss_tolerance
+from tests.conftest import GOLDEN
+from tests.test_gpu_parity import DEV, TINY_OUTPUTS, banner, check_choice, loss_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -31,8 +38,13 @@ def awq():
 
 
 def gram_tolerance(X64, W32, s_table, ref_losses):
+    """1e-3 relative per candidate from TINY_OUTPUTS outputs on (measured: the small cases here
+    stay within 3.2e-4, the full-size layers within 1e-5); below it max(1e-3, the bound in the
+    module docstring)."""
     M, K = X64.shape
     N = W32.shape[0]
+    if M * N >= TINY_OUTPUTS:
+        return 1e-3 * np.asarray(ref_losses)
     cG = 2.0 ** -16 + (1024 + M / 1024 + 1 + K + 16) * 2.0 ** -24
     absX = np.abs(X64)
     tol = np.empty(len(s_table))
@@ -66,9 +78,10 @@ def test_gram_search_vs_oracle(awq, M, K, N):
     err = np.abs(L - ref["losses"])
     bad = np.nonzero(err > tol)[0]
     assert bad.size == 0, f"gram loss error {err[bad] / ref['losses'][bad]} (rel) above tolerance at {bad}"
-    check_choice(res.best_index, ref["losses"], ref["best"], tol)
+    check_choice(res.best_index, ref["losses"], ref["best"], tol, n_out=M * N)
     assert np.array_equal(res.s_best.cpu().numpy(), ref["s_table"][res.best_index])
-    print(f"[gpu-case] gram max rel err {np.max(err / ref['losses']):.2e}", flush=True)
+    print(f"[gpu-case] gram max rel err {np.max(err / ref['losses']):.2e}, tolerance used "
+          f"{np.max(tol / ref['losses']):.2e} rel", flush=True)
 
 
 def test_gram_and_direct_agree(awq):
@@ -91,6 +104,34 @@ def test_gram_and_direct_agree(awq):
     if rg.best_index != rd.best_index:
         assert abs(ref["losses"][rg.best_index] - ref["losses"][rd.best_index]) <= \
             tol[rg.best_index] + tol[rd.best_index]
+
+
+GOLDEN_LOSSES = os.path.join(GOLDEN, "oracle_losses.json")
+# the layers the Gram form is for: M > 2K (16384 tokens, K = 4096), so it does less work
+GRAM_KEYS = ["block/qkv", "block/o_proj", "block/gate_up"]
+
+
+@pytest.mark.parametrize("key", GRAM_KEYS)
+def test_gram_full_size_vs_stored_oracle(awq, key):
+    """The decoder block's K = 4096 layers (M = 16384) in the Gram form against the oracle's
+    losses stored by tests/golden/make_oracle_losses.py (oracle + generator only): every
+    candidate within 1e-3 relative, the chosen candidate by the single-weight rule."""
+    g = json.load(open(GOLDEN_LOSSES))[key]
+    cfg, name = key.split("/")
+    li = [l.name for l in synth.CONFIGS[cfg].layers].index(name)
+    banner(f"full-size gram search {key} M={g['M']} K={g['K']} N={g['N']}")
+    spec, X, W = synth.make_layer(cfg, li)
+    a32 = o.activation_stat(synth.to_f64(X)).astype(np.float32)
+    assert hashlib.sha256(a32.tobytes()).hexdigest()[:16] == g["a_sha"], "generator drift"
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    del X, W
+    res = awq.search(Xd, Wd, torch.from_numpy(a32).to(DEV), gram=True)
+    L = res.losses.cpu().numpy()
+    ref = np.array(g["losses"])
+    rel = np.abs(L - ref) / ref
+    banner(f"{key} gram: best gpu {res.best_index} oracle {g['best']} max rel {rel.max():.2e}")
+    assert rel.max() <= 1e-3, rel
+    check_choice(res.best_index, ref, g["best"])
 
 
 def test_gram_is_deterministic(awq):

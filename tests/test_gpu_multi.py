@@ -59,7 +59,8 @@ def test_multi_ragged_vs_oracle(awq, Ns):
     tol = loss_tolerance(X64, W32, ref["s_table"], ref["losses"], False)
     err = np.abs(L - ref["losses"])
     assert np.all(err <= tol), f"loss error {err / ref['losses']} (rel) above tolerance"
-    check_choice(res.best_index, ref["losses"], ref["best"], tol)
+    print(f"[gpu-case] max rel err {np.max(err / ref['losses']):.2e}", flush=True)
+    check_choice(res.best_index, ref["losses"], ref["best"], tol, n_out=M * W32.shape[0])
 
 
 def test_multi_strided_views(awq):

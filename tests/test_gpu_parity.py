@@ -36,10 +36,13 @@ def banner(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
-def check_choice(best_gpu, losses_oracle, best_oracle, tol=None):
+def check_choice(best_gpu, losses_oracle, best_oracle, tol=None, n_out=None):
     """The chosen candidate must be the oracle's unless the two are within 1e-3 relative in
-    the oracle's own losses (several choices are then correct).  With a per-candidate error
-    bound ``tol`` (degenerate shapes), any choice the bounds cannot separate is correct."""
+    the oracle's own losses (several choices are then correct).  For layers with fewer than
+    TINY_OUTPUTS outputs (n_out), whose per-candidate error bound ``tol`` is wider than 1e-3,
+    any choice those bounds cannot separate is correct."""
+    if n_out is not None and n_out >= TINY_OUTPUTS:
+        tol = None
     if best_gpu == best_oracle:
         return
     gap = losses_oracle[best_gpu] - losses_oracle[best_oracle]
@@ -50,15 +53,23 @@ def check_choice(best_gpu, losses_oracle, best_oracle, tol=None):
         f"gpu picked {best_gpu}, oracle {best_oracle}, gap {rel:.2e}"
 
 
+# Below this many outputs (M N) no averaging hides the bf16 rounding of E, and the per-candidate
+# tolerance is the bound derived below; from it on every candidate is held to 1e-3 relative.
+# Measured on the small cases of this file: M N >= 6144 stay within 6.5e-4; the one-token,
+# one-output cases (M N = 1) are at 3e-2.
+TINY_OUTPUTS = 4096
+
+
 def loss_tolerance(X64, W32, s_table, ref_losses, x_is_f32):
-    """Per-candidate tolerance: max(1e-3 relative, a bound derived from the kernel's
-    arithmetic).  Each output y = sum_k x_k e_k is formed from e rounded once to bf16 (8
-    significand bits: |de| <= 2^-8 |e|), fp32 quantities rounded a few times (<= 2^-21 |w|), an
-    fp32 split of fp32 X into two bf16 terms (<= 2^-16 |x|) and fp32 accumulation over K
-    (<= K 2^-24).
-    So |dy| <= c_A sum|x||e| + c_B sum|x||w| and |d(y^2)| <= 2|y||dy| + dy^2.  The bound only
-    matters for a handful of outputs (M N small), where no averaging hides bf16 rounding."""
-    K = X64.shape[1]
+    """Per-candidate tolerance: 1e-3 relative (the rule for the search), except for layers with
+    fewer than TINY_OUTPUTS outputs, which take max(1e-3 relative, a bound derived from the
+    kernel's arithmetic).  Each output y = sum_k x_k e_k is formed from e rounded once to bf16
+    (8 significand bits: |de| <= 2^-8 |e|), fp32 quantities rounded a few times (<= 2^-21 |w|),
+    an fp32 split of fp32 X into two bf16 terms (<= 2^-16 |x|) and fp32 accumulation over K
+    (<= K 2^-24).  So |dy| <= c_A sum|x||e| + c_B sum|x||w| and |d(y^2)| <= 2|y||dy| + dy^2."""
+    M, K = X64.shape
+    if M * W32.shape[0] >= TINY_OUTPUTS:
+        return LOSS_RTOL * np.asarray(ref_losses)
     cA = 2.0 ** -8 + K * 2.0 ** -24 + (2.0 ** -16 if x_is_f32 else 0.0)
     cB = 2.0 ** -21
     absX = np.abs(X64)
@@ -88,9 +99,11 @@ def run_search_case(awq, X, W, n_grid=20):
     err = np.abs(L - ref["losses"])
     bad = np.nonzero(err > tol)[0]
     assert bad.size == 0, f"loss error {err[bad] / ref['losses'][bad]} (rel) above tolerance at {bad}"
-    check_choice(res.best_index, ref["losses"], ref["best"], tol)
+    check_choice(res.best_index, ref["losses"], ref["best"], tol, n_out=X.shape[0] * W.shape[0])
     assert np.array_equal(res.s_best.cpu().numpy(), ref["s_table"][res.best_index])
     rel = err / ref["losses"]
+    print(f"[gpu-case] max rel err {rel.max():.2e}, tolerance used {np.max(tol / ref['losses']):.2e} rel",
+          flush=True)
     return res, ref, rel
 
 
