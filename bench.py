@@ -33,11 +33,18 @@ def cpu_baseline(config: str, n_sample: int, min_seconds: float = 10.0, max_reps
     import numpy as np
     from oracle import awq_oracle as o
     from post_weight_quantization_mean_amd import synth
+    affinity = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in infos] or [1])
+        if infos:
+            i = infos[0]
+            blas = f"{i.get('internal_api', '?')} {i.get('version', '?')} ({i.get('threading_layer', '?')}, " \
+                   f"{i.get('num_threads', '?')} threads)"
     except Exception:  # threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
+        threads = affinity
     spec = synth.CONFIGS[config].layers[0]
     cfg_id = synth.CONFIGS[config].cfg_id
     X = synth.make_x(spec, 0, cfg_id, 0)
@@ -52,7 +59,8 @@ def cpu_baseline(config: str, n_sample: int, min_seconds: float = 10.0, max_reps
         times.append(time.perf_counter() - t0)
     dt = statistics.mean(times)
     frac = n_sample / spec.N
-    return {"value": frac / dt, "unit": "layer-searches/s", "cores": int(threads), "kind": "oracle",
+    return {"value": frac / dt, "unit": "layer-searches/s", "cores": int(threads), "affinity_cores": affinity,
+            "blas": blas, "kind": "oracle",
             "sample": f"{config} layer, all {spec.M} tokens and {spec.K} channels, first {n_sample} of "
                       f"{spec.N} output channels (statistic over the full X), stats + 20-candidate search "
                       f"+ pack; {len(times)} run(s), mean {dt:.2f} s, scaled by N/{n_sample}"}
@@ -134,39 +142,6 @@ def clip_search(torch, awq, Xd, Wd, s_best, stride: int = 8, reps: int = 10):
             "note": "whole awq_clip call (range pre-pass, clipped qdq + bf16 MFMA product, select)"}
 
 
-def gram_form(torch, awq, dev, reps: int = 3):
-    """The scale search in both loss forms on the decoder block's qkv layer (M = 16384 tokens,
-    K = 4096, N = 6144, bf16): the direct form (20 x 2 M K N flop on the matrix cores) and the
-    Gram form (G = X^T X once, 2 M K^2 flop, then 20 x 2 (2K) K N flop for the [G_hi; G_lo]
-    stack).  Whole calls, event-timed; seeded random values with the workload's shapes."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(3)
-    M, K, N = 16384, 4096, 6144
-    c = torch.exp(0.5 * torch.randn(K, generator=g, device=dev))
-    X = (torch.randn((M, K), generator=g, device=dev) * c).to(torch.bfloat16)
-    W = torch.randn((N, K), generator=g, device=dev).mul_(K ** -0.5).to(torch.bfloat16)
-    a = awq.stats(X)
-    ws = torch.empty(max(awq.search_workspace_bytes(M, K, N), awq.search_workspace_bytes(M, K, N, gram=True)),
-                     dtype=torch.uint8, device=dev)
-    fl = torch.zeros(1, dtype=torch.int32, device=dev)
-    res = {}
-    out = {}
-    for name, gram in (("direct", False), ("gram", True)):
-        out[name] = awq.search(X, W, a, workspace=ws, flags=fl, check=False, gram=gram)
-        ms = _time_reps(torch, lambda: awq.search(X, W, a, workspace=ws, flags=fl, check=False, gram=gram), reps)
-        flop = 20 * 2.0 * (2 * K if gram else M) * K * N + (2.0 * M * K * K if gram else 0.0)
-        res[name] = {"ms": ms, "flop": flop, "tflops": flop / (ms * 1e-3) / 1e12,
-                     "best": out[name].best_index}
-    awq.raise_for_flags(fl)
-    Ld, Lg = out["direct"].losses.double(), out["gram"].losses.double()
-    res["shape"] = [M, K, N]
-    res["speedup"] = res["direct"]["ms"] / res["gram"]["ms"]
-    res["max_rel_loss_diff"] = float(((Lg - Ld).abs() / Ld).max())
-    res["direct_equiv_tflops"] = res["direct"]["flop"] / (res["gram"]["ms"] * 1e-3) / 1e12
-    res["note"] = "whole awq_search / awq_search_gram calls; direct_equiv_tflops = direct-form flop / gram time"
-    return res
-
-
 def fold_ops(torch, awq, dev, reps: int = 10):
     """Applying the scales, at the decoder block's largest shapes: awq_scale_cols in place on the
     fused gate+up weight bf16 [28672 x 4096] and awq_scaled_act (GELU) from the MLP activation
@@ -226,6 +201,164 @@ def w4a16_products(torch, awq, dev, reps: int = 10):
                         "frac_mfma_peak": flop / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
 
 
+# Layer-searches/s (blocks/s for the block) at 50 % of the bf16 peak for the search's own
+# flop: the targets the configurations are quoted against (context, not part of `value`).
+TARGET_HALF_PEAK = {"attn": 457.8, "down": 170.3, "gate_up": 27.1, "block": 8.8}
+
+
+def layer_step(torch, awq, synth, spec, dev, reps, gram=False):
+    """One full-size layer through the whole path (statistic -> search -> pack), inputs drawn on
+    the GPU with the synthetic recipe: median of reps event-timed steps, each split into its
+    stages, with the fused kernel timed alone by the events awq_search_timed records.  gram: the
+    Gram-form search of the same layer as well (whole call)."""
+    X, W = synth.make_layer_device(spec, dev)
+    M, K, N = spec.M, spec.K, spec.N
+    a = torch.empty(K, dtype=torch.float32, device=dev)
+    ws_st = torch.empty(awq.stats_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    ws_se = torch.empty(awq.search_workspace_bytes(M, K, N), dtype=torch.uint8, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = (torch.empty((N, K // 8), dtype=torch.int32, device=dev),
+           torch.empty((N, K // 128), dtype=torch.float16, device=dev),
+           torch.empty((N, K // 128), dtype=torch.float16, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def one(ev):
+        ev[0].record(stream)
+        awq.stats(X, out=a, workspace=ws_st, flags=fl, check=False)
+        ev[1].record(stream)
+        r = awq.search(X, W, a, workspace=ws_se, flags=fl, check=False, fused_events=(ev[4], ev[5]))
+        ev[2].record(stream)
+        awq.pack(W, r.s_best, flags=fl, out=out, check=False)
+        ev[3].record(stream)
+        return r
+
+    def events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    one(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(reps)]
+    for ev in evs:
+        res = one(ev)
+    torch.cuda.synchronize()
+    awq.raise_for_flags(fl)
+    med = lambda i, j: statistics.median(ev[i].elapsed_time(ev[j]) for ev in evs)
+    step, fused = med(0, 3), med(4, 5)
+    flop = 20 * 2.0 * M * K * N
+    row = {"shape": [M, K, N], "dtype": spec.dtype, "step_ms": step, "stats_ms": med(0, 1),
+           "search_ms": med(1, 2), "fused_ms": fused, "pack_ms": med(2, 3),
+           "layer_searches_per_s": 1000.0 / step, "fused_tflops": flop / (fused * 1e-3) / 1e12,
+           "fused_frac": flop / (fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "step_tflops": flop / (step * 1e-3) / 1e12, "best_alpha": res.best_index / 20.0}
+    if gram:
+        ws_g = torch.empty(awq.search_workspace_bytes(M, K, N, gram=True), dtype=torch.uint8, device=dev)
+        call = lambda: awq.search(X, W, a, workspace=ws_g, flags=fl, check=False, gram=True)
+        g_ms = _time_reps(torch, call, reps)
+        awq.raise_for_flags(fl)
+        row["gram_search_ms"] = g_ms
+        row["gram_direct_equiv_tflops"] = flop / (g_ms * 1e-3) / 1e12
+        row["gram_speedup_vs_direct_search"] = row["search_ms"] / g_ms
+        del ws_g
+    del X, W, ws_se, ws_st, out
+    torch.cuda.empty_cache()
+    return row
+
+
+def per_config(torch, awq, dev):
+    """Every configuration's throughput beside the headline: tiny, attn, down and gate+up as one
+    layer each, and the decoder block as its four layers searched in turn (blocks/s), with the
+    Gram form as well for the block's K = 4096 layers (M = 16384 > 2K)."""
+    from post_weight_quantization_mean_amd import synth
+    reps = {"tiny": 20, "attn": 10, "down": 5, "gate_up": 3}
+    res = {}
+    for name in ("tiny", "attn", "down", "gate_up"):
+        spec = synth.CONFIGS[name].layers[0]
+        res[name] = layer_step(torch, awq, synth, spec, dev, reps[name])
+        if name in TARGET_HALF_PEAK:
+            res[name]["target_at_half_peak"] = TARGET_HALF_PEAK[name]
+    layers = {}
+    for spec in synth.CONFIGS["block"].layers:
+        layers[spec.name] = layer_step(torch, awq, synth, spec, dev, 3, gram=spec.K == 4096)
+    total = sum(r["step_ms"] for r in layers.values())
+    best = sum(r["stats_ms"] + r["pack_ms"] + min(r["search_ms"], r.get("gram_search_ms", float("inf")))
+               for r in layers.values())
+    flop = sum(20 * 2.0 * r["shape"][0] * r["shape"][1] * r["shape"][2] for r in layers.values())
+    res["block"] = {"layers": layers, "block_ms": total, "blocks_per_s": 1000.0 / total,
+                    "block_ms_with_gram": best, "blocks_per_s_with_gram": 1000.0 / best,
+                    "effective_tflops": flop / (total * 1e-3) / 1e12,
+                    "target_at_half_peak": TARGET_HALF_PEAK["block"]}
+    res["note"] = ("inputs drawn on the GPU with the synthetic recipe (dense-kernel cost does not depend on the "
+                   "values); step = stats + search + pack, medians of event-timed steps; fused_* is the fused "
+                   "search kernel alone; *_with_gram takes the Gram-form search where it is faster")
+    return res
+
+
+def clock_sample(torch, awq, dev, seconds=2.0, samples=3):
+    """The GPU clock while the fused search runs back to back: amd-smi's per-XCD gfx clocks,
+    sampled from a second thread during seconds of queued attn-layer searches."""
+    import subprocess
+    import threading
+    from post_weight_quantization_mean_amd import synth
+    spec = synth.CONFIGS["attn"].layers[0]
+    X, W = synth.make_layer_device(spec, dev)
+    a = awq.stats(X)
+    ws = torch.empty(awq.search_workspace_bytes(spec.M, spec.K, spec.N), dtype=torch.uint8, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    awq.search(X, W, a, workspace=ws, flags=fl, check=False)
+    torch.cuda.synchronize()
+    found, errors = [], []
+
+    def sampler():
+        time.sleep(0.3)
+        for _ in range(samples):
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                                     text=True, timeout=20)
+                found.extend(_gfx_clocks(json.loads(out.stdout)))
+            except Exception as e:  # amd-smi missing or its output changed: report, do not fail
+                errors.append(repr(e)[:200])
+            time.sleep(0.1)
+
+    t = threading.Thread(target=sampler)
+    t0 = time.perf_counter()
+    t.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds or t.is_alive():
+        for _ in range(50):
+            awq.search(X, W, a, workspace=ws, flags=fl, check=False)
+        n += 50
+        torch.cuda.synchronize()
+        if n > 20000:
+            break
+    t.join()
+    del X, W, ws
+    torch.cuda.empty_cache()
+    if not found:
+        return {"mhz": None, "source": "amd-smi", "errors": errors}
+    return {"mhz": statistics.median(found), "min_mhz": min(found), "max_mhz": max(found), "samples": len(found),
+            "source": "amd-smi metric --clock (median of the per-XCD gfx clocks) during back-to-back attn searches"}
+
+
+def _gfx_clocks(obj):
+    """Every gfx_<i>.clk value (MHz) in amd-smi's JSON, wherever it sits."""
+    vals = []
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                val = v["clk"].get("value")
+                if isinstance(val, (int, float)):
+                    vals.append(float(val))
+            else:
+                vals.extend(_gfx_clocks(v))
+    elif isinstance(obj, list):
+        for v in obj:
+            vals.extend(_gfx_clocks(v))
+    return vals
+
+
 def _time_reps(torch, fn, reps, flush=None):
     """Median of reps event-timed calls.  flush, when given, is a buffer larger than the
     last-level cache that is overwritten between calls (outside the timed intervals), so that
@@ -271,7 +404,8 @@ def main():
     ap.add_argument("--no-clip", action="store_true", help="skip the clipping-search timing")
     ap.add_argument("--no-w4a16", action="store_true", help="skip the W4A16 product timing")
     ap.add_argument("--no-fold", action="store_true", help="skip the scale-application timing")
-    ap.add_argument("--no-gram", action="store_true", help="skip the Gram-form search timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration throughput")
+    ap.add_argument("--no-clock", action="store_true", help="skip the GPU clock sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -373,8 +507,10 @@ def main():
         "effective_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "pct_mfma_peak": 100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_ms": {"stats": st_ms, "search": se_ms, "search_fused_kernel": fu_ms, "pack": pk_ms},
-        "stats_gbs": 2.0 * M * K / (st_ms * 1e-3) / 1e9,
-        "pack_gbs": 2.53125 * K * N / (pk_ms * 1e-3) / 1e9,
+        # the attn layer's X (32 MiB) and W fit in the 256 MB last-level cache: these rates are
+        # cache-resident; the `hbm` field times both kernels on larger inputs streamed from HBM
+        "stats_gbs_cache_resident": 2.0 * M * K / (st_ms * 1e-3) / 1e9,
+        "pack_gbs_cache_resident": 2.53125 * K * N / (pk_ms * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "search_pipelined_kernel (fused quantize + bf16 MFMA error product + "
@@ -392,8 +528,13 @@ def main():
         out["w4a16"] = w4a16_products(torch, awq, dev)
     if not args.no_fold:
         out["fold"] = fold_ops(torch, awq, dev)
-    if not args.no_gram:
-        out["gram"] = gram_form(torch, awq, dev)
+    if not args.no_configs:
+        out["configs"] = per_config(torch, awq, dev)
+    if not args.no_clock:
+        clk = clock_sample(torch, awq, dev)
+        out["gpu_clock"] = clk
+        if clk.get("mhz"):
+            out["roofline"]["frac_at_measured_clock"] = achieved / (PEAK_BF16_TFLOPS * clk["mhz"] / 2400.0)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -150,3 +150,27 @@ def to_f32(t: torch.Tensor) -> np.ndarray:
 
 def all_layers() -> List[Tuple[str, int]]:
     return [(c, i) for c, cfg in CONFIGS.items() for i in range(len(cfg.layers))]
+
+
+def make_layer_device(spec: LayerSpec, device, seed: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The same recipe drawn with torch's generator on ``device`` (fast for the full-size
+    benchmark layers, whose timing does not depend on the values).  The values differ from
+    make_x / make_w: this stream is not the numpy one, so parity tests use the CPU generator."""
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * seed + 7919 * spec.K + spec.N)
+    c = torch.exp(0.5 * torch.randn(spec.K, generator=g, device=device))
+    idx = torch.randperm(spec.K, generator=g, device=device)[:spec.n_out]
+    if spec.out_mult[0] == "const":
+        c[idx] *= spec.out_mult[1]
+    else:
+        lo, hi = spec.out_mult[1], spec.out_mult[2]
+        c[idx] *= lo + (hi - lo) * torch.rand(spec.n_out, generator=g, device=device)
+    if spec.x_kind == "sign":
+        x = torch.where(torch.rand((spec.M, spec.K), generator=g, device=device) < 0.5, -c, c)
+    else:
+        x = torch.randn((spec.M, spec.K), generator=g, device=device) * c
+        if spec.x_kind == "sparse":
+            x = torch.where(torch.rand((spec.M, spec.K), generator=g, device=device) < 0.7, 0.01 * x, x)
+    w = torch.randn((spec.N, spec.K), generator=g, device=device) * (1.0 / spec.K ** 0.5)
+    dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+    return x.to(dt), w.to(dt)
