@@ -90,8 +90,8 @@ def hbm_kernels(torch, awq, dev, reps: int = 10):
     """The two bandwidth-bound kernels at the largest shapes of the decoder-block workload:
     awq_stats on the MLP down-projection input X bf16 [16384 x 14336] (2 bytes per element
     read) and awq_pack on the fused gate+up weight W bf16 [28672 x 4096] (2 bytes read, 0.53125
-    written per weight).  Each call streams from HBM: a 512 MiB buffer is overwritten between
-    calls, so no input is left in the 256 MB last-level cache.  Seeded random values; the
+    written per weight).  Each call streams from HBM: a 512 MiB buffer is read between calls,
+    so no input is left in the 256 MB last-level cache.  Seeded random values; the
     kernels' cost does not depend on them."""
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -175,8 +175,9 @@ def fold_ops(torch, awq, dev, reps: int = 10):
 def w4a16_products(torch, awq, dev, reps: int = 10):
     """The W4A16 product over a packed artefact of the decoder block's fused gate+up weight
     (N = 28672, K = 4096): decode with one token (HBM-bound: 0.53125 bytes per weight, the
-    last-level cache flushed between calls) and prefill with 4096 tokens (MFMA-bound,
-    2 M K N flop).  The artefact is packed on the GPU from a seeded bf16 weight."""
+    last-level cache flushed between calls), decode with 1, 2, 4 and 8 tokens back to back over
+    eight such artefacts in one HIP graph, and prefill with 4096 tokens (MFMA-bound, 2 M K N
+    flop).  The artefacts are packed on the GPU from seeded bf16 weights."""
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     N, K = 28672, 4096
@@ -189,13 +190,36 @@ def w4a16_products(torch, awq, dev, reps: int = 10):
     y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
     ms_d = _time_reps(torch, lambda: awq.w4a16(x1, q, sc, zz, out=y1), reps, flush)
     bytes_d = N * K * 0.5 + N * (K // 128) * 4.0 + K * 2.0 + N * 4.0
+    # back to back, as consecutive layers of a model decode: eight artefacts (8 x 62.5 MB, more
+    # than the last-level cache), 32 calls captured in one HIP graph, so that neither a launch's
+    # host cost nor the fixed cost of timing one short launch with events is in the figure
+    arts = [(q, sc, zz)]
+    for _ in range(7):
+        Wi = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
+        arts.append(awq.pack(Wi, s))
+        del Wi
+    graph = {}
+    for m in (1, 2, 4, 8):
+        xm = torch.randn((m, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        ys = [torch.empty((m, N), dtype=torch.float32, device=dev) for _ in arts]
+        eager = [awq.w4a16(xm, *a) for a in arts]
+        ms = _graph_ms_per_call(torch, lambda: [awq.w4a16(xm, *a, out=y) for _ in range(4) for a, y in zip(arts, ys)],
+                                4 * len(arts), reps)
+        if not all(torch.equal(y, e) for y, e in zip(ys, eager)):
+            raise RuntimeError("w4a16 decode: graph replay differs from the eager call")
+        b = N * K * 0.5 + N * (K // 128) * 4.0 + m * K * 2.0 + m * N * 4.0
+        graph[str(m)] = {"ms": ms, "gbs": b / (ms * 1e-3) / 1e9, "frac_hbm": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del arts
     M = 4096
     xp = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     yp = torch.empty((M, N), dtype=torch.float32, device=dev)
     ms_p = _time_reps(torch, lambda: awq.w4a16(xp, q, sc, zz, out=yp), max(3, reps // 2))
     flop = 2.0 * M * K * N
     return {"decode": {"tokens": 1, "shape": [N, K], "ms": ms_d, "bytes": bytes_d,
-                       "gbs": bytes_d / (ms_d * 1e-3) / 1e9, "frac_hbm": bytes_d / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                       "gbs": bytes_d / (ms_d * 1e-3) / 1e9, "frac_hbm": bytes_d / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "note": "ms: one call, events around it, last-level cache flushed before it"},
+            "decode_in_graph": {"tokens": graph, "artefacts": 8, "calls": 32,
+                                "note": "per-call time of 32 back-to-back calls over 8 different artefacts, one HIP graph"},
             "prefill": {"tokens": M, "shape": [N, K], "ms": ms_p, "flop": flop,
                         "tflops": flop / (ms_p * 1e-3) / 1e12,
                         "frac_mfma_peak": flop / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
@@ -361,19 +385,47 @@ def _gfx_clocks(obj):
 
 def _time_reps(torch, fn, reps, flush=None):
     """Median of reps event-timed calls.  flush, when given, is a buffer larger than the
-    last-level cache that is overwritten between calls (outside the timed intervals), so that
-    every call reads its input from HBM."""
+    last-level cache that is read between calls (outside the timed intervals), so that every
+    call reads its input from HBM.  It is read, not overwritten: a fill leaves the cache full
+    of dirty lines, and the next call would pay for writing them back (a 28672 x 4096 pack
+    measured 59 us after a fill and 55 us after a read; a device copy 4.4 TB/s against 5.7)."""
     fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    words = flush.view(torch.int32) if flush is not None else None
     for e0, e1 in evs:
-        if flush is not None:
-            flush.zero_()
+        if words is not None:
+            words.amax()
         e0.record()
         fn()
         e1.record()
     torch.cuda.synchronize()
     return statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
+def _graph_ms_per_call(torch, fn, calls, reps):
+    """Median over reps replays of one HIP graph that holds fn's launches, per launch (calls of
+    them in fn).  fn runs once on a side stream before the capture (first-call set-up)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fn()
+    gr.replay()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) / calls)
+    return statistics.median(t)
 
 
 def copy_probe(mib: int, reps: int):

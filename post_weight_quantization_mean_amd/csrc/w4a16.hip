@@ -37,14 +37,8 @@ template <int C>
 __device__ __forceinline__ float ubyte(uint32_t x) { return (float)((x >> (8 * C)) & 0xffu); }
 
 // ---- decode ------------------------------------------------------------------------------
-#ifndef AWQ_GV_ROWS
-#define AWQ_GV_ROWS 4
-#endif
-constexpr int kGvRows = AWQ_GV_ROWS;  // weight rows per wave step
-#ifndef AWQ_GV_WORD_OUTER
-#define AWQ_GV_WORD_OUTER 2
-#endif
-constexpr int kGvWordOuter = AWQ_GV_WORD_OUTER;  // bf16 decode: up to this many tokens, word-outer order
+constexpr int kGvRows = 4;       // weight rows per wave step (fp32 activations)
+constexpr int kGvWordOuter = 2;  // bf16 decode: up to this many tokens, word-outer order
 constexpr int kGvThreads = 256;
 
 // K is covered in passes of kc channels (4096 for up to two tokens, else 2048): X of the pass
@@ -196,7 +190,8 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
 // quarter group: sum x q - z sum x = sum x (128 + q) - (128 + z) sum x.  Products are exact;
 // the sums carry the bias, so their rounding is relative to sum |x| (128 + q), about 2^7 times
 // the unbiased sum's (still far below the bf16 precision of the activations).
-template <int M>
+// R weight rows per wave step: 2 for one or two tokens, 4 for more (see the launch).
+template <int M, int R>
 __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
@@ -215,7 +210,7 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
   // wave-uniform row bookkeeping lives in scalar registers, so row addresses cost no VALU
   const int64_t wave = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * kGvThreads + threadIdx.x) >> 6));
   const int64_t nwaves = ((int64_t)gridDim.x * kGvThreads) >> 6;
-  const int64_t step = nwaves * kGvRows;
+  const int64_t step = nwaves * R;
   auto dot = [](uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfx2, a), __builtin_bit_cast(bfx2, b), c, false);
   };
@@ -224,13 +219,13 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
   uint32_t bias;
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias));
   struct Slab {
-    u32x4 q[kGvRows];
-    uint16_t d[kGvRows], z[kGvRows];  // fp16 bits: converted where used, so that nothing
+    u32x4 q[R];
+    uint16_t d[R], z[R];  // fp16 bits: converted where used, so that nothing
                                       // waits for the prefetch before the current math
   };
   // this wave's row groups n0 = R wave + i step (i < nrg), each in segs segments per pass: the
   // items (row group, segment) in that order, three slabs in a ring, two items in flight
-  const int64_t first = wave * kGvRows;
+  const int64_t first = wave * R;
   const int64_t nrg = first < N ? (N - 1 - first) / step + 1 : 0;
   for (int64_t c0 = 0; c0 < K; c0 += kc) {
     const int64_t kw = K - c0 < kc ? K - c0 : kc;  // a multiple of 128
@@ -244,7 +239,7 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
       const int w0 = lw < pw ? lw : 0;                      // word within the pass
       const int g = (int)((c0 + 8 * (int64_t)w0) / kGroup);  // group of those words
 #pragma unroll
-      for (int r = 0; r < kGvRows; ++r) {
+      for (int r = 0; r < R; ++r) {
         const int64_t n = fn0 + r < N ? fn0 + r : N - 1;
         const int32_t* rowp = qweight + n * words + c0 / 8;
         S.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + w0));
@@ -293,12 +288,12 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
       }
     }
     __syncthreads();
-    float acc[kGvRows][M];
+    float acc[R][M];
     int64_t pn0 = first, pt = 0;  // cursor of the next item to process
     auto process = [&](const Slab& S) {
       if (pt == 0) {
 #pragma unroll
-        for (int r = 0; r < kGvRows; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
       }
@@ -316,26 +311,26 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
           const f32x4 s4 = xs4[(m * (kc / 8) + lw) / 4];
           const float sxm = (s4.x + s4.y) + (s4.z + s4.w);  // sum of the lane's 32 activations
 #pragma unroll
-          for (int r = 0; r < kGvRows; ++r)
+          for (int r = 0; r < R; ++r)
             acc[r][m] = fmaf(h2f(S.d[r]), fmaf(-(128.0f + h2f(S.z[r])), sxm, sq[r]), acc[r][m]);
         };
         if constexpr (M <= kGvWordOuter) {
           // few tokens: word by word, so that only one word's pairs are live
-          float sq[M][kGvRows];
+          float sq[M][R];
 #pragma unroll
           for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int r = 0; r < kGvRows; ++r) sq[m][r] = 0.0f;
+            for (int r = 0; r < R; ++r) sq[m][r] = 0.0f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            uint32_t qp[kGvRows][4];
+            uint32_t qp[R][4];
 #pragma unroll
-            for (int r = 0; r < kGvRows; ++r) pairs(r, j, qp[r]);
+            for (int r = 0; r < R; ++r) pairs(r, j, qp[r]);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
               const u32x4 x4 = xq[m * (kc / 8) + lw + j];
 #pragma unroll
-              for (int r = 0; r < kGvRows; ++r) {
+              for (int r = 0; r < R; ++r) {
                 sq[m][r] = dot(x4.x, qp[r][0], sq[m][r]);
                 sq[m][r] = dot(x4.y, qp[r][1], sq[m][r]);
                 sq[m][r] = dot(x4.z, qp[r][2], sq[m][r]);
@@ -347,21 +342,21 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
           for (int m = 0; m < M; ++m) finish(m, sq[m]);
         } else {
           // more tokens: all pairs once, then token by token
-          uint32_t qp[kGvRows][4][4];
+          uint32_t qp[R][4][4];
 #pragma unroll
-          for (int r = 0; r < kGvRows; ++r)
+          for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int j = 0; j < 4; ++j) pairs(r, j, qp[r][j]);
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            float sq[kGvRows];
+            float sq[R];
 #pragma unroll
-            for (int r = 0; r < kGvRows; ++r) sq[r] = 0.0f;
+            for (int r = 0; r < R; ++r) sq[r] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const u32x4 x4 = xq[m * (kc / 8) + lw + j];
 #pragma unroll
-              for (int r = 0; r < kGvRows; ++r) {
+              for (int r = 0; r < R; ++r) {
                 sq[r] = dot(x4.x, qp[r][j][0], sq[r]);
                 sq[r] = dot(x4.y, qp[r][j][1], sq[r]);
                 sq[r] = dot(x4.z, qp[r][j][2], sq[r]);
@@ -374,7 +369,7 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
       }
       if (pt + 1 == segs) {  // row group done: sum over the wave's lanes, one row and token at a time
 #pragma unroll
-        for (int r = 0; r < kGvRows; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int m = 0; m < M; ++m) {
             const float v = wave_sum(acc[r][m]);
@@ -635,14 +630,18 @@ __global__ __launch_bounds__(64 * NW, 1) void w4a16_gemm_kernel(
 
 }  // namespace
 
-// decode grid: one wave per row group, at most what is resident at once (every wave then
-// starts at the launch and loads its first rows while X is staged).  The resident count is a
-// property of the device and of the kernel instantiation (its LDS size is fixed by its token
-// count), so it is queried once per device and kept: a decode launch costs ~20 us and the
-// occupancy query is not free.  The cache packs (LDS bytes, resident blocks) in one word; two
-// threads that race on the first call store the same value.
+// decode grid: one wave per row group, at most what is resident at once and at most
+// max_per_cu blocks per CU (every wave then starts at the launch and loads its first rows while
+// X is staged).  Fewer blocks sweeping the weight as a moving window stream it faster than a
+// wave per row group: back to back over eight 28672 x 4096 artefacts, one token took 15.2 us
+// per call at four blocks per CU and 16.4 us at all that is resident (eight); four tokens 26 us
+// at two blocks per CU against 30 us.  The resident count is a property of the device and of
+// the kernel instantiation (its LDS size is fixed by its token count), so it is queried once
+// per device and kept: a decode launch costs ~15 us and the occupancy query is not free.  The
+// cache packs (LDS bytes, resident blocks per CU, CUs) in one word; two threads that race on
+// the first call store the same value.
 template <typename Kern>
-int64_t gemv_blocks(Kern kern, size_t lds, int64_t waves) {
+int64_t gemv_blocks(Kern kern, size_t lds, int64_t waves, int max_per_cu) {
   constexpr int kMaxDevices = 64;
   static std::atomic<uint64_t> cache[kMaxDevices];
   int dev = 0;
@@ -655,10 +654,11 @@ int64_t gemv_blocks(Kern kern, size_t lds, int64_t waves) {
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kGvThreads, lds) != hipSuccess || per_cu < 1)
       per_cu = 1;
-    packed = ((uint64_t)lds << 32) | (uint64_t)((int64_t)cus * per_cu);
+    packed = ((uint64_t)lds << 32) | ((uint64_t)(per_cu < 255 ? per_cu : 255) << 24) | (uint64_t)(cus & 0xffffff);
     if (slot) slot->store(packed, std::memory_order_relaxed);
   }
-  const int64_t resident = (int64_t)(packed & 0xffffffffu);
+  const int64_t per_cu = (int64_t)((packed >> 24) & 0xff), cus = (int64_t)(packed & 0xffffff);
+  const int64_t resident = cus * (per_cu < max_per_cu ? per_cu : max_per_cu);
   const int64_t need = (waves + kGvThreads / 64 - 1) / (kGvThreads / 64);
   return need < resident ? need : resident;
 }
@@ -678,7 +678,6 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
     return hipGetLastError();
   }
   // decode path, up to 8 tokens per launch (fp32 X always takes it)
-  const int64_t waves = (N + kGvRows - 1) / kGvRows;
   for (int64_t m0 = 0; m0 < M; m0 += kW4a16GemvMax) {
     const int64_t mb = M - m0 < kW4a16GemvMax ? M - m0 : kW4a16GemvMax;
     const char* xp = static_cast<const char*>(X) + m0 * ldx * (xf32 ? 4 : 2);
@@ -689,13 +688,16 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
 #define AWQ_GV(MV)                                                                                       \
   do {                                                                                                   \
     if (!xf32) {                                                                                         \
+      constexpr int RV = MV <= 2 ? 2 : 4;                                                                \
       const size_t ldsd = (size_t)mb * kcd * 5 / 2;                                                      \
-      const int64_t blocks = gemv_blocks(w4a16_gemv_dot_kernel<MV>, ldsd, waves);                        \
-      w4a16_gemv_dot_kernel<MV><<<(unsigned)blocks, kGvThreads, ldsd, st>>>(                             \
+      const int64_t blocks = gemv_blocks(w4a16_gemv_dot_kernel<MV, RV>, ldsd, (N + RV - 1) / RV,         \
+                                         MV <= 2 ? 4 : 2);                                               \
+      w4a16_gemv_dot_kernel<MV, RV><<<(unsigned)blocks, kGvThreads, ldsd, st>>>(                         \
           static_cast<const uint16_t*>(static_cast<const void*>(xp)), ldx, K, qweight, scales, zeros, N, \
           yp, ldy, kcd);                                                                                 \
     } else {                                                                                             \
-      const int64_t blocks = gemv_blocks(w4a16_gemv_kernel<MV, true>, lds, waves);                       \
+      const int64_t blocks = gemv_blocks(w4a16_gemv_kernel<MV, true>, lds, (N + kGvRows - 1) / kGvRows,  \
+                                         64);                                                            \
       w4a16_gemv_kernel<MV, true><<<(unsigned)blocks, kGvThreads, lds, st>>>(xp, ldx, K, qweight, scales, \
                                                                             zeros, N, yp, ldy, kc);      \
     }                                                                                                    \

@@ -165,3 +165,28 @@ def test_prefill_full_size_sampled(awq):
     X64 = X.float().numpy().astype(np.float64)[rows]
     frac = check(Ys, X64, sub, prefill=True, biased=False)
     print(f"[gpu-case] full-size prefill sample: largest error {frac:.3f} of its tolerance", flush=True)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5])
+def test_decode_full_size_sampled(awq, M):
+    """The decode in the shape the benchmark times: M bf16 tokens against a 28672 x 4096
+    artefact (synthetic: uniformly random code words, positive fp16 scales, integer zeros).  The
+    grid sweeps the rows several times (each wave owns several row groups), so every wave's
+    later rows are covered; a sample of 256 outputs (the first and last rows included) is
+    checked against the oracle."""
+    banner(f"w4a16 decode full size M={M} x 28672 x 4096, sampled")
+    K, N = 4096, 28672
+    rng = np.random.default_rng(20 + M)
+    art = {"qweight": rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint32).view(np.int32),
+           "scales": (np.abs(rng.standard_normal((N, K // 128))) * 0.01 + 1e-3).astype(np.float16),
+           "zeros": rng.integers(0, 16, size=(N, K // 128)).astype(np.float16)}
+    X = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    sc = torch.from_numpy(art["scales"]).to(DEV)
+    zz = torch.from_numpy(art["zeros"]).to(DEV)
+    Y = awq.w4a16(X.to(DEV), q, sc, zz)
+    cols = np.unique(np.concatenate([rng.choice(N, 254, replace=False), [0, N - 1]]))
+    Ys = Y[:, torch.from_numpy(cols).to(DEV)].cpu().numpy().astype(np.float64)
+    sub = {k: v[cols] for k, v in art.items()}
+    frac = check(Ys, X.float().numpy().astype(np.float64), sub, prefill=False, biased=True)
+    print(f"[gpu-case] full-size decode M={M} sample: largest error {frac:.3f} of its tolerance", flush=True)
