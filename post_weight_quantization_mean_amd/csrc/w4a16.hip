@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
 // itself; the codes of kMfDepth groups are in flight per wave.
 constexpr int kMfDepth = 4;     // group pairs per round (8 groups)
 constexpr int kMfPerCu = 4;     // blocks per CU of the matrix-core decode (2 measured the same)
-constexpr int kMfMinTokens = 3;  // fewer tokens: the dot kernel (faster at one and two tokens)
+constexpr int kMfMinTokens = 2;  // fewer tokens: the dot kernel (faster at one token)
 
 __device__ __forceinline__ int mf_pitch(int64_t kc) { return (int)(kc / 2) + 4; }  // uint32 per token row (padded: no bank conflict across tokens)
 
@@ -422,10 +422,12 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int M, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
     float* __restrict__ Y, int64_t ldy, int64_t kc) {
-  // LDS: [M][kc / 2 + 4] activation pairs, then [kc / 128][16] fp32 group sums (16 token slots)
+  // LDS: [M][kc / 2 + 4] activation pairs, then [kc / 128][16] fp32 group sums (16 token slots),
+  // then each wave's round of codes [16 rows][128 words]
   extern __shared__ __attribute__((aligned(16))) uint32_t xp[];
   const int pitch = mf_pitch(kc);
   float* gsum = reinterpret_cast<float*>(xp + (int64_t)M * pitch);
+  uint32_t* wcodes = xp + (int64_t)M * pitch + (kc / kGroup) * 16 + (threadIdx.x >> 6) * (16 * 128);
   typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
   const int64_t G = K / kGroup, words = K / 8;
   const int lane = threadIdx.x & 63, tk = lane & 15, ch = lane >> 4;
@@ -469,40 +471,53 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_mfma_kernel(
     for (int64_t tile = wave; tile < tiles; tile += nwaves) {
       const int64_t n = 16 * tile + tk;                 // this lane's weight row
       const int64_t nl = n < N ? n : N - 1;             // rows past N: load row N - 1, store nothing
-      const int32_t* wrow = qweight + nl * words + c0 / 8 + 4 * ch;
       const uint16_t* drow = scales + nl * G + c0 / kGroup;
       const uint16_t* zrow = zeros + nl * G + c0 / kGroup;
-      // Rounds of 8 groups (kMfDepth pairs (g, g + 1)).  A lane's 16 bytes of a pair's two groups
-      // lie 64 bytes apart, so the wave reads both halves of each row's 128-byte line at once; the
-      // row's fp16 scales and zeros of a round are one 16-byte load each (a 2-byte load per group
-      // made most of the kernel's memory requests and took it from 15 to 31 us).  The codes of
-      // the next round and its scales and zeros are in flight while a round is multiplied.
-      // Tiles start at different rounds (rot), so that waves do not all read the same 128 bytes
-      // of rows 2 KiB apart at once; the sum over groups is then taken in a rotated order, fixed
-      // per tile.
+      // Rounds of 8 groups: the tile's 16 rows x 512 bytes of codes.  The wave loads a round as
+      // eight instructions of two rows each, whole 128-byte lines (lane l: row 2 i + l / 32,
+      // 16-byte piece l % 32), and passes it through its own 8 KiB of LDS into the product's
+      // layout (lane: row tk, piece 4 g + ch of the round's group g); the row's fp16 scales and
+      // zeros of a round are one 16-byte load each.  Loading each lane's pieces directly touched
+      // twice the lines per instruction and took the kernel from 14.6 to 18.8 us (one token).
+      // Pieces are stored at piece ^ (row % 16), which keeps both the stores (8 lanes, one row)
+      // and the reads (16 lanes, 16 rows) free of bank conflicts.  The codes of the next round
+      // and its scales and zeros are in flight while a round is multiplied.  Tiles start at
+      // different rounds (rot), so that waves do not all read the same bytes of rows 2 KiB apart
+      // at once; the sum over groups is then taken in a rotated order, fixed per tile.
       const int rounds = gpp / (2 * kMfDepth);  // the pass width is a multiple of 1024 channels
       const int rot = (int)((tile * 5) % rounds);
       auto round_of = [&](int r) { return r + rot < rounds ? r + rot : r + rot - rounds; };
-      u32x4 cq[kMfDepth][2];
+      u32x4 cq[2 * kMfDepth];
       u32x4 sdc, szc, sdn, szn;  // this and the next round's 8 scales and zeros (fp16 bits)
-      // round r's pair s into slot s (r clamped: a harmless reload).  The scheduling barrier keeps
-      // the pairs' loads in issue order, so that the wait before a pair's products is for that
-      // pair's loads and not for those issued after it.
-      auto fetch = [&](int slot, int r, u32x4* sd, u32x4* sz) {
+      const int lrow = lane >> 5, lpc = lane & 31;  // load layout: row 2 i + lrow, piece lpc
+      // round r into cq (r clamped: a harmless reload); the scheduling barrier keeps rounds'
+      // loads in issue order, so that the wait before a round's stores is for that round only
+      auto fetch = [&](int r, u32x4* sd, u32x4* sz) {
         const int g0 = 2 * kMfDepth * round_of(r < rounds ? r : rounds - 1);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          cq[slot][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + 16 * (g0 + 2 * slot + h)));
-        if (sd) {
-          *sd = *reinterpret_cast<const u32x4*>(drow + g0);
-          *sz = *reinterpret_cast<const u32x4*>(zrow + g0);
+        for (int ii = 0; ii < 2 * kMfDepth; ++ii) {
+          const int64_t rr = 16 * tile + 2 * ii + lrow;
+          const int64_t rl = rr < N ? rr : N - 1;
+          cq[ii] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(qweight + rl * words + c0 / 8 + 16 * g0 + 4 * lpc));
         }
+        *sd = *reinterpret_cast<const u32x4*>(drow + g0);
+        *sz = *reinterpret_cast<const u32x4*>(zrow + g0);
         __builtin_amdgcn_sched_barrier(0);
+      };
+      auto stash = [&] {  // cq -> this wave's LDS round, swizzled
+#pragma unroll
+        for (int ii = 0; ii < 2 * kMfDepth; ++ii) {
+          const int row = 2 * ii + lrow;
+          *reinterpret_cast<u32x4*>(wcodes + row * 128 + 4 * (lpc ^ (row & 15))) = cq[ii];
+        }
       };
       float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       // groups gg and gg + 1 (codes w0, w1; fp16 scale and zero bits in the low / high halves of
       // dw, zw): two independent chains of four products, interleaved
-      auto consume2 = [&](const u32x4 w0, const u32x4 w1, uint32_t dw, uint32_t zw, int gg) {
+      auto consume2 = [&](int gr, uint32_t dw, uint32_t zw, int gg) {  // round groups gr, gr + 1
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(wcodes + tk * 128 + 4 * ((4 * gr + ch) ^ tk));
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(wcodes + tk * 128 + 4 * ((4 * gr + 4 + ch) ^ tk));
         f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
         const uint32_t wj[2][4] = {{w0.x, w0.y, w0.z, w0.w}, {w1.x, w1.y, w1.z, w1.w}};
 #pragma unroll
@@ -527,20 +542,14 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_mfma_kernel(
           y[3] = fmaf(dv, fmaf(-zb, sg.w, acc[h][3]), y[3]);
         }
       };
-      fetch(0, 0, &sdc, &szc);
-#pragma unroll
-      for (int sl = 1; sl < kMfDepth; ++sl) fetch(sl, 0, nullptr, nullptr);
+      fetch(0, &sdc, &szc);
       for (int r = 0; r < rounds; ++r) {
         const int g0 = 2 * kMfDepth * round_of(r);
+        stash();  // round r's codes into LDS (this wave only; a wave's LDS accesses keep their order)
         const uint32_t dw[4] = {sdc.x, sdc.y, sdc.z, sdc.w}, zw[4] = {szc.x, szc.y, szc.z, szc.w};
+        fetch(r + 1, &sdn, &szn);
 #pragma unroll
-        for (int sl = 0; sl < kMfDepth; ++sl) {
-          consume2(cq[sl][0], cq[sl][1], dw[sl], zw[sl], g0 + 2 * sl);  // groups g0 + 2 sl, + 1
-          if (sl == 0)
-            fetch(0, r + 1, &sdn, &szn);
-          else
-            fetch(sl, r + 1, nullptr, nullptr);
-        }
+        for (int sl = 0; sl < kMfDepth; ++sl) consume2(2 * sl, dw[sl], zw[sl], g0 + 2 * sl);  // groups g0 + 2 sl, + 1
         sdc = sdn;
         szc = szn;
       }
@@ -827,15 +836,18 @@ int64_t gemv_blocks(Kern kern, size_t lds, int64_t waves, int max_per_cu) {
 int64_t w4a16_gemv_kc(int64_t M) { return M <= 2 ? 4096 : 2048; }
 
 // channels per pass of the matrix-core decode and its LDS bytes: the widest multiple of 1024
-// channels (whole rounds of kMfDepth groups) whose pairs and group sums fit in 72 KiB (two
-// blocks per CU), at most K
+// channels (whole rounds of kMfDepth groups) whose pairs and group sums fit, beside the four
+// waves' 8 KiB code rounds, in 104 KiB, at most K.  (At 72 KiB, two blocks per CU, eight tokens
+// took two K passes of 4096 channels and 22.9 us per call against 21.5 in one pass.)
+size_t w4a16_mfma_lds(int64_t M, int64_t kc) {
+  return (size_t)(M * (kc / 2 + 4) * 4 + (kc / kGroup) * 64 + (kGvThreads / 64) * 16 * 128 * 4);
+}
 int64_t w4a16_mfma_kc(int64_t M, int64_t K) {
   int64_t kc = K < 32768 ? K : 32768;
   if (kc > 1024) kc -= kc % 1024;
-  while (kc > 1024 && M * (kc / 2 + 4) * 4 + (kc / kGroup) * 64 > 72 * 1024) kc -= 1024;
+  while (kc > 1024 && w4a16_mfma_lds(M, kc) > 104 * 1024) kc -= 1024;
   return kc;
 }
-size_t w4a16_mfma_lds(int64_t M, int64_t kc) { return (size_t)(M * (kc / 2 + 4) * 4 + (kc / kGroup) * 64); }
 
 hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, float* Y, int64_t ldy,
@@ -848,11 +860,11 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
         static_cast<const uint16_t*>(X), M, ldx, K, qweight, scales, zeros, N, Y, ldy, ntiles, tiles, per_xcd);
     return hipGetLastError();
   }
-  // decode path, up to 8 tokens per launch (fp32 X always takes it).  bf16 X with three or more
+  // decode path, up to 8 tokens per launch (fp32 X always takes it).  bf16 X with two or more
   // tokens goes to the matrix cores when its rounds of 8 groups line up: K a multiple of 1024 and
   // 16-byte aligned scales and zeros (their 16-byte loads); otherwise to the dot kernel.  Back to
-  // back over eight 28672 x 4096 artefacts: 4 tokens 19.7 us per call against 26.0 us on the dot
-  // kernel, 8 tokens 21.2 against 40.4; 1 and 2 tokens 18.9 and 19.0 against 14.8 and 18.6.
+  // back over eight 28672 x 4096 artefacts, per call: 2 tokens 16.9 us against 18.6 on the dot
+  // kernel, 4 tokens 17.5 against 26.0, 8 tokens 21.5 against 40.4; one token 17.3 against 14.7.
   const bool mfma_ok = K % 1024 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15u) == 0 &&
                        (reinterpret_cast<uintptr_t>(zeros) & 15u) == 0;
   for (int64_t m0 = 0; m0 < M; m0 += kW4a16GemvMax) {

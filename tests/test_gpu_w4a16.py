@@ -65,10 +65,10 @@ def check(Y, X64, art, prefill, biased):
     return float(np.max(err / (tol + 1e-30)))  # the largest error as a fraction of its tolerance
 
 
-# dot kernel: 1-2 tokens, or K not a multiple of 1024; matrix-core kernel: 3-8 tokens with K a
-# multiple of 1024 (3 x 14336: two K passes; ragged last tiles of 16 rows)
+# dot kernel: one token, or K not a multiple of 1024; matrix-core kernel: 2-8 tokens with K a
+# multiple of 1024 (8 x 14336: two K passes; ragged last tiles of 16 rows)
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 256), (3, 14336, 130), (8, 384, 64), (2, 5120, 4),
-                                   (4, 2048, 33), (6, 3072, 50), (8, 4096, 100)])
+                                   (4, 2048, 33), (6, 3072, 50), (8, 4096, 100), (8, 14336, 70)])
 def test_decode_bf16(awq, M, K, N):
     banner(f"w4a16 decode M={M} K={K} N={N}")
     art = artefact(N, K, 1)
