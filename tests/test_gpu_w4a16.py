@@ -193,3 +193,25 @@ def test_decode_full_size_sampled(awq, M):
     sub = {k: v[cols] for k, v in art.items()}
     frac = check(Ys, X.float().numpy().astype(np.float64), sub, prefill=False, biased=True)
     print(f"[gpu-case] full-size decode M={M} sample: largest error {frac:.3f} of its tolerance", flush=True)
+
+
+def test_decode_unaligned_scales_take_the_dot_kernel(awq):
+    """The matrix-core decode reads scales and zeros 16 bytes at a time; tensors that are only
+    2-byte aligned (a contiguous view one element into a buffer) go to the dot kernel instead, with
+    the same result bound, for several token counts."""
+    banner("w4a16 decode, scales and zeros 2-byte aligned")
+    N, K = 96, 2048
+    art = artefact(N, K, 4)
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    G = K // 128
+    sbuf = torch.empty(N * G + 1, dtype=torch.float16, device=DEV)
+    zbuf = torch.empty(N * G + 1, dtype=torch.float16, device=DEV)
+    sc = sbuf[1:].view(N, G)
+    zz = zbuf[1:].view(N, G)
+    sc.copy_(torch.from_numpy(art["scales"].view(np.float16)))
+    zz.copy_(torch.from_numpy(art["zeros"].view(np.float16)))
+    assert sc.data_ptr() % 16 != 0 and zz.data_ptr() % 16 != 0
+    for M in (1, 2, 5):
+        X = torch.from_numpy(np.random.default_rng(30 + M).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+        Y = awq.w4a16(X.to(DEV), q, sc, zz).cpu().numpy().astype(np.float64)
+        check(Y, X.float().numpy().astype(np.float64), art, prefill=False, biased=True)
