@@ -50,9 +50,9 @@ __device__ __forceinline__ int gd_swz(int row) { return 2 * (row & 3); }
 
 // NST stages of TT tokens (LDS: NST x 2 x TT x 256 bytes).  Measured on the 16384 x 4096 X of
 // the decoder block (528 tiles): 4 stages of 64 tokens (one block per CU) 382 us; 3, 4 or 5
-// stages of 32 tokens (two blocks per CU) 426-439 us; 3 of 64, 474 us.  The register-transposing
-// kernel this replaces (each thread loaded an 8 x 8 block of X and stored channel rows into LDS)
-// took 590 us.  What bounds it now is the LDS traffic: a 64 x 64 wave tile reads one 32 x 16
+// stages of 32 tokens (two blocks per CU) 426-439 us; 3 of 64, 474 us.  A kernel that transposed X
+// in registers instead (each thread loaded an 8 x 8 block of X and stored channel rows into LDS)
+// took 590 us.  What bounds this one is the LDS traffic: a 64 x 64 wave tile reads one 32 x 16
 // operand per product, eight bytes per lane per transposed read.
 template <int NST, int TT>
 __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gram_dma_kernel(

@@ -400,18 +400,19 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_dot_kernel(
 }
 
 // bf16 activations on the matrix cores: v_mfma_f32_16x16x32_bf16 with the tokens as its 16
-// rows (M of them real, the rest zero) and 16 weight rows as its 16 columns.  Lane l supplies
-// the A operand of token l % 16 and the B operand of weight row n0 + l % 16, both for its
-// k-chunk c = l / 16: in MFMA j of a group, chunk c stands for word 4 c + j of the group (a
-// fixed permutation of the sum over k, the same on both operands), so a lane's four words of a
-// group are 16 contiguous bytes, one load.  Each word becomes four biased bf16 pairs
-// (q_i, q_{i+4}) + 128, as in the dot kernel, against activation pairs (x_i, x_{i+4}) staged in
-// LDS; the MFMA sums the group's 128 exact products in fp32, and the group's scale and zero come
-// off once per group: Delta (sum x (128 + q) - (128 + z) sum x), with sum x per (token, group)
-// staged beside the pairs.  The VALU work per code (the pair building, about 0.9 instructions,
-// and the epilogue) no longer grows with the tokens, where the dot kernel spends one
-// instruction per two products.  A wave owns 16 whole rows (all of K), so it writes its outputs
-// itself; the codes of kMfDepth groups are in flight per wave.
+// rows (M of them real; the rest repeat a staged token and are never stored) and 16 weight rows
+// as its 16 columns.  Lane l supplies the A operand of token l % 16 and the B operand of weight
+// row n0 + l % 16, both for its k-chunk c = l / 16: in MFMA j of a group, chunk c stands for
+// word 4 c + j of the group (a fixed permutation of the sum over k, the same on both operands),
+// so a lane's four words of a group are 16 contiguous bytes of the row.  Each word becomes four
+// biased bf16 pairs (q_i, q_{i+4}) + 128, as in the dot kernel, against activation pairs
+// (x_i, x_{i+4}) staged in LDS; the MFMA sums the group's 128 exact products in fp32, and the
+// group's scale and zero come off once per group: Delta (sum x (128 + q) - (128 + z) sum x),
+// with sum x per (token, group) staged beside the pairs.  The VALU work per code (the pair
+// building, about 0.9 instructions, and the epilogue) no longer grows with the tokens, where the
+// dot kernel spends one instruction per two products.  A wave owns 16 whole rows (all of K), so
+// it writes its outputs itself; the codes of the next round of 8 groups are in flight while a
+// round is multiplied.
 constexpr int kMfDepth = 4;     // group pairs per round (8 groups)
 constexpr int kMfPerCu = 4;     // blocks per CU of the matrix-core decode (2 measured the same)
 constexpr int kMfMinTokens = 2;  // fewer tokens: the dot kernel (faster at one token)
@@ -428,7 +429,6 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_mfma_kernel(
   const int pitch = mf_pitch(kc);
   float* gsum = reinterpret_cast<float*>(xp + (int64_t)M * pitch);
   uint32_t* wcodes = xp + (int64_t)M * pitch + (kc / kGroup) * 16 + (threadIdx.x >> 6) * (16 * 128);
-  typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
   const int64_t G = K / kGroup, words = K / 8;
   const int lane = threadIdx.x & 63, tk = lane & 15, ch = lane >> 4;
   const int64_t wave = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * kGvThreads + threadIdx.x) >> 6));
