@@ -215,3 +215,13 @@ def test_decode_unaligned_scales_take_the_dot_kernel(awq):
         X = torch.from_numpy(np.random.default_rng(30 + M).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
         Y = awq.w4a16(X.to(DEV), q, sc, zz).cpu().numpy().astype(np.float64)
         check(Y, X.float().numpy().astype(np.float64), art, prefill=False, biased=True)
+
+
+# matrix-core decode edges: one row, rows around one 16-row tile, one 1024-channel round, five
+# rounds (tiles start at rotated rounds), 257 tiles with a partial last one
+@pytest.mark.parametrize("M,K,N", [(2, 1024, 1), (3, 1024, 15), (8, 1024, 17), (5, 5120, 33), (2, 3072, 4100)])
+def test_decode_mfma_edges(awq, M, K, N):
+    banner(f"w4a16 decode (matrix cores) M={M} K={K} N={N}")
+    art = artefact(N, K, 5)
+    X = torch.from_numpy(np.random.default_rng(40 + M).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    run(awq, art, X, prefill=False)
