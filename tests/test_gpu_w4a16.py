@@ -170,13 +170,14 @@ def test_prefill_full_size_sampled(awq):
     print(f"[gpu-case] full-size prefill sample: largest error {frac:.3f} of its tolerance", flush=True)
 
 
-@pytest.mark.parametrize("M", [1, 2, 5])
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_decode_full_size_sampled(awq, M):
     """The decode in the shape the benchmark times: M bf16 tokens against a 28672 x 4096
     artefact (synthetic: uniformly random code words, positive fp16 scales, integer zeros).  The
-    grid sweeps the rows several times (each wave owns several row groups), so every wave's
-    later rows are covered; a sample of 256 outputs (the first and last rows included) is
-    checked against the oracle."""
+    grid sweeps the rows several times (one token: each wave owns several row groups; eight
+    tokens: one block per CU, so waves loop over several 16-row tiles), so every wave's later rows
+    are covered; a sample of 256 outputs (the first and last rows included) is checked against the
+    oracle."""
     banner(f"w4a16 decode full size M={M} x 28672 x 4096, sampled")
     K, N = 4096, 28672
     rng = np.random.default_rng(20 + M)
