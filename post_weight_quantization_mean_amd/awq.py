@@ -229,7 +229,7 @@ def search(X: torch.Tensor, W, a: torch.Tensor, group_size: int = GROUP, n_grid:
     (awq_search_multi), all of one dtype.
 
     ``gram``: evaluate the losses in the Gram form sum_n E[n] (X^T X) E[n]^T (awq_search_gram;
-    bf16 X and a single bf16 W): cheaper when M > 2K, equal up to rounding.
+    bf16 X and a single bf16 W): cheaper when M > K + 512, equal up to rounding.
 
     ``fused_events``: two timing events that the library records right before and after the
     fused candidate kernel (awq_search_timed), so that ``e0.elapsed_time(e1)`` is that

@@ -130,7 +130,10 @@ hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx,
                                bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
                                const float2* sr_tab, const float2* params, int n_grid,
                                const SearchPlan& plan, double* partial, hipStream_t st, bool gram = false);
-// Gram form: Gs bf16 [2K, K] = [bf16(G); bf16(G - bf16(G))], G = X^T X for bf16 X [M, K]
+// Gram form: Gs bf16 [2K, K] = [bf16(G); bf16(G - bf16(G))], G = X^T X for bf16 X [M, K];
+// when gram_triangular(K), G there stands for T = diag(X^T X) + 2 triu(X^T X, 1) (zero below
+// the diagonal), and each candidate block's K loop starts at its first row of T
+inline bool gram_triangular(int64_t K) { return K > kSearchBM; }
 // bytes of fp32 slice sums that launch_gram needs beside Gs (0 when no tile is split)
 size_t gram_partial_bytes(int64_t M, int64_t K);
 hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,

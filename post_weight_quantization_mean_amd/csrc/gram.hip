@@ -10,6 +10,14 @@
 // that the quadratic form depends on).  The candidate kernel then multiplies Gs with E^T as
 // it multiplies X with E^T, and dots each output row k' with E[:, k' mod K].
 //
+// Triangular form (K > 512).  G is symmetric, so e G e^T = sum_k G[k,k] e_k^2 +
+// 2 sum_{k < k'} G[k,k'] e_k e_k': the same quadratic form with T = diag(G) + 2 triu(G, 1) in
+// place of G, which is zero below the diagonal.  The stored stack is then [T_hi; T_lo]
+// (T_hi = 2 G_hi and T_lo = 2 G_lo above the diagonal: doubling is exact), and a candidate
+// block whose 512 rows start at row k0 of T needs only the columns k >= k0: the K loop of
+// the block starts there, which cuts the candidate work to (K + 512) / (2K) of the full form.
+// With K <= 512 every block starts at column 0 and the symmetric G is kept.
+//
 // One workgroup = one 128 x 128 tile of G with k1b <= k2b (G is symmetric: the tile is also
 // written transposed); four waves of 64 x 64, i.e. 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.
 // Accumulation: fp32 in the matrix cores over 1024 tokens, then added into a second fp32 sum,
@@ -48,6 +56,23 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int gd_swz(int row) { return 2 * (row & 3); }
 
+// Element (k1, k2) of G, g, from a tile with k1b <= k2b: its hi and lo parts go to rows k1 and
+// K + k1 of the stack.  Off the tile diagonal (off_diag: k1b < k2b) the transposed element
+// (k2, k1) is written too.  Triangular form: T[k1, k2] = 2 g above the diagonal, g on it, and 0
+// below it (so the transposed element of an off-diagonal tile is 0).
+__device__ __forceinline__ void store_g(uint16_t* __restrict__ Gs, int64_t K, int64_t k1, int64_t k2, bool off_diag,
+                                        bool tri, float g) {
+  const float t = !tri || k1 == k2 ? g : (k1 < k2 ? 2.0f * g : 0.0f);
+  const uint16_t hi = bf16_bits(t);
+  const uint16_t lo = bf16_bits(t - __uint_as_float((uint32_t)hi << 16));
+  Gs[k1 * K + k2] = hi;
+  Gs[(K + k1) * K + k2] = lo;
+  if (off_diag) {
+    Gs[k2 * K + k1] = tri ? (uint16_t)0 : hi;
+    Gs[(K + k2) * K + k1] = tri ? (uint16_t)0 : lo;
+  }
+}
+
 // NST stages of TT tokens (LDS: NST x 2 x TT x 256 bytes).  Measured on the 16384 x 4096 X of
 // the decoder block (528 tiles): 4 stages of 64 tokens (one block per CU) 382 us; 3, 4 or 5
 // stages of 32 tokens (two blocks per CU) 426-439 us; 3 of 64, 474 us.  A kernel that transposed X
@@ -57,7 +82,7 @@ __device__ __forceinline__ int gd_swz(int row) { return 2 * (row & 3); }
 template <int NST, int TT>
 __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gram_dma_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx, uint16_t* __restrict__ Gs, int64_t full,
-    int S, int64_t slice_tokens, float* __restrict__ partial) {
+    int S, int64_t slice_tokens, float* __restrict__ partial, bool tri) {
   constexpr int STRIP = TT * GT * 2;  // one strip of a stage
   constexpr int STAGE = 2 * STRIP;
   constexpr int NDMA = TT / 8;        // 1 KiB copies per wave per stage
@@ -227,17 +252,9 @@ __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gr
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float g = tot[a][c][e] + acc[a][c][e];
         const int64_t k1 = k1b + r1 + 32 * a + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
         const int64_t k2 = k2b + c2 + 32 * c + (lane & 31);
-        const uint16_t hi = bf16_bits(g);
-        const uint16_t lo = bf16_bits(g - __uint_as_float((uint32_t)hi << 16));
-        Gs[k1 * K + k2] = hi;
-        Gs[(K + k1) * K + k2] = lo;
-        if (k1b != k2b) {
-          Gs[k2 * K + k1] = hi;
-          Gs[(K + k2) * K + k1] = lo;
-        }
+        store_g(Gs, K, k1, k2, k1b != k2b, tri, tot[a][c][e] + acc[a][c][e]);
       }
 }
 
@@ -245,7 +262,7 @@ __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gr
 // starting from 0 -- the order in which a whole tile adds its 1024-token block sums, so with one
 // block per slice the result is the same bits as the whole-tile kernel's.
 __global__ __launch_bounds__(256) void gram_fixup_kernel(const float* __restrict__ partial, int64_t K,
-                                                          int64_t full, int S, uint16_t* __restrict__ Gs) {
+                                                          int64_t full, int S, uint16_t* __restrict__ Gs, bool tri) {
   const int64_t u = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // k1 GT + k2, tile-local
   const int k1l = (int)(idx / GT), k2l = (int)(idx % GT);
@@ -258,15 +275,7 @@ __global__ __launch_bounds__(256) void gram_fixup_kernel(const float* __restrict
   const int64_t k1b = i * GT, k2b = (i + rem) * GT;
   float g = 0.0f;
   for (int s = 0; s < S; ++s) g += partial[(u * S + s) * (GT * GT) + idx];
-  const int64_t k1 = k1b + k1l, k2 = k2b + k2l;
-  const uint16_t hi = bf16_bits(g);
-  const uint16_t lo = bf16_bits(g - __uint_as_float((uint32_t)hi << 16));
-  Gs[k1 * K + k2] = hi;
-  Gs[(K + k1) * K + k2] = lo;
-  if (k1b != k2b) {
-    Gs[k2 * K + k1] = hi;
-    Gs[(K + k2) * K + k1] = lo;
-  }
+  store_g(Gs, K, k1b + k1l, k2b + k2l, k1b != k2b, tri, g);
 }
 
 // With tiles = q 512 + r (512: two rounds of one block on each of 256 CUs), the first q 512 tiles
@@ -312,11 +321,13 @@ size_t gram_partial_bytes(int64_t M, int64_t K) {
 hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,
                        hipStream_t st) {
   const GramPlan p = gram_plan(M, K);
+  const bool tri = gram_triangular(K);
   gram_dma_kernel<4, 64><<<(unsigned)(p.full + p.r * p.S), 256, 0, st>>>(X, M, K, ldx, Gs, p.full, p.S,
-                                                                        p.slice_tokens, partial);
+                                                                        p.slice_tokens, partial, tri);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.r == 0) return e;
-  gram_fixup_kernel<<<dim3((unsigned)(GT * GT / 256), (unsigned)p.r), 256, 0, st>>>(partial, K, p.full, p.S, Gs);
+  gram_fixup_kernel<<<dim3((unsigned)(GT * GT / 256), (unsigned)p.r), 256, 0, st>>>(partial, K, p.full, p.S, Gs,
+                                                                                     tri);
   return hipGetLastError();
 }
 

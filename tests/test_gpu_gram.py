@@ -2,7 +2,9 @@
 Activation", §1, the exact output error through X^T X) against the oracle's exact losses.
 
 Tolerance, from the arithmetic.  The kernel forms Y' = G~ E~^T with E~ = E rounded to bf16
-and G~ = G_hi + G_lo, then sums Y'[k', n] e[n, k'] with the unrounded e:
+and G~ = G_hi + G_lo, then sums Y'[k', n] e[n, k'] with the unrounded e (for K > 512, G~ is the
+triangular T = diag(G) + 2 triu(G, 1), whose quadratic form is G's; only the K <= 512 cases,
+where G~ is G itself, can fall under the small-layer bound below):
   * bf16 E: sum_n e G (E~ - E)^T = sum_{m,n} y (X dE^T), at most 2^-8 sum |y| (|X| |E|^T): the
     first-order term of the direct form with coefficient 1 instead of 2;
   * G: 2^-16 relative per entry (G_lo's rounding) plus fp32 sums over 1024-token blocks and
@@ -64,6 +66,10 @@ def gram_tolerance(X64, W32, s_table, ref_losses):
     (64, 128, 1),       # degenerate: one group, one output
     (4096, 512, 256),
     (2048, 4096, 128),  # 528 G tiles: 512 whole, the other 16 in two token slices each
+    # triangular form (K > 512): row tiles of T start their K loop past column 0
+    (2600, 1024, 200),  # tiles start at columns 0, 512 (T_hi) and 0, 512 (T_lo)
+    (3000, 1152, 131),  # K % 512 = 128: a tile straddles T_hi and T_lo (starts at 0), the T_lo
+                        # tiles start at 256 and 768, the last one ends past 2K
 ])
 def test_gram_search_vs_oracle(awq, M, K, N):
     banner(f"search gram M={M} K={K} N={N}")
