@@ -568,198 +568,308 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_mfma_kernel(
   }
 }
 
-// ---- prefill -------------------------------------------------------------------------------
-// A block of 8 waves (two per SIMD, at most 256 registers each) computes a 512-token x
-// 128-output tile.  Each wave multiplies its own 64 tokens, so X never needs sharing: the wave
-// copies its rows of every 32-channel chunk from global memory straight into LDS (buffer load
-// with LDS destination, 1 KiB per instruction), three chunks deep, and nothing of X passes
-// through registers or waits for a barrier.  The decoded weight tile is shared by all waves:
-// its codes are loaded two chunks ahead, decoded after the chunk's matrix instructions and
-// stored for the next chunk, which one barrier per chunk publishes.  The three X stages and
-// the three W stages are distinct LDS objects with a fixed role in each step of the unrolled
-// loop, so the compiler's wait counts for the copies stay exact.  LDS rows are 64 bytes,
-// unpadded, their four 16-byte slots permuted per row (X by (row >> 2) & 3, W by wslot below)
-// so that neither the fragment reads nor the stores meet a bank conflict.  (A 4-wave block,
-// 128 tokens a wave at 512 registers, is the other instance of the template; it measured the
-// same at 4096 tokens and slower at 512 and 16384.)
+// ---- prefill (bf16 X, more than 8 tokens) ----------------------------------------------------
 #define AWQ_LDS __attribute__((address_space(3)))
 constexpr int PBM = 512, PBN = 128, PKC = 32;
-constexpr int XSTAGE = PBM * PKC * 2;  // 32 KiB
-constexpr int WSTAGE = PBN * PKC * 2;  // 8 KiB
 
 __device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
   const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
   return __builtin_bit_cast(uint32_t, h);
 }
-__device__ __forceinline__ int pslot(int row, int s) { return (s ^ ((row >> 2) & 3)) * 16; }  // bytes
-// W stage slots: f(row) = ((row >> 1) & 3) ^ 3 ((row >> 3) & 1).  LDS serves a 16-byte read for
-// 16 lanes at a time over 64 four-byte banks and a 16-byte write for 8 lanes at a time over 32
-// banks (measured with the bank-conflict counter); under this f both the 32-row fragment reads
-// (16 consecutive rows, one slot) and the decode's stores (8 lanes: 4 rows x 2 slots) are
-// conflict-free, where (row >> 2) & 3 doubled the stores' time.
-__device__ __forceinline__ int wslot(int row, int s) {
-  return (s ^ ((row >> 1) & 3) ^ (((row >> 3) & 1) * 3)) * 16;
-}
 
-// NW waves per block: wave w multiplies tokens RW w .. RW w + RW - 1 of the tile (RW = 512 / NW);
-// a W row's four words of a chunk are decoded by TPR = NW / 2 threads, WPT = 4 / TPR words each.
-template <int NW>
-struct WRegs {
-  uint32_t qv[8 / NW];  // this thread's words of its row: 8 codes each
+// The tile (512 tokens x 128 outputs, four waves of 128 x 128 outputs, one per SIMD, 256 fp32
+// accumulators a lane) and the pipeline of the candidate search's fused kernel, with the int4
+// decode where the search quantizes.  Step c multiplies chunk c (32 channels: 32
+// v_mfma_f32_32x32x16_bf16 per wave, back to back) and issues between them:
+//   * the decode of chunk c+2 into W stage (c+2) % 3: wave w decodes W rows 32w .. 32w+31, lane l
+//     rows 32w + l/4 and 32w + 16 + l/4, channels 8 (l%4) .. +7, i.e. one code word per row,
+//     loaded four or five steps earlier; Delta (q - z) = fma(q, Delta, -z Delta) is exact in fp32
+//     (q, z <= 15, Delta fp16) and is rounded once to bf16, the bf16 W~ of the other kernels;
+//   * the fragment reads of chunk c's second K-half and of chunk c+1's B fragments and first two
+//     A fragments;
+//   * even steps: the code words of chunks c+4 and c+5 (one 4-byte load per row each) and, at a
+//     group's first chunk, the next group's fp16 scales and zeros of the lane's two rows; every
+//     step: half of the X pair that follows, copied from global memory straight into LDS.
+// X lives in two pair stages (chunks 2p, 2p+1: a full 128-byte line of a row), each split into
+// the first and the last 64 of every wave's rows (distinct LDS objects with a static role in
+// each unrolled step, so the compiler's waits for the copies stay exact).  Each wave copies and
+// reads only its own 128 X rows; the decoded W is shared, and one barrier per step, after every
+// wave stored its part of chunk c+2, makes chunk c+1 readable.  Slots are permuted per row (X
+// pair rows by (row >> 1) & 7, W rows by (row >> 2) & 3) so that the 32-row fragment reads are
+// free of bank conflicts.  Rows past M or N read as zero through the buffer resources (a zero
+// scale decodes to zero weights) and their outputs are not stored.
+constexpr int QXROW = 128;            // bytes of an X pair row (two chunks)
+constexpr int QXPSTAGE = PBM * QXROW;  // 64 KiB
+constexpr int QEROW = PKC * 2;        // bytes of a decoded W row of one chunk
+constexpr int QESTAGE = PBN * QEROW;  // 8 KiB
+constexpr int QNES = 3;               // W stages
+
+__device__ __forceinline__ int qswz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int qxswz(int row) { return (row >> 1) & 7; }
+
+struct CodeSet {
+  uint32_t w[2];  // this lane's code word of its rows r0 and r1 for one chunk
+};
+struct ScaleZero {
+  uint32_t d0, d1, z0, z1;  // fp16 bits of the rows' scales and zeros for one group
+};
+struct RowDq {
+  float d, nzd;  // Delta and -z Delta of one row's group
 };
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void w4a16_gemm_kernel(
+__global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
     float* __restrict__ Y, int64_t ldy, int64_t ntiles, int64_t tiles, int64_t per_xcd) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs1[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs2[XSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ws0[WSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ws1[WSTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t ws2[WSTAGE];
-  const int64_t G = K / kGroup, words = K / 8;
-  // Blocks go to the 8 XCDs round robin (block b to XCD b % 8); XCD x takes the tiles
-  // x per_xcd .. (x + 1) per_xcd - 1 in order, so its blocks share token tiles and the tile's X
-  // stays in that XCD's L2.  Blocks past the last tile (grid rounded up to 8) return at once.
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[QXPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[QXPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[QXPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[QXPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t es[QNES * QESTAGE];
+  // XCD x (= block % 8) takes the tiles x per_xcd .. (x + 1) per_xcd - 1 in order (token-tile
+  // major), so its resident blocks share token tiles in its L2
   const int64_t L = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (L >= tiles) return;
-  const int64_t mt = L / ntiles, nt = L % ntiles;
-  const int64_t m0 = mt * PBM, n0 = nt * PBN;
+  const int64_t m0 = (L / ntiles) * PBM, n0 = (L % ntiles) * PBN;
+  const int64_t G = K / kGroup, words = K / 8;
+  const int nchunks = (int)(K / PKC);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // X rows of this tile through a buffer resource: rows past M read as zero (host: 512 rows of
-  // X span less than 2^31 bytes)
-  const int64_t xbytes = (M - m0) * ldx * 2;
-  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(X + m0 * ldx), (short)0, (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
-  constexpr int RW = PBM / NW, RT = RW / 32, NDMA = RW / 16, TPR = NW / 2, WPT = 4 / TPR;
-  // copy instruction i (0 .. NDMA - 1) of this wave fills its rows 16 i + lane / 4 with 16 bytes
-  // each: physical slot lane % 4 receives logical slot (lane % 4) ^ swizzle(row)
-  uint32_t xoff[NDMA];
+  // buffer resources rebased at the tile: rows past M (or N) read as zero; offsets stay below
+  // 2^31 (host: 512 rows of X; 128 rows of codes, scales or zeros are far smaller)
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t xrsrc = rsrc(X + m0 * ldx, (M - m0) * ldx * 2);
+  const __amdgpu_buffer_rsrc_t crsrc = rsrc(qweight + n0 * words, (N - n0) * words * 4);
+  const __amdgpu_buffer_rsrc_t srsrc = rsrc(scales + n0 * G, (N - n0) * G * 2);
+  const __amdgpu_buffer_rsrc_t zrsrc = rsrc(zeros + n0 * G, (N - n0) * G * 2);
+  // X copy instruction i (0..15) of wave w fills pair rows 128 w + 8 i + lane / 8, slot lane % 8,
+  // with the global 16-byte piece slot ^ qxswz(row); qxswz depends on i only through i % 2
+  uint32_t xoff[2];
 #pragma unroll
-  for (int i = 0; i < NDMA; ++i) {
-    const int row = wave * RW + 16 * i + (lane >> 2);
-    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
+  for (int i = 0; i < 2; ++i) {
+    const int row = wave * 128 + 8 * i + (lane >> 3);
+    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 7) ^ qxswz(row)) * 16));
   }
-  auto dma_x = [&](uint8_t* stage, int64_t c) {
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(stage + (wave * RW + 16 * i) * 64), 16,
-                                               (int)xoff[i], (int)(c * PKC * 2), 0, 0);
+  const uint32_t xrow16 = (uint32_t)(16 * ldx * 2);
+  const int xwave = wave * 64 * QXROW;  // this wave's 64 rows in a half stage
+  auto dma_x_one = [&](uint8_t* xh, int i, int p) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(xh + xwave + (i & 7) * 1024), 16,
+                                             (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * QXROW),
+                                             0, 0);
   };
-  // W chunk: 128 rows x 4 words (32 channels); thread: row tid / TPR, words WPT (tid % TPR) ..
-  const int wr = tid / TPR, wq = tid % TPR;
-  const int64_t wn = n0 + wr;
-  const bool wlive = wn < N;
-  const int32_t* wrow = qweight + (wlive ? wn : 0) * words;
-  const int64_t nch = K / PKC;  // a multiple of 4: a group is four chunks
-  auto load_codes = [&](WRegs<NW>& R, int64_t c) {
-    const int64_t cc = c < nch ? c : nch - 1;  // past the end: an in-bounds reload, never stored
-    if constexpr (WPT == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(wrow + cc * (PKC / 8) + 2 * wq);
-      R.qv[0] = v.x;
-      R.qv[1] = v.y;
-    } else {
-      R.qv[0] = wrow[cc * (PKC / 8) + wq];
-    }
+  // decode: rows r0, r1 of the W tile, code word q4 of each chunk (channels 8 q4 .. 8 q4 + 7)
+  const int q4 = lane & 3;
+  const int r0 = wave * 32 + (lane >> 2), r1 = r0 + 16;
+  const uint32_t coff0 = (uint32_t)(r0 * words * 4 + q4 * 4), coff1 = (uint32_t)(r1 * words * 4 + q4 * 4);
+  const uint32_t soff0 = (uint32_t)(r0 * G * 2), soff1 = (uint32_t)(r1 * G * 2);
+  const int eslot0 = r0 * QEROW + ((q4 ^ qswz(r0)) * 16);
+  const int eslot1 = r1 * QEROW + ((q4 ^ qswz(r1)) * 16);
+  // code word of row i for chunk (cb / 16 + j): the constant part goes in the immediate offset;
+  // chunks past the end read other words of the row or zeros and are never used
+  auto load_c = [&](CodeSet& S, int i, int cb, int j) {
+    S.w[i] = __builtin_amdgcn_raw_buffer_load_b32(crsrc, (int)(i == 0 ? coff0 : coff1) + j * 16, cb, 0);
   };
-  // The row's fp16 scale and zero are loaded once per group, with the group's first chunk, into
-  // register pair g mod 3; they stay fp16 bits until the decode, which comes two chunks later.
-  uint32_t sd[3] = {0, 0, 0}, sz[3] = {0, 0, 0};
-  auto load_group = [&](uint32_t& d, uint32_t& z, int64_t c) {
-    const int64_t g = (c < nch ? c : nch - 1) / 4;
-    d = scales[(wlive ? wn : 0) * G + g];
-    z = zeros[(wlive ? wn : 0) * G + g];
+  auto load_sz = [&](ScaleZero& P, int g) {
+    P.d0 = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (int)soff0, g * 2, 0);
+    P.d1 = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (int)soff1, g * 2, 0);
+    P.z0 = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, (int)soff0, g * 2, 0);
+    P.z1 = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, (int)soff1, g * 2, 0);
   };
-  auto store_w = [&](const WRegs<NW>& R, uint32_t dh, uint32_t zh, uint8_t* stage) {
-    const float dv = wlive ? h2f((uint16_t)dh) : 0.0f, zv = h2f((uint16_t)zh);  // rows past N: weight 0
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float a = dv * ((float)((R.qv[j] >> (8 * c)) & 15u) - zv);  // exact in fp32
-        const float bq = dv * ((float)((R.qv[j] >> (8 * c + 4)) & 15u) - zv);
-        pk[c] = bf16x2_of(a, bq);
-      }
-      *reinterpret_cast<uint4*>(stage + wr * 64 + wslot(wr, WPT * wq + j)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    }
+  auto row_setup = [](uint32_t dh, uint32_t zh) {
+    RowDq q;
+    q.d = h2f((uint16_t)dh);
+    q.nzd = -(h2f((uint16_t)zh) * q.d);  // exact: z <= 15 is an integer, Delta has 11 bits
+    return q;
   };
-  f32x16 acc[RT][4];
+  // weight j (0..7) of row i's word: Delta (q - z) with q = nibble j
+  auto elem = [&](const CodeSet& S, const RowDq& q, int i, int j) {
+    const uint32_t u = (j & 1) ? (S.w[i] >> 4) & 0x0f0f0f0fu : S.w[i] & 0x0f0f0f0fu;
+    const int b = j >> 1;
+    const float qf = b == 0 ? ubyte<0>(u) : b == 1 ? ubyte<1>(u) : b == 2 ? ubyte<2>(u) : ubyte<3>(u);
+    return fmaf(qf, q.d, q.nzd);
+  };
+  auto store_piece = [&](uint8_t* estage, int slot, const float* e8) {
+    uint32_t pk[4];
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+    for (int h = 0; h < 4; ++h) pk[h] = bf16x2_of(e8[2 * h], e8[2 * h + 1]);
+    *reinterpret_cast<uint4*>(estage + slot) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  };
+  auto decode_all = [&](const CodeSet& S, const RowDq& q0, const RowDq& q1, uint8_t* estage) {  // prologue
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, q0, 0, j);
+    store_piece(estage, eslot0, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, q1, 1, j);
+    store_piece(estage, eslot1, e);
+  };
+  // fragment reads: lane reads row (32 t + fr), 16-byte piece 2 h + fh of K-half h of its chunk
+  const int fr = lane & 31, fh = lane >> 5;
+  const int efoff0 = fr * QEROW + (((0 + fh) ^ qswz(fr)) * 16);
+  const int efoff1 = fr * QEROW + (((2 + fh) ^ qswz(fr)) * 16);
+  auto xfoff = [&](int half, int h) { return fr * QXROW + (((4 * half + 2 * h + fh) ^ qxswz(fr)) * 16); };
+  auto frag = [&](const uint8_t* base, int fo) { return *reinterpret_cast<const bf16x8*>(base + fo); };
+  auto vm_wait = [](auto n) {  // s_waitcnt vmcnt(n), other counters untouched
+    constexpr int v = decltype(n)::value;
+    __builtin_amdgcn_s_waitcnt((v & 0xf) | (0x7 << 4) | (0xf << 8) | ((v >> 4) << 14));
+  };
+  constexpr int kWaitLgkm0 = 0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
-  const int frow = lane & 31, fs = lane >> 5;
-  auto compute = [&](const uint8_t* xst, const uint8_t* wst) {
+
+  CodeSet S0, S1, S2, S3;  // code words of chunk c live in set c % 4
+  ScaleZero PC, PN;        // scales and zeros of the group being decoded, of the next group
+  RowDq q0, q1;            // row_setup of PC (rows r0, r1)
+  // Prologue: group 0's scales and zeros, codes of chunks 0-3, the X pair of chunks 0 and 1;
+  // then chunks 0 and 1 are decoded.
+  load_sz(PC, 0);
+  load_c(S0, 0, 0, 0);
+  load_c(S1, 0, 0, 1);
+  load_c(S0, 1, 0, 0);
+  load_c(S1, 1, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 af[RT], bfr[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int row = cc * 32 + frow;
-        bfr[cc] = *reinterpret_cast<const bf16x8*>(wst + row * 64 + wslot(row, 2 * h + fs));
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int row = wave * RW + r * 32 + frow;
-        af[r] = *reinterpret_cast<const bf16x8*>(xst + row * 64 + pslot(row, 2 * h + fs));
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[r], bfr[cc], acc[r][cc], 0, 0, 0);
-    }
-  };
-  // stage i as the shared object itself (not through a pointer table), so that the compiler
-  // knows which copy writes which stage and its wait counts stay exact
-  auto xst = [&](auto I) -> uint8_t* {
-    constexpr int i = decltype(I)::value % 3;
-    if constexpr (i == 0) return xs0; else if constexpr (i == 1) return xs1; else return xs2;
-  };
-  auto wst = [&](auto I) -> uint8_t* {
-    constexpr int i = decltype(I)::value % 3;
-    if constexpr (i == 0) return ws0; else if constexpr (i == 1) return ws1; else return ws2;
-  };
-  // The barrier that publishes a W stage: this wave's LDS stores done (lgkmcnt 0), then
-  // s_barrier.  No workgroup fence: a fence would also wait for every X copy still in flight
-  // (they write LDS), though only the issuing wave reads those rows and its reads wait for
-  // their own copies.  The signal fences keep the compiler from moving LDS accesses across.
-  auto publish_w = [] {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63, expcnt 7 (no wait), lgkmcnt 0
+  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_c(S2, 0, 0, 2);
+  load_c(S3, 0, 0, 3);
+  load_c(S2, 1, 0, 2);
+  load_c(S3, 1, 0, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  vm_wait(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  q0 = row_setup(PC.d0, PC.z0);
+  q1 = row_setup(PC.d1, PC.z1);
+  decode_all(S0, q0, q1, es + 0 * QESTAGE);
+  decode_all(S1, q0, q1, es + 1 * QESTAGE);
+  bf16x8 a0[4], b0[4];
+  {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a0[t] = frag(xp0lo + xwave + t * 32 * QXROW, xfoff(0, 0));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * QEROW, efoff0);
+    // use the code words of chunks 2 and 3 here, so that their loads are not sunk to the loop
+    // head (where every iteration would wait for them)
+    asm volatile("" ::"v"(S2.w[0]), "v"(S2.w[1]), "v"(S3.w[0]), "v"(S3.w[1]));
+  }
+
+  // One step, hand-scheduled in 32 groups, one per matrix instruction of chunk c (k = c % 4
+  // known at compile time; xc is chunk c's pair stage, xn chunk c+1's):
+  //   groups 0, 1: A fragments 2, 3 of chunk c (first used in groups 8 and 12);
+  //   groups 0-7: second-half fragment reads of chunk c (A even, B odd groups);
+  //   groups 3-25, two of every three: the sixteen weights of chunk c+2; W stores in groups 14
+  //   and 26;
+  //   groups 17-23 (odd): chunk c+1's B fragments of the first K-half; groups 24, 25: its A
+  //   fragments 0, 1;
+  //   vector memory: even steps the code words of chunks c+4 and c+5 (groups 0-3), when k = 0
+  //   the next group's scales and zeros (groups 4, 5), and the copy of pair c/2 + 1, rows 0-63
+  //   (groups 6, 9, ..., 27); odd steps the same pair's rows 64-127 (groups 0, 2, ..., 14).
+  // vmcnt accounting (even steps: 4 code loads, 4 more when k = 0, 8 copies; odd steps: 8):
+  //   * start of an even step: everything landed (the rows 64-127 of chunk c, copied by the
+  //     previous step, are read now); start of an odd step: at most the previous step's last 12
+  //     outstanding (chunk c's X comes from steps c-3 and c-2, the codes of chunk c+2 from step
+  //     c-3 or c-2);
+  //   * group 24 of an odd step: chunk c+1's rows 0-63 (copied by step c-1) landed, with this
+  //     step's 8 copies after them; of an even step: nothing is awaited (those rows came from
+  //     step c-2), the count is this step's loads before group 24.
+  auto step = [&](int c8, auto jc, const uint8_t* xclo, const uint8_t* xchi, const uint8_t* xnlo, uint8_t* xdlo,
+                  uint8_t* xdhi, const CodeSet& Q, CodeSet& F4, CodeSet& F5, int& eo0, int& eo1, int& eo2) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int k = j & 3;
+    constexpr bool even = (k & 1) == 0;
+    const int cb = c8 * 16;                    // chunk c8's byte offset in a row of code words
+    const int pd = (c8 >> 1) + (j >> 1) + 1;   // pair being copied
+    const int gn = (c8 >> 2) + (j >> 2) + 1;   // next group (k = 0 steps)
+    const uint8_t* ec = es + eo0;
+    const uint8_t* en = es + eo1;
+    uint8_t* eq = es + eo2;
+    const uint8_t* xwlo = xclo + xwave;
+    const uint8_t* xwhi = xchi + xwave;
+    const uint8_t* xnw = xnlo + xwave;
+    auto xa = [&](int t) { return (t < 2 ? xwlo : xwhi) + (t & 1) * 32 * QXROW; };
+    const int xo0 = xfoff(k & 1, 0), xo1 = xfoff(k & 1, 1), xn0 = xfoff((k + 1) & 1, 0);
+    if (k == 2) {  // chunks c+2 .. c+5: the next group
+      PC = PN;
+      q0 = row_setup(PC.d0, PC.z0);
+      q1 = row_setup(PC.d1, PC.z1);
+    }
+    bf16x8 a1[4], b1[4];
+    float e[16];
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait(std::integral_constant<int, even ? 0 : 12>{});
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      const int r = (g >> 2) & 3, cc = g & 3;
+      if (g < 16)
+        acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[r], b0[cc], acc[r][cc], 0, 0, 0);
+      else
+        acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[r], b1[cc], acc[r][cc], 0, 0, 0);
+      if (g < 2) a0[2 + g] = frag(xa(2 + g), xo0);
+      if (g < 8) {
+        if (g & 1)
+          b1[g >> 1] = frag(ec + (g >> 1) * 32 * QEROW, efoff1);
+        else
+          a1[g >> 1] = frag(xa(g >> 1), xo1);
+      }
+      // weight el in group 3 + 3 (el / 2) + el % 2: groups 3-13 for row r0, 15-25 for r1
+      const int el = g >= 3 && g <= 25 && (g - 3) % 3 != 2 ? 2 * ((g - 3) / 3) + (g - 3) % 3 : -1;
+      if (el >= 0) {
+        e[el] = el < 8 ? elem(Q, q0, 0, el) : elem(Q, q1, 1, el - 8);
+        asm volatile("" : "+v"(e[el]));  // keep the weight in this group
+      }
+      if (g == 14) store_piece(eq, eslot0, e);
+      if (g == 26) store_piece(eq, eslot1, e + 8);
+      // every fragment read before group 8 has landed; only the W store of group 14 may be in
+      // flight
+      if (g == 15) __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x1 << 8) | (0x3 << 14));
+      if (g >= 16 && g < 24 && (g & 1)) b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * QEROW, efoff0);
+      if (g == 24) vm_wait(std::integral_constant<int, even ? (k == 0 ? 14 : 10) : 8>{});
+      if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * QXROW, xn0);
+      if (even) {
+        if (g == 0) load_c(F4, 0, cb, j + 4);
+        if (g == 1) load_c(F5, 0, cb, j + 5);
+        if (g == 2) load_c(F4, 1, cb, j + 4);
+        if (g == 3) load_c(F5, 1, cb, j + 5);
+        if (k == 0 && g == 4) {
+          PN.d0 = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (int)soff0, gn * 2, 0);
+          PN.d1 = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (int)soff1, gn * 2, 0);
+        }
+        if (k == 0 && g == 5) {
+          PN.z0 = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, (int)soff0, gn * 2, 0);
+          PN.z1 = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, (int)soff1, gn * 2, 0);
+        }
+        if (g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(xdlo, (g - 6) / 3, pd);
+      } else {
+        if (g <= 14 && (g & 1) == 0) dma_x_one(xdhi, 8 + g / 2, pd);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // W stores of chunk c+2, fragment reads
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int et = eo0;
+    eo0 = eo1;
+    eo1 = eo2;
+    eo2 = et;
   };
-  WRegs<NW> rg[3];  // W codes of chunk c in set c % 3
-  // Step c, with S = c mod 12 known at compile time (so that every stage, register set and
-  // group pair is fixed and the step has no branch, which would cost the exact wait counts):
-  // copy X chunk c + 2 into the X stage read two steps ago (past the end: a harmless re-copy
-  // into a stage no later step reads), load W chunk c + 2's codes (and, at a group's first chunk,
-  // its scale and zero), multiply chunk c, decode and store W chunk c + 1 into the W stage read
-  // two steps ago, then the barrier that publishes it.
-  auto step = [&](int64_t c, auto Sc) {
-    constexpr int S = decltype(Sc)::value;
-    dma_x(xst(std::integral_constant<int, S + 2>{}), c + 2 < nch ? c + 2 : nch - 1);
-    load_codes(rg[(S + 2) % 3], c + 2);
-    if constexpr ((S + 2) % 4 == 0) load_group(sd[((S + 2) / 4) % 3], sz[((S + 2) / 4) % 3], c + 2);
-    __builtin_amdgcn_sched_barrier(0);  // the copies and loads ahead of the products they hide behind
-    compute(xst(std::integral_constant<int, S>{}), wst(std::integral_constant<int, S>{}));
-    store_w(rg[(S + 1) % 3], sd[((S + 1) / 4) % 3], sz[((S + 1) / 4) % 3], wst(std::integral_constant<int, S + 1>{}));
-    publish_w();
-  };
-  dma_x(xs0, 0);
-  dma_x(xs1, 1);
-  load_codes(rg[0], 0);
-  load_codes(rg[1], 1);
-  load_group(sd[0], sz[0], 0);
-  store_w(rg[0], sd[0], sz[0], ws0);
-  __syncthreads();
+
+  // nchunks = K / 32 is a multiple of 4.  Step c multiplies chunk c from pair stage (c / 2) % 2,
+  // decodes set (c+2) % 4 into W stage (c+2) % 3, copies half of pair c/2 + 1 into stage
+  // (c/2 + 1) % 2 and, when even, loads the codes of chunks c+4 and c+5 into sets c % 4 and
+  // (c+1) % 4.  The unrolled body covers eight steps so that both pair stages keep static roles.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -768,30 +878,33 @@ __global__ __launch_bounds__(64 * NW, 1) void w4a16_gemm_kernel(
   using I5 = std::integral_constant<int, 5>;
   using I6 = std::integral_constant<int, 6>;
   using I7 = std::integral_constant<int, 7>;
-  using I8 = std::integral_constant<int, 8>;
-  using I9 = std::integral_constant<int, 9>;
-  using I10 = std::integral_constant<int, 10>;
-  using I11 = std::integral_constant<int, 11>;
-  int64_t c = 0;
-  for (; c + 12 <= nch; c += 12) {
-    step(c, I0{}); step(c + 1, I1{}); step(c + 2, I2{}); step(c + 3, I3{});
-    step(c + 4, I4{}); step(c + 5, I5{}); step(c + 6, I6{}); step(c + 7, I7{});
-    step(c + 8, I8{}); step(c + 9, I9{}); step(c + 10, I10{}); step(c + 11, I11{});
+  int eo0 = 0, eo1 = QESTAGE, eo2 = 2 * QESTAGE;
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    step(c, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, eo0, eo1, eo2);
+    step(c, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, eo0, eo1, eo2);
+    step(c, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, eo0, eo1, eo2);
+    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, eo0, eo1, eo2);
+    step(c, I4{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, eo0, eo1, eo2);
+    step(c, I5{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, eo0, eo1, eo2);
+    step(c, I6{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, eo0, eo1, eo2);
+    step(c, I7{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, eo0, eo1, eo2);
   }
-  if (c < nch) {  // 4 or 8 chunks remain (nch is a multiple of 4)
-    step(c, I0{}); step(c + 1, I1{}); step(c + 2, I2{}); step(c + 3, I3{});
-    if (c + 4 < nch) {
-      step(c + 4, I4{}); step(c + 5, I5{}); step(c + 6, I6{}); step(c + 7, I7{});
-    }
+  if (c < nchunks) {  // K / 128 odd: one more group
+    step(c, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, eo0, eo1, eo2);
+    step(c, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, eo0, eo1, eo2);
+    step(c, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, eo0, eo1, eo2);
+    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, eo0, eo1, eo2);
   }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no copy outlives the block
   // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t m = m0 + wave * RW + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+        const int64_t m = m0 + wave * 128 + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
         const int64_t n = n0 + cc * 32 + (lane % 32);
         if (m < M && n < N) Y[m * ldy + n] = acc[r][cc][i];
       }
@@ -855,8 +968,7 @@ hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t 
   if (!xf32 && M > kW4a16GemvMax) {
     const int64_t mtiles = (M + PBM - 1) / PBM, ntiles = (N + PBN - 1) / PBN;
     const int64_t tiles = mtiles * ntiles, per_xcd = (tiles + 7) / 8;
-    constexpr int kGemmWaves = 8;
-    w4a16_gemm_kernel<kGemmWaves><<<(unsigned)(8 * per_xcd), 64 * kGemmWaves, 0, st>>>(
+    w4a16_gemm_pipe_kernel<<<(unsigned)(8 * per_xcd), 256, 0, st>>>(
         static_cast<const uint16_t*>(X), M, ldx, K, qweight, scales, zeros, N, Y, ldy, ntiles, tiles, per_xcd);
     return hipGetLastError();
   }
