@@ -233,10 +233,11 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   if (mul_ok(mul_ok(awq::kSearchBM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
   // one candidate's group ranges (float2 [K/128][NP]) are addressed with 32-bit offsets
   if (mul_ok(mul_ok(K / kGroup, NP), 8) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
-  // Gram form: the product's left operand is Gs [2K, K] bf16 (rows of G_hi, then G_lo)
+  // Gram form: the product's left operand is Tp [K, 2K] bf16 (G_hi and G_lo interleaved by
+  // 32-column chunks); 512 of its rows are addressed with 32-bit offsets
   if (gram && (x_dtype != AWQ_DTYPE_BF16 || w_dtype != AWQ_DTYPE_BF16)) return AWQ_ERR_UNSUPPORTED;
-  if (gram && mul_ok(mul_ok(awq::kSearchBM, K), 2) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
-  const int64_t rows = gram ? 2 * K : M;  // rows of the product's left operand
+  if (gram && mul_ok(mul_ok(awq::kSearchBM, 2 * K), 2) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  const int64_t rows = gram ? K : M;  // rows of the product's left operand
   SearchLayout L;
   if (!search_layout(rows, K, NP, n_grid, &L)) return AWQ_ERR_SHAPE;
   size_t total = L.total, gs_off = 0, gp_off = 0;
@@ -280,8 +281,7 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   if (e == hipSuccess && fused_begin != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
   if (e == hipSuccess && gram)
-    e = awq::launch_search_fused(Gs, false, rows, K, segs, false, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
-                                 partial, s, true);
+    e = awq::launch_search_gram(Gs, K, segs, sr_tab, params, n_grid, plan, partial, s);
   else if (e == hipSuccess)
     e = awq::launch_search_fused(X, xf32, M, ldx, segs, wf32, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
                                  partial, s);
@@ -332,7 +332,7 @@ AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, 
       K > INT64_MAX / 8)
     return 0;
   SearchLayout L;
-  if (!search_layout(2 * K, K, N, n_grid, &L)) return 0;
+  if (!search_layout(K, K, N, n_grid, &L)) return 0;
   const int64_t gsb = mul_ok(mul_ok(2 * K, K), 2);
   if (gsb < 0) return 0;
   return L.total + align_up((size_t)gsb) + align_up(awq::gram_partial_bytes(M, K));

@@ -129,15 +129,20 @@ hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, in
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
                                bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
                                const float2* sr_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st, bool gram = false);
-// Gram form: Gs bf16 [2K, K] = [bf16(G); bf16(G - bf16(G))], G = X^T X for bf16 X [M, K];
-// when gram_triangular(K), G there stands for T = diag(X^T X) + 2 triu(X^T X, 1) (zero below
-// the diagonal), and each candidate block's K loop starts at its first row of T
+                               const SearchPlan& plan, double* partial, hipStream_t st);
+// Gram form: Tp bf16 [K, 2K], row k' = chunks of 32 columns of G_hi and G_lo interleaved
+// (bf16(G) and bf16(G - bf16(G)), G = X^T X for bf16 X [M, K]); when gram_triangular(K), G there
+// stands for T = diag(X^T X) + 2 triu(X^T X, 1) (zero below the diagonal), and each candidate
+// block's K loop starts at its first row of T
 inline bool gram_triangular(int64_t K) { return K > kSearchBM; }
 // bytes of fp32 slice sums that launch_gram needs beside Gs (0 when no tile is split)
 size_t gram_partial_bytes(int64_t M, int64_t K);
 hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,
                        hipStream_t st);
+// the candidate losses' partial sums in the Gram form (plan: search_plan with K rows)
+hipError_t launch_search_gram(const uint16_t* Tp, int64_t K, const WSegs& W, const float2* sr_tab,
+                              const float2* params, int n_grid, const SearchPlan& plan, double* partial,
+                              hipStream_t st);
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
                          float* s_best, uint32_t* flags, hipStream_t st);

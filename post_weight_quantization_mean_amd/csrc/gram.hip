@@ -4,25 +4,27 @@
 // so after G is formed once (2 M K^2 flop) every candidate costs 2 K^2 N flop instead of
 // 2 M K N: less work whenever M > K (here 2 K, see below).
 //
-// gram_dma_kernel forms G on the bf16 matrix cores and stores it as two bf16 matrices stacked
-// along the rows, Gs = [G_hi; G_lo] [2K x K] with G_hi = bf16(G), G_lo = bf16(G - G_hi), so
-// G_hi + G_lo keeps 16 significand bits of G (a single bf16 G would lose the cancellation
-// that the quadratic form depends on).  The candidate kernel then multiplies Gs with E^T as
-// it multiplies X with E^T, and dots each output row k' with E[:, k' mod K].
+// gram_dma_kernel forms G on the bf16 matrix cores and stores it as two bf16 matrices,
+// G_hi = bf16(G) and G_lo = bf16(G - G_hi), so G_hi + G_lo keeps 16 significand bits of G (a
+// single bf16 G would lose the cancellation that the quadratic form depends on).  They are
+// interleaved in one [K x 2K] matrix Tp: row k' holds, for every 32-column chunk c, chunk c of
+// row k' of G_hi and then of G_lo.  gram_search_kernel multiplies both with E^T into the same
+// accumulators and dots each output (k', n) with E[n, k'].
 //
 // Triangular form (K > 512).  G is symmetric, so e G e^T = sum_k G[k,k] e_k^2 +
 // 2 sum_{k < k'} G[k,k'] e_k e_k': the same quadratic form with T = diag(G) + 2 triu(G, 1) in
-// place of G, which is zero below the diagonal.  The stored stack is then [T_hi; T_lo]
-// (T_hi = 2 G_hi and T_lo = 2 G_lo above the diagonal: doubling is exact), and a candidate
-// block whose 512 rows start at row k0 of T needs only the columns k >= k0: the K loop of
-// the block starts there, which cuts the candidate work to (K + 512) / (2K) of the full form.
-// With K <= 512 every block starts at column 0 and the symmetric G is kept.
+// place of G, which is zero below the diagonal.  Tp then holds T_hi and T_lo (T_hi = 2 G_hi and
+// T_lo = 2 G_lo above the diagonal: doubling is exact), and a candidate block whose 512 rows
+// start at row k0 of T needs only the columns k >= k0: the K loop of the block starts there,
+// which cuts the candidate work to about (K + 512) / (2K) of the full form.  With K <= 512
+// every block starts at column 0 and the symmetric G is kept.
 //
 // One workgroup = one 128 x 128 tile of G with k1b <= k2b (G is symmetric: the tile is also
 // written transposed); four waves of 64 x 64, i.e. 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.
 // Accumulation: fp32 in the matrix cores over 1024 tokens, then added into a second fp32 sum,
 // so the rounding of the long sum over M grows with M / 1024 + 1024, not with M.
 #include <type_traits>
+#include <utility>
 
 #include "awq_internal.h"
 
@@ -56,20 +58,24 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int gd_swz(int row) { return 2 * (row & 3); }
 
-// Element (k1, k2) of G, g, from a tile with k1b <= k2b: its hi and lo parts go to rows k1 and
-// K + k1 of the stack.  Off the tile diagonal (off_diag: k1b < k2b) the transposed element
-// (k2, k1) is written too.  Triangular form: T[k1, k2] = 2 g above the diagonal, g on it, and 0
-// below it (so the transposed element of an off-diagonal tile is 0).
-__device__ __forceinline__ void store_g(uint16_t* __restrict__ Gs, int64_t K, int64_t k1, int64_t k2, bool off_diag,
+// Element (k1, k2) of G, g, from a tile with k1b <= k2b: its hi and lo parts go to row k1 of Tp
+// [K x 2K], columns 64 (k2 / 32) + k2 % 32 and 32 more.  Off the tile diagonal (off_diag:
+// k1b < k2b) the transposed element (k2, k1) is written too.  Triangular form: T[k1, k2] = 2 g
+// above the diagonal, g on it, and 0 below it (so the transposed element of an off-diagonal
+// tile is 0).
+__device__ __forceinline__ int64_t tp_at(int64_t K, int64_t row, int64_t col) {
+  return row * 2 * K + 64 * (col >> 5) + (col & 31);
+}
+__device__ __forceinline__ void store_g(uint16_t* __restrict__ Tp, int64_t K, int64_t k1, int64_t k2, bool off_diag,
                                         bool tri, float g) {
   const float t = !tri || k1 == k2 ? g : (k1 < k2 ? 2.0f * g : 0.0f);
   const uint16_t hi = bf16_bits(t);
   const uint16_t lo = bf16_bits(t - __uint_as_float((uint32_t)hi << 16));
-  Gs[k1 * K + k2] = hi;
-  Gs[(K + k1) * K + k2] = lo;
+  Tp[tp_at(K, k1, k2)] = hi;
+  Tp[tp_at(K, k1, k2) + 32] = lo;
   if (off_diag) {
-    Gs[k2 * K + k1] = tri ? (uint16_t)0 : hi;
-    Gs[(K + k2) * K + k1] = tri ? (uint16_t)0 : lo;
+    Tp[tp_at(K, k2, k1)] = tri ? (uint16_t)0 : hi;
+    Tp[tp_at(K, k2, k1) + 32] = tri ? (uint16_t)0 : lo;
   }
 }
 
@@ -311,6 +317,427 @@ GramPlan gram_plan(int64_t M, int64_t K) {
   return p;
 }
 
+// ---- the candidate kernel of the Gram form ------------------------------------------------
+// The stack is stored as Tp [K, 2K] (see store_g): row k' of T_hi and row k' of T_lo
+// interleaved by 32-column chunks, so that one 128-byte line of a row holds chunk c of both.
+// Since (T_hi + T_lo) e^T = T_hi e^T + T_lo e^T, both parts accumulate into the same outputs:
+// a block is a tile of 512 rows k' x 128 outputs n for one candidate, and its step c multiplies
+// the hi and the lo part of chunk c with the same E chunk, 64 v_mfma_f32_32x32x16_bf16 per wave.
+// Per matrix instruction that halves, against a [2K x K] stack of separate hi and lo rows, the
+// quantization, the E stores and reads and the barriers, and the blocks' fixed prologue and
+// epilogue; the bytes of T per instruction stay the same.
+// The pipeline is the direct search kernel's (search.hip), with these differences:
+//   * X (here T) comes as one pair per step, DMA'd one step ahead into the other pair stage:
+//     instruction i (rows 8 i .. 8 i + 7 of the wave's 128) in group 1 + 3 i;
+//   * the 64 matrix instructions of a step run K-half by K-half; within one, row block r of
+//     the wave, hi then lo: group g = 32 h + 8 r + 4 part + cc.  Each A fragment is read two
+//     blocks of four before its first use (the first two of a step in the previous step);
+//   * the B fragments of the second K-half are read in groups 1-7 and the next chunk's first
+//     K-half in groups 33-39, after the last use of the current ones;
+//   * the quantization of chunk c+2 places element el in group 3 + 3 el, its two stores after
+//     elements 7 and 15.
+// Triangular form: the block's K loop starts at its first row, chunk m0 / 32 (a multiple of 16).
+constexpr int GS_BM = 512, GS_BN = 128, GS_KC = 32;
+constexpr int GS_PROW = GS_KC * 2;            // bytes of an E row (one chunk)
+constexpr int GS_XROW = 2 * GS_PROW;          // bytes of a T pair row (hi and lo chunk)
+constexpr int GS_XPSTAGE = GS_BM * GS_XROW;   // 64 KiB
+constexpr int GS_ESTAGE = GS_BN * GS_PROW;    // 8 KiB
+constexpr int GS_NES = 3;
+constexpr int GS_SRG = kGroup * 8;            // one group's (s, 1/s) pairs: 1 KiB
+#define AWQ_LDS_G __attribute__((address_space(3)))
+
+__device__ __forceinline__ int gs_swz(int row) { return (row >> 2) & 3; }   // E rows
+__device__ __forceinline__ int gs_xswz(int row) { return (row >> 1) & 7; }  // T pair rows
+__device__ __forceinline__ float gs_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float gs_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ uint32_t gs_pack(float a, float b) {
+  const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+struct GsWSet {
+  uint4 w[2];  // this lane's 8 bf16 channels of its rows r0 and r1
+};
+// f(integral_constant<int, G>) for every G of the sequence, in order: the group index is a
+// compile-time constant in every call, whatever the size of the step
+template <typename F, int... G>
+__device__ __forceinline__ void gs_each(F&& f, std::integer_sequence<int, G...>) {
+  (f(std::integral_constant<int, G>{}), ...);
+}
+struct GsRowQ {
+  float delta, inv, lo, hi;
+};
+
+__global__ __launch_bounds__(256, 1) void gram_search_kernel(
+    const uint16_t* __restrict__ Tp, int64_t K, const WSegs segs, const float2* __restrict__ sr_tab,
+    const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles, bool tri,
+    double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[GS_XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[GS_XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[GS_XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[GS_XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t es[GS_NES * GS_ESTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * GS_SRG];
+  __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * GS_SRG];
+
+  // XCD x (= b % 8) runs its blocks l = b / 8 in order: row tile mt = l / (spx n_grid), then
+  // output tile ((x + mt) % 8) + 8 s, s < spx = ceil(nt_count / 8), candidate-fastest.  Blocks of
+  // the triangular form differ in length with their row tile, so every XCD works on the same row
+  // tile at a time; its resident blocks share that tile's rows and a few W tiles in its L2.
+  const int64_t b = blockIdx.x;
+  const int64_t spx = (nt_count + 7) >> 3, per_m = spx * n_grid, l = b >> 3;
+  const int64_t mt = l / per_m, rr = l - mt * per_m, sj = rr / n_grid;
+  const int64_t ntile = (((b & 7) + mt) & 7) + 8 * sj;
+  if (mt * nt_count >= tiles || ntile >= nt_count) return;
+  const int64_t tile = mt * nt_count + ntile;
+  const int al = (int)(rr - sj * n_grid);
+  const int64_t m0 = mt * GS_BM;      // first row of T
+  const int64_t n0 = ntile * GS_BN;   // in the padded row space of all weights
+  const WSel sel = select_wseg(segs, ntile);
+  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(sel.w);
+  const int64_t N = sel.n, ldw = sel.ldw, n0w = sel.n0;
+  const int G = (int)(K / kGroup);
+  const int64_t NP = nt_count * GS_BN;
+  const int nchunks = (int)(K / GS_KC);
+  const int c0 = tri ? (int)(m0 / GS_KC) : 0;
+  const int64_t ldx = 2 * K;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // rows of T past K (and rows of W past N) read as zero; offsets stay below 2^31 (host: 512
+  // rows of Tp, 128 rows of W)
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t xrsrc = rsrc(Tp + m0 * ldx, (K - m0) * ldx * 2);
+  const __amdgpu_buffer_rsrc_t wrsrc = rsrc(W + n0w * ldw, (N - n0w) * ldw * 2);
+  const __amdgpu_buffer_rsrc_t srsrc = rsrc(sr_tab + (int64_t)al * K, K * 8);
+  const __amdgpu_buffer_rsrc_t prsrc = rsrc(params + (int64_t)al * G * NP, (int64_t)G * NP * 8);
+  // T copy instruction i (0..15) of wave w fills pair rows 128 w + 8 i + lane / 8, slot lane % 8,
+  // with the global 16-byte piece slot ^ gs_xswz(row)
+  uint32_t xoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = wave * 128 + 8 * i + (lane >> 3);
+    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 7) ^ gs_xswz(row)) * 16));
+  }
+  const uint32_t xrow16 = (uint32_t)(16 * ldx * 2);
+  const int xwave = wave * 64 * GS_XROW;  // this wave's 64 rows in a half stage
+  // quantization: rows r0, r1 of the E tile, channel piece q4 of each chunk
+  const int q4 = lane & 3;
+  const int r0 = wave * 32 + (lane >> 2), r1 = r0 + 16;
+  const uint32_t woff0 = (uint32_t)(r0 * ldw * 2 + q4 * 16);
+  const uint32_t woff1 = (uint32_t)(r1 * ldw * 2 + q4 * 16);
+  const int eslot0 = r0 * GS_PROW + ((q4 ^ gs_swz(r0)) * 16);
+  const int eslot1 = r1 * GS_PROW + ((q4 ^ gs_swz(r1)) * 16);
+  const bool live0 = n0w + r0 < N, live1 = n0w + r1 < N;
+  const int poff = (int)((n0 + 32 * wave + 2 * (lane >> 2)) * 8);
+  // fragment reads: lane reads row (32 t + fr), 16-byte piece 2 h + fh of K-half h; in a pair
+  // row the hi chunk is pieces 0-3, the lo chunk pieces 4-7
+  const int fr = lane & 31, fh = lane >> 5;
+  const int efoff0 = fr * GS_PROW + (((0 + fh) ^ gs_swz(fr)) * 16);
+  const int efoff1 = fr * GS_PROW + (((2 + fh) ^ gs_swz(fr)) * 16);
+  auto xfoff = [&](int part, int h) { return fr * GS_XROW + (((4 * part + 2 * h + fh) ^ gs_xswz(fr)) * 16); };
+
+  auto dma_x_one = [&](uint8_t* xh, int i, int p) {  // instruction i of pair p into half stage xh
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS_G void*)(xh + xwave + (i & 7) * 1024), 16,
+                                             (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * GS_XROW),
+                                             0, 0);
+  };
+  auto load_w = [&](GsWSet& S, int i, int cb, int j) {
+    S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           wrsrc, (int)(i == 0 ? woff0 : woff1) + j * (GS_KC * 2), cb, 0));
+  };
+  auto load_p = [&](int g) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prsrc, poff, (int)(g * NP * 8), 0));
+  };
+  auto dma_sr = [&](uint8_t* table, int g) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (AWQ_LDS_G void*)(table + GS_SRG * wave), 16, 16 * lane,
+                                             g * GS_SRG, 0, 0);
+  };
+  auto sr_addr = [&](const uint8_t* table, int c) {
+    return table + GS_SRG * wave + (32 * (c & 3) + 8 * q4) * 8;
+  };
+  auto row_setup = [&](const float4& P, int i) {
+    const bool live = i == 0 ? live0 : live1;
+    GsRowQ q;
+    q.delta = live ? (i == 0 ? P.x : P.z) : 1.0f;  // rows past N: Delta 1, z 0, w 0: e = 0
+    const float z = live ? (i == 0 ? P.y : P.w) : 0.0f;
+    q.inv = __builtin_amdgcn_rcpf(q.delta);  // search only; the pack divides exactly
+    q.lo = -z;
+    q.hi = 15.0f - z;
+    return q;
+  };
+  auto elem = [&](const GsWSet& S, const float4* sv, const GsRowQ& q, int i, int j) {
+    const uint4& w4 = S.w[i];
+    const uint32_t u = j < 2 ? w4.x : j < 4 ? w4.y : j < 6 ? w4.z : w4.w;
+    const float w = (j & 1) ? gs_hi(u) : gs_lo(u);
+    const float s = (j & 1) ? sv[j >> 1].z : sv[j >> 1].x;
+    const float rs = (j & 1) ? sv[j >> 1].w : sv[j >> 1].y;
+    const float v = w * s;                                    // S W
+    const float r = rintf(v * q.inv);                         // rne(v / Delta)
+    const float qz = __builtin_amdgcn_fmed3f(r, q.lo, q.hi);  // clamp(r + z, 0, 15) - z
+    return fmaf(-(qz * q.delta), rs, w);                      // w - Delta (q - z) / s
+  };
+  auto store_piece = [&](uint8_t* estage, int slot, const float* e8) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pk[h] = gs_pack(e8[2 * h], e8[2 * h + 1]);
+    *reinterpret_cast<uint4*>(estage + slot) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  };
+  auto quantize_all = [&](const GsWSet& S, const float4& P, int c, uint8_t* estage) {  // prologue only
+    float4 sv[4];
+    const uint8_t* sa = sr_addr(srs0, c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
+    const GsRowQ q0 = row_setup(P, 0), q1 = row_setup(P, 1);
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, sv, q0, 0, j);
+    store_piece(estage, eslot0, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, sv, q1, 1, j);
+    store_piece(estage, eslot1, e);
+  };
+  auto frag = [&](const uint8_t* base, int fo) { return *reinterpret_cast<const bf16x8*>(base + fo); };
+  auto vm_wait = [](auto n) {  // s_waitcnt vmcnt(n), other counters untouched
+    constexpr int v = decltype(n)::value;
+    __builtin_amdgcn_s_waitcnt((v & 0xf) | (0x7 << 4) | (0xf << 8) | ((v >> 4) << 14));
+  };
+  constexpr int kWaitLgkm0 = 0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
+
+  GsWSet S0, S1, S2, S3;  // W words of chunk c live in set c % 4
+  float4 PC, PN;          // ranges of the group being quantized, of the next group
+  GsRowQ q0, q1;
+  // Prologue: group c0 / 4's scale table and ranges, W of chunks c0 .. c0 + 3, pair c0 of T;
+  // chunks c0 and c0 + 1 are quantized.
+  dma_sr(srs0, c0 >> 2);
+  PC = load_p(c0 >> 2);
+  load_w(S0, 0, c0 * (GS_KC * 2), 0);
+  load_w(S1, 0, c0 * (GS_KC * 2), 1);
+  load_w(S0, 1, c0 * (GS_KC * 2), 0);
+  load_w(S1, 1, c0 * (GS_KC * 2), 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, c0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(S2, 0, c0 * (GS_KC * 2), 2);
+  load_w(S3, 0, c0 * (GS_KC * 2), 3);
+  load_w(S2, 1, c0 * (GS_KC * 2), 2);
+  load_w(S3, 1, c0 * (GS_KC * 2), 3);
+  __builtin_amdgcn_sched_barrier(0);
+  vm_wait(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  quantize_all(S0, PC, 0, es + 0 * GS_ESTAGE);  // chunks c0, c0 + 1: positions 0, 1 of their group
+  quantize_all(S1, PC, 1, es + 1 * GS_ESTAGE);
+  q0 = row_setup(PC, 0);
+  q1 = row_setup(PC, 1);
+  bf16x8 b0[4], an0, an1;  // B fragments of K-half 0 of chunk c; A fragments of blocks 0, 1 of step c
+  {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * GS_PROW, efoff0);
+    an0 = frag(xp0lo + xwave, xfoff(0, 0));
+    an1 = frag(xp0lo + xwave, xfoff(1, 0));
+    asm volatile("" ::"v"(S2.w[0].x), "v"(S2.w[0].y), "v"(S2.w[0].z), "v"(S2.w[0].w), "v"(S2.w[1].x),
+                 "v"(S2.w[1].y), "v"(S2.w[1].z), "v"(S2.w[1].w));
+    asm volatile("" ::"v"(S3.w[0].x), "v"(S3.w[0].y), "v"(S3.w[0].z), "v"(S3.w[0].w), "v"(S3.w[1].x),
+                 "v"(S3.w[1].y), "v"(S3.w[1].z), "v"(S3.w[1].w));
+  }
+
+  // Step c (k = c % 4 known at compile time): xc is pair c's stage, xd pair c+1's.
+  // vmcnt accounting (even steps: 4 W loads in groups 0-3, 2 more in groups 4, 5 when k = 0, and
+  // 16 T copies in groups 1, 4, ..., 46; odd steps: the 16 copies):
+  //   * group 8: pair c's rows 64-127 (copied in the previous step) landed before their first read;
+  //     what may be outstanding is this step's loads before group 8 (even: 4 W, 2 when k = 0,
+  //     3 copies; odd: 3 copies);
+  //   * group 56: pair c+1's rows 0-63 (this step's copies 0-7) landed before the next step's
+  //     first fragments are read: only copies 8-15 may be outstanding.  Every earlier load,
+  //     including the scale table DMA of a k = 0 step, has landed then.
+  auto step = [&](int c8, auto jc, const uint8_t* xclo, const uint8_t* xchi, uint8_t* xdlo, uint8_t* xdhi,
+                  const GsWSet& Q, GsWSet& F4, GsWSet& F5, const uint8_t* srq, uint8_t* srn, int& eo0, int& eo1,
+                  int& eo2) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int k = j & 3;
+    constexpr bool even = (k & 1) == 0;
+    const int c = c8 + j;
+    const int cb = c8 * (GS_KC * 2);
+    const int gn = (c8 >> 2) + (j >> 2) + 1;  // next group (k = 0 steps)
+    const uint8_t* ec = es + eo0;
+    const uint8_t* en = es + eo1;
+    uint8_t* eq = es + eo2;
+    const uint8_t* sa = sr_addr(srq, k + 2);
+    // A fragment of row block r of pair stage (lo, hi), part p, K-half h
+    auto xa = [&](const uint8_t* lo, const uint8_t* hi, int r, int p, int h) {
+      return frag((r < 2 ? lo : hi) + xwave + (r & 1) * 32 * GS_XROW, xfoff(p, h));
+    };
+    if (k == 2) {  // chunks c+2 .. c+5 of this quad after the first two: next group
+      PC = PN;
+      q0 = row_setup(PC, 0);
+      q1 = row_setup(PC, 1);
+    }
+    bf16x8 a[16], b1[4];
+    a[0] = an0;
+    a[1] = an1;
+    float4 sv[4];
+    float e[16];
+    __builtin_amdgcn_sched_barrier(0);
+    gs_each([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int blk = g >> 2, h = blk >> 3, r = (blk >> 1) & 3, cc = g & 3;
+      if (g == 8) vm_wait(std::integral_constant<int, even ? (k == 0 ? 9 : 7) : 3>{});
+      // the A fragment of block blk + 2, two blocks ahead (blocks 0, 1 of the next step: groups 56, 60)
+      if ((g & 3) == 0 && blk + 2 < 16) {
+        constexpr int nb = blk + 2 < 16 ? blk + 2 : 15;
+        a[nb] = xa(xclo, xchi, (nb >> 1) & 3, nb & 1, nb >> 3);
+      }
+      if (g == 56) vm_wait(std::integral_constant<int, 8>{});
+      if (g == 56) an0 = xa(xdlo, xdhi, 0, 0, 0);
+      if (g == 60) an1 = xa(xdlo, xdhi, 0, 1, 0);
+      acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[blk], h == 0 ? b0[cc] : b1[cc], acc[r][cc], 0, 0, 0);
+      if (g == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
+      }
+      if (g < 8 && (g & 1)) b1[g >> 1] = frag(ec + (g >> 1) * 32 * GS_PROW, efoff1);
+      if (g >= 33 && g < 40 && (g & 1)) b0[(g - 33) >> 1] = frag(en + ((g - 33) >> 1) * 32 * GS_PROW, efoff0);
+      // element el in group 3 + 3 el: row r0 in groups 3-24, row r1 in 27-48
+      constexpr int el = g >= 3 && g <= 48 && g % 3 == 0 ? g / 3 - 1 : -1;
+      if (el >= 0) {
+        e[el] = el < 8 ? elem(Q, sv, q0, 0, el) : elem(Q, sv, q1, 1, el - 8);
+        asm volatile("" : "+v"(e[el]));  // keep the element in this group
+      }
+      if (g == 25) store_piece(eq, eslot0, e);
+      if (g == 49) store_piece(eq, eslot1, e + 8);
+      if (even) {
+        if (g == 0) load_w(F4, 0, cb, j + 4);
+        if (g == 1) load_w(F5, 0, cb, j + 5);
+        if (g == 2) load_w(F4, 1, cb, j + 4);
+        if (g == 3) load_w(F5, 1, cb, j + 5);
+        if (k == 0 && g == 4) PN = load_p(gn);
+        if (k == 0 && g == 5) dma_sr(srn, gn);
+      }
+      if (g <= 46 && (g - 1) % 3 == 0) dma_x_one((g - 1) / 3 < 8 ? xdlo : xdhi, (g - 1) / 3, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }, std::make_integer_sequence<int, 64>{});
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // E stores of chunk c+2, fragment reads
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int et = eo0;
+    eo0 = eo1;
+    eo1 = eo2;
+    eo2 = et;
+  };
+
+  // The body covers two groups (8 steps) so that each scale table has a static role; the pair
+  // stages alternate every step.  nchunks - c0 is a multiple of 4 (c0 a multiple of 16).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+  int eo0 = 0, eo1 = GS_ESTAGE, eo2 = 2 * GS_ESTAGE;
+  int c = c0;
+  for (; c + 8 <= nchunks; c += 8) {
+    step(c, I0{}, xp0lo, xp0hi, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, xp1lo, xp1hi, xp0lo, xp0hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, xp0lo, xp0hi, xp1lo, xp1hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I4{}, xp0lo, xp0hi, xp1lo, xp1hi, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I5{}, xp1lo, xp1hi, xp0lo, xp0hi, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I6{}, xp0lo, xp0hi, xp1lo, xp1hi, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I7{}, xp1lo, xp1hi, xp0lo, xp0hi, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
+  }
+  if (c < nchunks) {  // K / 128 odd: one more group
+    step(c, I0{}, xp0lo, xp0hi, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, xp1lo, xp1hi, xp0lo, xp0hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, xp0lo, xp0hi, xp1lo, xp1hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no copy (the last ones read past the end) outlives the block
+
+  // This wave's 128 rows are rows kb .. kb + 127 of T: one whole group gq of K (rows past K hold
+  // zeros and are skipped).  Lane l's outputs sit at k' = kb + 32 r + 8 (i / 4) + 4 (l / 32) + i % 4
+  // and n = n0 + 32 cc + l % 32, where it recomputes e = E[n, k'] exactly as the K loop formed it
+  // (before the bf16 rounding) and adds acc e.
+  double ss = 0.0;
+  const int64_t kb = m0 + 128 * wave;
+  if (kb < K) {
+    const int gq = (int)(kb / kGroup);
+    GsRowQ rq[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int nl = 32 * cc + (lane & 31);
+      const float2 P = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      prsrc, (int)(((int64_t)gq * NP + range_slot(n0 + nl)) * 8), 0, 0));
+      const bool live = n0w + nl < N;
+      rq[cc].delta = live ? P.x : 1.0f;  // rows past N: Delta 1, z 0, w 0 (read as zero): e = 0
+      const float z = live ? P.y : 0.0f;
+      rq[cc].inv = __builtin_amdgcn_rcpf(rq[cc].delta);
+      rq[cc].lo = -z;
+      rq[cc].hi = 15.0f - z;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4 sv[4][2];  // (s, 1/s) of the four consecutive channels of each i / 4
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int kk = (int)kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          sv[i4][hh] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, kk * 8 + 16 * hh, 0, 0));
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int nl = 32 * cc + (lane & 31);
+        float t = 0.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int kk = (int)kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
+          const uint2 w4 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                         wrsrc, (int)(nl * ldw * 2 + kk * 2), 0, 0));
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t u = jj < 2 ? w4.x : w4.y;
+            const float w = (jj & 1) ? gs_hi(u) : gs_lo(u);
+            const float4& sp = sv[i4][jj >> 1];
+            const float s = (jj & 1) ? sp.z : sp.x, rs = (jj & 1) ? sp.w : sp.y;
+            const float v = w * s;
+            const float q = __builtin_amdgcn_fmed3f(rintf(v * rq[cc].inv), rq[cc].lo, rq[cc].hi);
+            const float e = fmaf(-(q * rq[cc].delta), rs, w);
+            t = fmaf(acc[r][cc][4 * i4 + jj], e, t);
+          }
+        }
+        ss += (double)t;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  // every wave is past its last LDS access (the barrier ending the last step), so the first E
+  // stage can hold the four wave sums
+  double* red = reinterpret_cast<double*>(es);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  if (tid == 0) partial[(int64_t)al * tiles + tile] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
 }  // namespace
 
 size_t gram_partial_bytes(int64_t M, int64_t K) {
@@ -328,6 +755,16 @@ hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uin
   if (e != hipSuccess || p.r == 0) return e;
   gram_fixup_kernel<<<dim3((unsigned)(GT * GT / 256), (unsigned)p.r), 256, 0, st>>>(partial, K, p.full, p.S, Gs,
                                                                                      tri);
+  return hipGetLastError();
+}
+
+hipError_t launch_search_gram(const uint16_t* Tp, int64_t K, const WSegs& W, const float2* sr_tab,
+                              const float2* params, int n_grid, const SearchPlan& plan, double* partial,
+                              hipStream_t st) {
+  // eight XCD slots per row tile and output-tile group of eight (see the kernel)
+  const dim3 grid((unsigned)(8 * plan.mt * ((plan.nt + 7) / 8) * n_grid));
+  gram_search_kernel<<<grid, 256, 0, st>>>(Tp, K, W, sr_tab, params, n_grid, plan.nt, plan.tiles,
+                                           gram_triangular(K), partial);
   return hipGetLastError();
 }
 

@@ -351,18 +351,10 @@ struct RowQ {
   float delta, inv, lo, hi;
 };
 
-// GRAM: X is the stacked [G_hi; G_lo] (2K rows, gram.hip) and the block's result is
-// sum over its outputs of (Gs E^T)[k', n] E[n, k' mod K] instead of the squares.  With tri the
-// stack holds the upper-triangular T instead of G (zero below the diagonal), so a block whose
-// rows are rows k0 .. k0 + 511 of T starts its K loop at chunk 8 floor(k0 / 256) (a multiple of
-// eight chunks, so that every stage keeps its role); a block whose rows straddle T_hi and T_lo
-// starts at 0.  Blocks then differ in length, so the GRAM grid spreads each row tile's output
-// tiles over the eight XCDs (below) instead of giving each XCD a run of row tiles.
-template <bool GRAM>
 __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const WSegs segs, int64_t K,
     const float2* __restrict__ sr_tab, const float2* __restrict__ params, int n_grid,
-    int64_t nt_count, int64_t tiles, int64_t per_xcd, double* __restrict__ partial, bool tri) {
+    int64_t nt_count, int64_t tiles, int64_t per_xcd, double* __restrict__ partial) {
   // X pair stages (pairs 0, 2, 4, ... in xp0; 1, 3, 5, ... in xp1), each split into the first
   // and the last 64 of every wave's 128 rows: distinct LDS objects, so reads of one half never
   // wait for the DMA into the other
@@ -376,26 +368,10 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * SRG];
 
   const int64_t b = blockIdx.x;
-  int64_t tile;
-  int al;
-  if constexpr (GRAM) {
-    // XCD x (= b % 8) runs its blocks l = b / 8 in order: row tile mt = l / (spx n_grid), then
-    // output tile ((x + mt) % 8) + 8 s, s < spx = ceil(nt_count / 8), candidate-fastest.  Every
-    // XCD thus works on the same row tile at a time (equal work per XCD when 8 divides
-    // nt_count; the rotation spreads the remainder), and its resident blocks share that tile's
-    // rows and a few W tiles in its L2.  Slots past the last output tile return at once.
-    const int64_t spx = (nt_count + 7) >> 3, per_m = spx * n_grid, l = b >> 3;
-    const int64_t mt = l / per_m, r = l - mt * per_m, sj = r / n_grid;
-    const int64_t nt = (((b & 7) + mt) & 7) + 8 * sj;
-    if (mt * nt_count >= tiles || nt >= nt_count) return;
-    tile = mt * nt_count + nt;
-    al = (int)(r - sj * n_grid);
-  } else {
-    const int64_t L = (b & 7) * per_xcd + (b >> 3);
-    if (L >= tiles * n_grid) return;
-    tile = L / n_grid;
-    al = (int)(L - tile * n_grid);
-  }
+  const int64_t L = (b & 7) * per_xcd + (b >> 3);
+  if (L >= tiles * n_grid) return;
+  const int64_t tile = L / n_grid;
+  const int al = (int)(L - tile * n_grid);
   const int64_t m0 = (tile / nt_count) * BM;
   const int64_t n0 = (tile % nt_count) * BN;  // in the padded row space of all weights
   // the weight this tile belongs to; n0w: the tile's first row within it
@@ -405,14 +381,6 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   const int G = (int)(K / kGroup);
   const int64_t NP = nt_count * BN;
   const int nchunks = (int)(K / PKC);
-  // first chunk of the K loop: 0, or (triangular Gram form) where the block's rows of T begin
-  int c0 = 0;
-  if constexpr (GRAM) {
-    if (tri) {
-      const int64_t k0 = m0 >= K ? m0 - K : (m0 + BM <= K ? m0 : 0);
-      c0 = (int)(k0 / 256) * 8;
-    }
-  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -547,26 +515,26 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   WSet S0, S1, S2, S3;  // W words of chunk c live in set c % 4
   float4 PC, PN;        // ranges of the group being quantized, of the next group
   RowQ q0, q1;          // row_setup of PC (rows r0, r1), renewed when PC changes
-  // Prologue (once per block): group c0 / 4's scale table and ranges, W of chunks c0 .. c0 + 3
-  // and the X pair of chunks c0 and c0 + 1, then chunks c0 and c0 + 1 are quantized.
-  dma_sr(srs0, c0 >> 2);
-  PC = load_p(c0 >> 2);
-  load_w(S0, 0, c0 * (PKC * 2), 0);
-  load_w(S1, 0, c0 * (PKC * 2), 1);
-  load_w(S0, 1, c0 * (PKC * 2), 0);
-  load_w(S1, 1, c0 * (PKC * 2), 1);
+  // Prologue (once per block): group 0's scale table and ranges, W of chunks 0-3 and the X
+  // pair of chunks 0 and 1, then chunks 0 and 1 are quantized.
+  dma_sr(srs0, 0);
+  PC = load_p(0);
+  load_w(S0, 0, 0, 0);
+  load_w(S1, 0, 0, 1);
+  load_w(S0, 1, 0, 0);
+  load_w(S1, 1, 0, 1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, c0 >> 1);
+  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(S2, 0, c0 * (PKC * 2), 2);
-  load_w(S3, 0, c0 * (PKC * 2), 3);
-  load_w(S2, 1, c0 * (PKC * 2), 2);
-  load_w(S3, 1, c0 * (PKC * 2), 3);
+  load_w(S2, 0, 0, 2);
+  load_w(S3, 0, 0, 3);
+  load_w(S2, 1, 0, 2);
+  load_w(S3, 1, 0, 3);
   __builtin_amdgcn_sched_barrier(0);
   vm_wait(std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
-  quantize_all(S0, PC, 0, es + 0 * ESTAGE);  // chunks c0, c0 + 1: positions 0, 1 of their group
+  quantize_all(S0, PC, 0, es + 0 * ESTAGE);
   quantize_all(S1, PC, 1, es + 1 * ESTAGE);
   q0 = row_setup(PC, 0);
   q1 = row_setup(PC, 1);
@@ -715,7 +683,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   using I6 = std::integral_constant<int, 6>;
   using I7 = std::integral_constant<int, 7>;
   int eo0 = 0, eo1 = ESTAGE, eo2 = 2 * ESTAGE;
-  int c = c0;
+  int c = 0;
   for (; c + 8 <= nchunks; c += 8) {
     step(c, I0{}, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
     step(c, I1{}, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
@@ -734,71 +702,15 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   }
 
   double ss = 0.0;
-  if constexpr (GRAM) {
-    // This wave's 128 rows are rows k' = (m0 + 128 wave + ...) mod K of G (the first K rows
-    // of X hold G_hi, the next K G_lo): one whole group gq of K.  Lane l's outputs sit at
-    // k' = kb + 32 r + 8 (i / 4) + 4 (l / 32) + i % 4 and n = n0 + 32 c + l % 32, where it
-    // recomputes e = E[n, k'] exactly as the K loop formed it (before the bf16 rounding).
-    const int kb = (int)((m0 + (int64_t)WAVE_ROWS * wave) % K);
-    const int gq = kb / kGroup;
-    RowQ rq[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int nl = 32 * c + (lane & 31);
-      const float2 P = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                      prsrc, (int)(((int64_t)gq * NP + range_slot(n0 + nl)) * 8), 0, 0));
-      const bool live = n0w + nl < N;
-      rq[c].delta = live ? P.x : 1.0f;  // rows past N: Delta 1, z 0, w 0 (read as zero): e = 0
-      const float z = live ? P.y : 0.0f;
-      rq[c].inv = __builtin_amdgcn_rcpf(rq[c].delta);
-      rq[c].lo = -z;
-      rq[c].hi = 15.0f - z;
+      float t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t = fmaf(acc[r][c][i], acc[r][c][i], t);
+      ss += (double)t;
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float4 sv[4][2];  // (s, 1/s) of the four consecutive channels of each i / 4
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int kk = kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          sv[i4][h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, kk * 8 + 16 * h, 0, 0));
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int nl = 32 * c + (lane & 31);
-        float t = 0.0f;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int kk = kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
-          const uint2 w4 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                         wrsrc, (int)(nl * ldw * 2 + kk * 2), 0, 0));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t u = j < 2 ? w4.x : w4.y;
-            const float w = (j & 1) ? bf16_hi(u) : bf16_lo(u);
-            const float4& sp = sv[i4][j >> 1];
-            const float s = (j & 1) ? sp.z : sp.x, rs = (j & 1) ? sp.w : sp.y;
-            const float v = w * s;
-            const float q = __builtin_amdgcn_fmed3f(rintf(v * rq[c].inv), rq[c].lo, rq[c].hi);
-            const float e = fmaf(-(q * rq[c].delta), rs, w);
-            t = fmaf(acc[r][c][4 * i4 + j], e, t);
-          }
-        }
-        ss += (double)t;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float t = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) t = fmaf(acc[r][c][i], acc[r][c][i], t);
-        ss += (double)t;
-      }
-  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   // every wave is past its last LDS access (the barrier ending the last step), so the first
@@ -825,24 +737,16 @@ SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
                                bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
                                const float2* sr_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st, bool gram) {
+                               const SearchPlan& plan, double* partial, hipStream_t st) {
   const int64_t per_xcd = plan.blocks / 8;
   const dim3 grid((unsigned)plan.blocks);
 #define AWQ_LAUNCH(XF, WF)                                                                  \
   search_fused_kernel<XF, WF><<<grid, THREADS, 0, st>>>(X, M, ldx, W, K, s_tab, rs_tab, params, \
                                                         n_grid, plan.nt, plan.tiles, per_xcd,   \
                                                         partial)
-  if (gram) {  // bf16 operands only (host-checked); eight XCD slots per row tile (see the kernel)
-    const dim3 ggrid((unsigned)(8 * plan.mt * ((plan.nt + 7) / 8) * n_grid));
-    search_pipelined_kernel<true><<<ggrid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K,
-                                                             sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd,
-                                                             partial, gram_triangular(K));
-    return hipGetLastError();
-  }
   if (!xf32 && !wf32) {
-    search_pipelined_kernel<false><<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K,
-                                                             sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd,
-                                                             partial, false);
+    search_pipelined_kernel<<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K, sr_tab,
+                                                      params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
     return hipGetLastError();
   }
   if (xf32 && wf32)

@@ -183,7 +183,7 @@ def test_search_multi_workspace_pads_each_weight(L):
 @pytest.mark.parametrize("kw,status", [
     (dict(X=None), INVALID), (dict(W=None), INVALID), (dict(xt=F32), UNSUP), (dict(wt=F32), UNSUP),
     (dict(group=64), UNSUP), (dict(n_grid=0), INVALID), (dict(a=None), INVALID), (dict(ws=None), WS),
-    (dict(wsb=1000), WS), (dict(K=1 << 21, ldx=1 << 21, ldw=1 << 21), SHAPE),  # 512 rows of G span 2^31
+    (dict(wsb=1000), WS), (dict(K=1 << 20, ldx=1 << 20, ldw=1 << 20), SHAPE),  # 512 rows of T span 2^31
 ])
 def test_search_gram_argument_errors(L, kw, status):
     a = dict(X=P, xt=BF16, M=64, K=256, ldx=256, W=P, wt=BF16, N=128, ldw=256, a=P, group=128, n_grid=20,
@@ -195,18 +195,19 @@ def test_search_gram_argument_errors(L, kw, status):
 
 
 def test_search_gram_workspace(L):
-    # the search workspace for 2K rows of the left operand plus the 2K x K bf16 stack of G
+    # the search workspace for K rows of the left operand (T as K x 2K: hi and lo interleaved)
+    # plus that K x 2K bf16 matrix
     K, N = 4096, 4096
     assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= \
-        L.awq_search_workspace_bytes(2 * K, K, N, 128, 20) + 2 * K * K * 2
+        L.awq_search_workspace_bytes(K, K, N, 128, 20) + 2 * K * K * 2
     assert L.awq_search_gram_workspace_bytes(16384, 4000, N, 128, 20) == 0
     assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 65) == 0
     # plus the fp32 sums of the G tiles split along the tokens: at K = 4096, 528 upper-triangle
     # tiles of 128 x 128, the 16 past the first 512 split into 16 slices of 1024 tokens
-    base = L.awq_search_workspace_bytes(2 * K, K, N, 128, 20) + 2 * K * K * 2
+    base = L.awq_search_workspace_bytes(K, K, N, 128, 20) + 2 * K * K * 2
     assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= base + 16 * 16 * 128 * 128 * 4
     # K = 5120: 820 tiles; the 308 past the first 512 would get one slice each, so none is split
-    base = L.awq_search_workspace_bytes(2 * 5120, 5120, N, 128, 20) + 2 * 5120 * 5120 * 2
+    base = L.awq_search_workspace_bytes(5120, 5120, N, 128, 20) + 2 * 5120 * 5120 * 2
     assert base <= L.awq_search_gram_workspace_bytes(16384, 5120, N, 128, 20) < base + 4096
 
 
