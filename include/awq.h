@@ -189,19 +189,20 @@ AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, i
  * squared error carries the cross terms of X^T X):
  *   sum_{m,n} (X E^T)[m,n]^2 = sum_n E[n,:] G E[n,:]^T,   G = X^T X,
  * with G formed once on the matrix cores (fp32 sums per 1024 tokens, then across blocks) and
- * kept as G_hi + G_lo, two bf16 matrices (16 significand bits of G).  Every candidate then
- * multiplies the [2K, K] stack [G_hi; G_lo] with E^T (2 * 2 K^2 N flop instead of 2 M K N)
- * and dots each output with E[n, k'].  For K > 512 the stack holds T = diag(G) + 2 triu(G, 1)
- * instead (the same quadratic form, zero below the diagonal), and each 512-row block of the
- * product skips the columns left of its first row: about 2 K (K + 512) N flop per candidate,
- * less work than the direct form when M > K + 512 (the cost of G aside).  The losses differ
+ * kept as G_hi + G_lo, two bf16 matrices (16 significand bits of G) interleaved in one
+ * [K, 2K] matrix.  Every candidate then multiplies both with E^T into the same outputs
+ * (2 * 2 K^2 N flop instead of 2 M K N) and dots each output with E[n, k'].  For K > 512 the
+ * matrix holds T = diag(G) + 2 triu(G, 1) instead (the same quadratic form, zero below the
+ * diagonal), and each 512-row block of the product skips the columns left of its first row:
+ * about 2 K (K + 512) N flop per candidate, less work than the direct form when
+ * M > K + 512 (the cost of G aside).  The losses differ
  * from awq_search's only by rounding: G's representation (2^-16 relative per entry) and its
  * sums, and the sums over k of products that cancel (the quadratic form), where the direct
  * form sums squares.  Candidates, codes, tie rule and outputs as awq_search.
- *   X, W   AWQ_DTYPE_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); 512 x K bf16 must span less
- *          than 2^31 bytes
+ *   X, W   AWQ_DTYPE_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); 512 x 2K bf16 must span less
+ *          than 2^31 bytes (K < 2^20)
  *   ws     workspace of at least awq_search_gram_workspace_bytes(...) bytes: the search
- *          workspace for 2K rows, the stack (2K x K bf16), and fp32 sums of the G tiles that are
+ *          workspace for K rows, the K x 2K bf16 matrix, and fp32 sums of the G tiles that are
  *          split along the tokens to fill the last round of blocks (at most 64 MiB)
  * Other arguments, results and errors as awq_search. */
 AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
