@@ -325,27 +325,35 @@ def layer_step(torch, awq, synth, spec, dev, reps, gram=False):
         row["gram_search_ms"] = g_ms
         row["gram_direct_equiv_tflops"] = flop / (g_ms * 1e-3) / 1e12
         row["gram_speedup_vs_direct_search"] = row["search_ms"] / g_ms
+        row["step_ms_with_gram"] = row["stats_ms"] + g_ms + row["pack_ms"]
+        row["layer_searches_per_s_with_gram"] = 1000.0 / row["step_ms_with_gram"]
         del ws_g
     del X, W, ws_se, ws_st, out
     torch.cuda.empty_cache()
     return row
 
 
+def gram_pays(spec) -> bool:
+    """The Gram form does less work than the direct one when M > K + 512 (its triangular
+    candidate product costs about 2 K (K + 512) N flop against 2 M K N; bf16 only)."""
+    return spec.dtype == "bf16" and spec.M > spec.K + 512
+
+
 def per_config(torch, awq, dev):
     """Every configuration's throughput beside the headline: tiny, attn, down and gate+up as one
     layer each, and the decoder block as its four layers searched in turn (blocks/s), with the
-    Gram form as well for the block's K = 4096 layers (M = 16384 > 2K)."""
+    Gram form as well for every layer where M > K + 512 (gate+up; the block's four layers)."""
     from post_weight_quantization_mean_amd import synth
     reps = {"tiny": 20, "attn": 10, "down": 5, "gate_up": 3}
     res = {}
     for name in ("tiny", "attn", "down", "gate_up"):
         spec = synth.CONFIGS[name].layers[0]
-        res[name] = layer_step(torch, awq, synth, spec, dev, reps[name])
+        res[name] = layer_step(torch, awq, synth, spec, dev, reps[name], gram=gram_pays(spec))
         if name in TARGET_HALF_PEAK:
             res[name]["target_at_half_peak"] = TARGET_HALF_PEAK[name]
     layers = {}
     for spec in synth.CONFIGS["block"].layers:
-        layers[spec.name] = layer_step(torch, awq, synth, spec, dev, 3, gram=spec.K == 4096)
+        layers[spec.name] = layer_step(torch, awq, synth, spec, dev, 3, gram=gram_pays(spec))
     total = sum(r["step_ms"] for r in layers.values())
     best = sum(r["stats_ms"] + r["pack_ms"] + min(r["search_ms"], r.get("gram_search_ms", float("inf")))
                for r in layers.values())

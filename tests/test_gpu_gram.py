@@ -113,15 +113,16 @@ def test_gram_and_direct_agree(awq):
 
 
 GOLDEN_LOSSES = os.path.join(GOLDEN, "oracle_losses.json")
-# the layers the Gram form is for: M > 2K (16384 tokens, K = 4096), so it does less work
-GRAM_KEYS = ["block/qkv", "block/o_proj", "block/gate_up"]
+# the layers the Gram form is for, M > K + 512: the decoder block's (16384 tokens; K = 4096, and
+# K = 14336 for down) and the gate+up configuration (8192 tokens, K = 5120)
+GRAM_KEYS = ["block/qkv", "block/o_proj", "block/gate_up", "block/down", "gate_up/gate_up"]
 
 
 @pytest.mark.parametrize("key", GRAM_KEYS)
 def test_gram_full_size_vs_stored_oracle(awq, key):
-    """The decoder block's K = 4096 layers (M = 16384) in the Gram form against the oracle's
-    losses stored by tests/golden/make_oracle_losses.py (oracle + generator only): every
-    candidate within 1e-3 relative, the chosen candidate by the single-weight rule."""
+    """The layers with M > K + 512 in the Gram form against the oracle's losses stored by
+    tests/golden/make_oracle_losses.py (oracle + generator only): every candidate within 1e-3
+    relative, the chosen candidate by the single-weight rule."""
     g = json.load(open(GOLDEN_LOSSES))[key]
     cfg, name = key.split("/")
     li = [l.name for l in synth.CONFIGS[cfg].layers].index(name)
