@@ -270,18 +270,18 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const awq::SearchPlan plan = awq::search_plan(rows, K, NP, n_grid);
-  uint16_t* Gs = gram ? reinterpret_cast<uint16_t*>(base + gs_off) : nullptr;
+  uint16_t* Tp = gram ? reinterpret_cast<uint16_t*>(base + gs_off) : nullptr;  // [K, 2K] bf16
   float* gpart = gram ? reinterpret_cast<float*>(base + gp_off) : nullptr;
 
   hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
-  if (e == hipSuccess && gram) e = awq::launch_gram(static_cast<const uint16_t*>(X), M, K, ldx, Gs, gpart, s);
+  if (e == hipSuccess && gram) e = awq::launch_gram(static_cast<const uint16_t*>(X), M, K, ldx, Tp, gpart, s);
   for (int i = 0; i < n_weights && e == hipSuccess; ++i)
     e = awq::launch_group_range(Ws[i], wf32, Ns[i], K, ldws[i], s_tab, n_grid, params, segs.tile0[i] * 128,
                                 NP, flags, s);
   if (e == hipSuccess && fused_begin != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
   if (e == hipSuccess && gram)
-    e = awq::launch_search_gram(Gs, K, segs, sr_tab, params, n_grid, plan, partial, s);
+    e = awq::launch_search_gram(Tp, K, segs, sr_tab, params, n_grid, plan, partial, s);
   else if (e == hipSuccess)
     e = awq::launch_search_fused(X, xf32, M, ldx, segs, wf32, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
                                  partial, s);

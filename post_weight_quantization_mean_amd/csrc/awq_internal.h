@@ -135,9 +135,9 @@ hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx,
 // stands for T = diag(X^T X) + 2 triu(X^T X, 1) (zero below the diagonal), and each candidate
 // block's K loop starts at its first row of T
 inline bool gram_triangular(int64_t K) { return K > kSearchBM; }
-// bytes of fp32 slice sums that launch_gram needs beside Gs (0 when no tile is split)
+// bytes of fp32 slice sums that launch_gram needs beside Tp (0 when no tile is split)
 size_t gram_partial_bytes(int64_t M, int64_t K);
-hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,
+hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Tp, float* partial,
                        hipStream_t st);
 // the candidate losses' partial sums in the Gram form (plan: search_plan with K rows)
 hipError_t launch_search_gram(const uint16_t* Tp, int64_t K, const WSegs& W, const float2* sr_tab,

@@ -87,7 +87,7 @@ __device__ __forceinline__ void store_g(uint16_t* __restrict__ Tp, int64_t K, in
 // operand per product, eight bytes per lane per transposed read.
 template <int NST, int TT>
 __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gram_dma_kernel(
-    const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx, uint16_t* __restrict__ Gs, int64_t full,
+    const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx, uint16_t* __restrict__ Tp, int64_t full,
     int S, int64_t slice_tokens, float* __restrict__ partial, bool tri) {
   constexpr int STRIP = TT * GT * 2;  // one strip of a stage
   constexpr int STAGE = 2 * STRIP;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gr
       for (int e = 0; e < 16; ++e) {
         const int64_t k1 = k1b + r1 + 32 * a + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
         const int64_t k2 = k2b + c2 + 32 * c + (lane & 31);
-        store_g(Gs, K, k1, k2, k1b != k2b, tri, tot[a][c][e] + acc[a][c][e]);
+        store_g(Tp, K, k1, k2, k1b != k2b, tri, tot[a][c][e] + acc[a][c][e]);
       }
 }
 
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256, (NST * TT * 512 <= 80 * 1024) ? 2 : 1) void gr
 // starting from 0 -- the order in which a whole tile adds its 1024-token block sums, so with one
 // block per slice the result is the same bits as the whole-tile kernel's.
 __global__ __launch_bounds__(256) void gram_fixup_kernel(const float* __restrict__ partial, int64_t K,
-                                                          int64_t full, int S, uint16_t* __restrict__ Gs, bool tri) {
+                                                          int64_t full, int S, uint16_t* __restrict__ Tp, bool tri) {
   const int64_t u = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // k1 GT + k2, tile-local
   const int k1l = (int)(idx / GT), k2l = (int)(idx % GT);
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void gram_fixup_kernel(const float* __restrict
   const int64_t k1b = i * GT, k2b = (i + rem) * GT;
   float g = 0.0f;
   for (int s = 0; s < S; ++s) g += partial[(u * S + s) * (GT * GT) + idx];
-  store_g(Gs, K, k1b + k1l, k2b + k2l, k1b != k2b, tri, g);
+  store_g(Tp, K, k1b + k1l, k2b + k2l, k1b != k2b, tri, g);
 }
 
 // With tiles = q 512 + r (512: two rounds of one block on each of 256 CUs), the first q 512 tiles
@@ -745,15 +745,15 @@ size_t gram_partial_bytes(int64_t M, int64_t K) {
   return (size_t)(p.r * p.S) * GT * GT * sizeof(float);
 }
 
-hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Gs, float* partial,
+hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Tp, float* partial,
                        hipStream_t st) {
   const GramPlan p = gram_plan(M, K);
   const bool tri = gram_triangular(K);
-  gram_dma_kernel<4, 64><<<(unsigned)(p.full + p.r * p.S), 256, 0, st>>>(X, M, K, ldx, Gs, p.full, p.S,
+  gram_dma_kernel<4, 64><<<(unsigned)(p.full + p.r * p.S), 256, 0, st>>>(X, M, K, ldx, Tp, p.full, p.S,
                                                                         p.slice_tokens, partial, tri);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.r == 0) return e;
-  gram_fixup_kernel<<<dim3((unsigned)(GT * GT / 256), (unsigned)p.r), 256, 0, st>>>(partial, K, p.full, p.S, Gs,
+  gram_fixup_kernel<<<dim3((unsigned)(GT * GT / 256), (unsigned)p.r), 256, 0, st>>>(partial, K, p.full, p.S, Tp,
                                                                                      tri);
   return hipGetLastError();
 }

@@ -61,8 +61,8 @@ def gram_tolerance(X64, W32, s_table, ref_losses):
 
 
 @pytest.mark.parametrize("M,K,N", [
-    (2000, 256, 200),   # M > 2K: the case the Gram form is for; N ragged (two tiles)
-    (700, 384, 130),    # 2K = 768 rows of [G_hi; G_lo]: a 512-row tile holds rows of both
+    (2000, 256, 200),   # M > K + 512: the case the Gram form is for; N ragged (two tiles)
+    (700, 384, 130),    # K = 384, three groups: the one 512-row tile of G ends past K
     (64, 128, 1),       # degenerate: one group, one output
     (4096, 512, 256),
     (2048, 4096, 128),  # 528 G tiles: 512 whole, the other 16 in two token slices each

@@ -226,3 +226,25 @@ def test_decode_mfma_edges(awq, M, K, N):
     art = artefact(N, K, 5)
     X = torch.from_numpy(np.random.default_rng(40 + M).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
     run(awq, art, X, prefill=False)
+
+
+def test_prefill_unaligned_scales_odd_groups(awq):
+    """The prefill reads each row's fp16 scale and zero with 2-byte loads: scales and zeros that
+    are only 2-byte aligned (a view one element into a buffer) with an odd number of groups per
+    row (K = 1152: every other row starts at an odd element) give the same result bound, on a
+    ragged M and N (two token tiles, two output tiles, the K loop's 4-step tail)."""
+    banner("w4a16 prefill, scales and zeros 2-byte aligned, K / 128 odd")
+    N, K, M = 200, 1152, 700
+    art = artefact(N, K, 8)
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    G = K // 128
+    sbuf = torch.empty(N * G + 1, dtype=torch.float16, device=DEV)
+    zbuf = torch.empty(N * G + 1, dtype=torch.float16, device=DEV)
+    sc = sbuf[1:].view(N, G)
+    zz = zbuf[1:].view(N, G)
+    sc.copy_(torch.from_numpy(art["scales"].view(np.float16)))
+    zz.copy_(torch.from_numpy(art["zeros"].view(np.float16)))
+    assert sc.data_ptr() % 4 != 0 and zz.data_ptr() % 4 != 0
+    X = torch.from_numpy(np.random.default_rng(41).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    Y = awq.w4a16(X.to(DEV), q, sc, zz).cpu().numpy().astype(np.float64)
+    check(Y, X.float().numpy().astype(np.float64), art, prefill=True, biased=False)
