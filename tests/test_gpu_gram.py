@@ -90,6 +90,28 @@ def test_gram_search_vs_oracle(awq, M, K, N):
           f"{np.max(tol / ref['losses']):.2e} rel", flush=True)
 
 
+@pytest.mark.parametrize("n_grid", [1, 7, 64])
+def test_gram_grid_sizes(awq, n_grid):
+    """Other candidate counts on a triangular shape (K = 1024: two row tiles; N = 300: three
+    output tiles, so every XCD slot group of eight holds empty slots): every candidate within
+    1e-3 of the oracle's loss, the choice by the single-weight rule."""
+    banner(f"search gram n_grid={n_grid}")
+    M, K, N = 2000, 1024, 300
+    _, X, W = synth.custom_layer(M, K, N, dtype="bf16", seed=24)
+    X64, W32 = synth.to_f64(X), synth.to_f32(W)
+    a32 = o.activation_stat(X64).astype(np.float32)
+    ref = o.search(X64, W32, a32, n_grid=n_grid)
+    res = awq.search(X.to(DEV), W.to(DEV), torch.from_numpy(a32).to(DEV), n_grid=n_grid, return_table=True,
+                     gram=True)
+    assert np.array_equal(res.s_table.cpu().numpy().view(np.int32), ref["s_table"].view(np.int32))
+    L = res.losses.cpu().numpy()
+    tol = 1e-3 * np.asarray(ref["losses"])
+    assert np.all(np.abs(L - ref["losses"]) <= tol), np.abs(L - ref["losses"]) / ref["losses"]
+    check_choice(res.best_index, ref["losses"], ref["best"], tol, n_out=M * N)
+    if n_grid == 1:
+        assert res.best_index == 0
+
+
 def test_gram_and_direct_agree(awq):
     """Both forms on the GPU, a block-shaped layer (M = 4 K): each is within its own tolerance
     of the oracle's exact losses, so they agree to the sum of the two tolerances, and their
