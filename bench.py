@@ -613,7 +613,7 @@ def main():
         "pack_gbs_cache_resident": 2.53125 * K * N / (pk_ms * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "search_pipelined_kernel (fused quantize + bf16 MFMA error product + "
+                     "kernel": "search_persistent_kernel (fused quantize + bf16 MFMA error product + "
                                "squared error, all 20 candidates in one launch)",
                      "work_per_launch": f"20 x 2*M*K*N = {flops:.4g} flop",
                      "ms_per_launch": fu_ms},

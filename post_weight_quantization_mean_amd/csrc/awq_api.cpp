@@ -52,7 +52,7 @@ bool search_layout(int64_t M, int64_t K, int64_t N, int n_grid, SearchLayout* ou
   const awq::SearchPlan plan = awq::search_plan(M, K, N, n_grid);
   const int64_t tab = mul_ok(mul_ok(n_grid, K), 4);
   const int64_t par = mul_ok(mul_ok(mul_ok(n_grid, awq::padded_n(N)), K / kGroup), 8);
-  const int64_t part = mul_ok(mul_ok(n_grid, plan.tiles), 8);
+  const int64_t part = mul_ok(mul_ok(n_grid, plan.tiles), 8 * 4);  // up to four sums per tile
   if (tab < 0 || par < 0 || part < 0) return false;
   SearchLayout L;
   L.s_tab = 0;
@@ -289,7 +289,8 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_end), s);
   if (e == hipSuccess)
     e = awq::launch_select(partial, plan.tiles, n_grid, M, n_total, K, s_tab, losses_out, best_out,
-                           s_best_out, flags, s);
+                           s_best_out, flags, s,
+                           gram ? 1 : awq::search_partials_per_tile(xf32, wf32, K, plan, n_grid));
   return map_hip(e);
 }
 

@@ -126,6 +126,9 @@ hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_ta
 hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
                               const float* s_tab, int n_grid, float2* params, int64_t row_base,
                               int64_t NP, uint32_t* flags, hipStream_t st);
+// fp64 sums per (candidate, tile) that launch_search_fused writes: 4 (one per wave) when it runs
+// the persistent kernel, else 1; the workspace holds 4 for every tile
+int search_partials_per_tile(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid);
 hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
                                bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
                                const float2* sr_tab, const float2* params, int n_grid,
@@ -143,9 +146,10 @@ hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uin
 hipError_t launch_search_gram(const uint16_t* Tp, int64_t K, const WSegs& W, const float2* sr_tab,
                               const float2* params, int n_grid, const SearchPlan& plan, double* partial,
                               hipStream_t st);
+// partial: per_tile fp64 sums per (candidate, tile) (search_partials_per_tile)
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
-                         float* s_best, uint32_t* flags, hipStream_t st);
+                         float* s_best, uint32_t* flags, hipStream_t st, int per_tile = 1);
 
 // ---- pack ------------------------------------------------------------------------------
 // clip: fp32 [N, K/128] thresholds of the clipped pack, or null

@@ -190,16 +190,22 @@ __global__ __launch_bounds__(kRangeThreads) void group_range_kernel(const void* 
 // ---- fixed-order loss reduction, first argmin, copy of the winning scales ---------------
 constexpr int kSelectThreads = 1024;
 
+// per_tile: 1 (one sum per tile) or 4 (one per wave of the tile, added in wave order first: the
+// same value the tile's block forms when it adds its four wave sums itself)
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const double* __restrict__ partial, int64_t tiles, int n_grid, double count, int64_t K,
     const float* __restrict__ s_tab, double* __restrict__ losses, int32_t* __restrict__ best,
-    float* __restrict__ s_best, uint32_t* __restrict__ flags) {
+    float* __restrict__ s_best, uint32_t* __restrict__ flags, int per_tile) {
   __shared__ double sl[64];
   __shared__ int sbest;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int al = wave; al < n_grid; al += kSelectThreads / 64) {
     double s = 0.0;
-    for (int64_t t = lane; t < tiles; t += 64) s += partial[(int64_t)al * tiles + t];
+    for (int64_t t = lane; t < tiles; t += 64) {
+      const int64_t u = (int64_t)al * tiles + t;
+      s += per_tile == 1 ? partial[u]
+                         : ((partial[4 * u] + partial[4 * u + 1]) + partial[4 * u + 2]) + partial[4 * u + 3];
+    }
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) sl[al] = s / count;
   }
@@ -246,10 +252,10 @@ hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, in
 
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
-                         float* s_best, uint32_t* flags, hipStream_t st) {
+                         float* s_best, uint32_t* flags, hipStream_t st, int per_tile) {
   const double count = (double)M * (double)N;
   select_kernel<<<1, kSelectThreads, 0, st>>>(partial, tiles, n_grid, count, K, s_tab, losses,
-                                              best, s_best, flags);
+                                              best, s_best, flags, per_tile);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@
 // Block order is XCD-aware: the hardware places workgroup b on XCD b % 8, so logical index
 // L = (b % 8) * ceil(G/8) + b / 8 gives every XCD a contiguous run of L.  L runs candidate-
 // fastest, so the ~32 blocks resident on one XCD share the same X rows and W rows in its L2.
+#include <atomic>
 #include <type_traits>
 
 #include "awq_internal.h"
@@ -721,7 +722,399 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
   if (tid == 0) partial[(int64_t)al * tiles + tile] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
+// ---- persistent variant of the pipelined kernel -------------------------------------------
+// One block per CU walks its tiles (those of its XCD's run of logical indices, every PX-th, PX
+// = blocks per XCD) and carries the pipeline across tiles: in the last eight steps of a tile the
+// look-ahead loads (W of chunks c+4, c+5, the next group's ranges and scale table, the next X
+// pair) and the quantization of chunks c+2 past the end read the next tile's data, so the next
+// tile starts with its first X pair, W sets and two E chunks already in place and no prologue.
+// At a tile boundary each wave squares its accumulators and reduces them across its lanes; the
+// first step of the next tile starts the products from zero and stores that wave's sum (one per
+// wave: partial[4 (al tiles + tile) + wave]), after its own wait, so nothing waits for the store.
+// Needs K / 32 to be a multiple of 8 (K / 128 even) and at least 16 (the first and the last
+// eight steps of a tile are distinct).
+struct TileRes {
+  __amdgpu_buffer_rsrc_t x, w, sr, p;  // X rows m0.., W rows n0w.., the candidate's (s, 1/s), ranges
+  uint32_t woff0, woff1;               // this lane's W rows r0, r1
+  int poff;                            // this lane's range slots
+  bool live0, live1;                   // rows r0, r1 inside the weight
+  int64_t slot;                        // al * tiles + tile
+};
+
+__global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const WSegs segs, int64_t K,
+    const float2* __restrict__ sr_tab, const float2* __restrict__ params, int n_grid,
+    int64_t nt_count, int64_t tiles, int64_t per_xcd, double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[XPSTAGE / 2];
+  __shared__ __attribute__((aligned(1024))) uint8_t es[NES * ESTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * SRG];
+  __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * SRG];
+
+  // this block's tiles: logical indices L0, L0 + PX, ... below its XCD's end
+  const int64_t PX = gridDim.x >> 3;
+  const int64_t xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int64_t total = tiles * n_grid;
+  const int64_t lend0 = (xcd + 1) * per_xcd, lend = lend0 < total ? lend0 : total;
+  const int64_t L0 = xcd * per_xcd + jx;
+  if (L0 >= lend) return;
+  const int G = (int)(K / kGroup);
+  const int64_t NP = nt_count * BN;
+  const int nchunks = (int)(K / PKC);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane & 3;
+  const int r0 = wave * 32 + (lane >> 2), r1 = r0 + 16;
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+  };
+  // (logical indices fit in 31 bits: host-checked)
+  const uint32_t ng = (uint32_t)n_grid, ntc = (uint32_t)nt_count;
+  auto make_res = [&](int64_t L, TileRes& T) {
+    const uint32_t tile = (uint32_t)L / ng;
+    const int al = (int)((uint32_t)L - tile * ng);
+    const uint32_t mt = tile / ntc, nt = tile - mt * ntc;
+    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+    const WSel sel = select_wseg(segs, nt);
+    const uint16_t* W = static_cast<const uint16_t*>(sel.w);
+    const int64_t N = sel.n, ldw = sel.ldw, n0w = sel.n0;
+    T.x = rsrc(X + m0 * ldx, (M - m0) * ldx * 2);
+    T.w = rsrc(W + n0w * ldw, (N - n0w) * ldw * 2);
+    T.sr = rsrc(sr_tab + (int64_t)al * K, K * 8);
+    T.p = rsrc(params + (int64_t)al * G * NP, (int64_t)G * NP * 8);
+    T.woff0 = (uint32_t)(r0 * ldw * 2 + q4 * 16);
+    T.woff1 = (uint32_t)(r1 * ldw * 2 + q4 * 16);
+    T.poff = (int)((n0 + 32 * wave + 2 * (lane >> 2)) * 8);
+    T.live0 = n0w + r0 < N;
+    T.live1 = n0w + r1 < N;
+    T.slot = (int64_t)al * tiles + tile;
+  };
+
+  uint32_t xoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = wave * WAVE_ROWS + 8 * i + (lane >> 3);
+    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 7) ^ xswz(row)) * 16));
+  }
+  const uint32_t xrow16 = (uint32_t)(16 * ldx * 2);
+  const int eslot0 = r0 * PROW + ((q4 ^ swz(r0)) * 16);
+  const int eslot1 = r1 * PROW + ((q4 ^ swz(r1)) * 16);
+  const int fr = lane & 31, fh = lane >> 5;
+  const int efoff0 = fr * PROW + (((0 + fh) ^ swz(fr)) * 16);
+  const int efoff1 = fr * PROW + (((2 + fh) ^ swz(fr)) * 16);
+  auto xfoff = [&](int half, int h) { return fr * XROW + (((4 * half + 2 * h + fh) ^ xswz(fr)) * 16); };
+  const int xwave = wave * (WAVE_ROWS / 2) * XROW;
+
+  auto dma_x_one = [&](const TileRes& T, uint8_t* xh, int i, int p) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(T.x, (AWQ_LDS void*)(xh + xwave + (i & 7) * 1024), 16,
+                                             (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * XROW),
+                                             0, 0);
+  };
+  auto load_w = [&](const TileRes& T, WSet& S, int i, int cb, int j) {
+    S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           T.w, (int)(i == 0 ? T.woff0 : T.woff1) + j * (PKC * 2), cb, 0));
+  };
+  auto load_p = [&](const TileRes& T, int g) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(T.p, T.poff, (int)(g * NP * 8), 0));
+  };
+  auto dma_sr = [&](const TileRes& T, uint8_t* table, int g) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(T.sr, (AWQ_LDS void*)(table + SRG * wave), 16, 16 * lane, g * SRG, 0, 0);
+  };
+  auto sr_addr = [&](const uint8_t* table, int c) {
+    return table + SRG * wave + (32 * (c & 3) + 8 * q4) * 8;
+  };
+  auto row_setup = [&](const TileRes& T, const float4& P, int i) {
+    const bool live = i == 0 ? T.live0 : T.live1;
+    RowQ q;
+    q.delta = live ? (i == 0 ? P.x : P.z) : 1.0f;  // rows past N: Delta 1, z 0, w 0: e = 0
+    const float z = live ? (i == 0 ? P.y : P.w) : 0.0f;
+    q.inv = __builtin_amdgcn_rcpf(q.delta);  // search only; the pack divides exactly
+    q.lo = -z;
+    q.hi = 15.0f - z;
+    return q;
+  };
+  auto elem = [&](const WSet& S, const float4* sv, const RowQ& q, int i, int j) {
+    const uint4& w4 = S.w[i];
+    const uint32_t u = j < 2 ? w4.x : j < 4 ? w4.y : j < 6 ? w4.z : w4.w;
+    const float w = (j & 1) ? bf16_hi(u) : bf16_lo(u);
+    const float s = (j & 1) ? sv[j >> 1].z : sv[j >> 1].x;
+    const float rs = (j & 1) ? sv[j >> 1].w : sv[j >> 1].y;
+    const float v = w * s;                                    // S W
+    const float r = rintf(v * q.inv);                         // rne(v / Delta)
+    const float qz = __builtin_amdgcn_fmed3f(r, q.lo, q.hi);  // clamp(r + z, 0, 15) - z
+    return fmaf(-(qz * q.delta), rs, w);                      // w - Delta (q - z) / s
+  };
+  auto store_piece = [&](uint8_t* estage, int slot, const float* e8) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pk[h] = pack_bf16x2(e8[2 * h], e8[2 * h + 1]);
+    *reinterpret_cast<uint4*>(estage + slot) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  };
+  auto quantize_all = [&](const TileRes& T, const WSet& S, const float4& P, int c, uint8_t* estage) {  // prologue
+    float4 sv[4];
+    const uint8_t* sa = sr_addr(srs0, c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
+    const RowQ q0 = row_setup(T, P, 0), q1 = row_setup(T, P, 1);
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, sv, q0, 0, j);
+    store_piece(estage, eslot0, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = elem(S, sv, q1, 1, j);
+    store_piece(estage, eslot1, e);
+  };
+  auto frag = [&](const uint8_t* base, int fo) { return *reinterpret_cast<const bf16x8*>(base + fo); };
+  auto vm_wait = [](auto n) {
+    constexpr int v = decltype(n)::value;
+    __builtin_amdgcn_s_waitcnt((v & 0xf) | (0x7 << 4) | (0xf << 8) | ((v >> 4) << 14));
+  };
+  constexpr int kWaitLgkm0 = 0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
+  const f32x16 zero16 = acc[0][0];
+
+  TileRes cur, nxt;
+  make_res(L0, cur);
+  WSet S0, S1, S2, S3;
+  float4 PC, PN;
+  RowQ q0, q1;
+  // prologue of the first tile, as in the pipelined kernel
+  dma_sr(cur, srs0, 0);
+  PC = load_p(cur, 0);
+  load_w(cur, S0, 0, 0, 0);
+  load_w(cur, S1, 0, 0, 1);
+  load_w(cur, S0, 1, 0, 0);
+  load_w(cur, S1, 1, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dma_x_one(cur, i < 8 ? xp0lo : xp0hi, i, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(cur, S2, 0, 0, 2);
+  load_w(cur, S3, 0, 0, 3);
+  load_w(cur, S2, 1, 0, 2);
+  load_w(cur, S3, 1, 0, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  vm_wait(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  quantize_all(cur, S0, PC, 0, es + 0 * ESTAGE);
+  quantize_all(cur, S1, PC, 1, es + 1 * ESTAGE);
+  q0 = row_setup(cur, PC, 0);
+  q1 = row_setup(cur, PC, 1);
+  bf16x8 a0[4], b0[4];
+  {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a0[t] = frag(xp0lo + xwave + t * 32 * XROW, xfoff(0, 0));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * PROW, efoff0);
+    auto consume = [](const WSet& S) {
+      asm volatile("" ::"v"(S.w[0].x), "v"(S.w[0].y), "v"(S.w[0].z), "v"(S.w[0].w), "v"(S.w[1].x),
+                   "v"(S.w[1].y), "v"(S.w[1].z), "v"(S.w[1].w));
+    };
+    consume(S2);
+    consume(S3);
+  }
+  double pend = 0.0;          // the sum of the wave's squares of the previous tile
+  int64_t pend_slot = cur.slot;  // its slot (the first tile's own slot, overwritten by its sum)
+
+  // Step c of the pipelined kernel.  FIRST: the tile's first step (products start from zero;
+  // the previous tile's wave sum is stored in group 1, after the step's own wait).  LAST: the
+  // tile's last eight steps, whose look-ahead past the tile's end uses the next tile (N: its
+  // resources; chunk, pair and group indices relative to its start).
+  auto step = [&](int c8, auto jc, auto firstc, auto lastc, const uint8_t* xclo, const uint8_t* xchi,
+                  const uint8_t* xnlo, uint8_t* xdlo, uint8_t* xdhi, const WSet& Q, WSet& F4, WSet& F5,
+                  const uint8_t* srq, uint8_t* srn, int& eo0, int& eo1, int& eo2) {
+    constexpr int j = decltype(jc)::value;
+    constexpr bool FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value;
+    constexpr int k = j & 3;
+    constexpr bool even = (k & 1) == 0;
+    // which look-ahead of this step falls past the tile's end (last eight steps only)
+    constexpr bool nw = LAST && j >= 4;  // W of chunks c+4, c+5 and the next group's ranges / table
+    constexpr bool nx = LAST && j >= 6;  // the X pair after this one
+    constexpr bool nq = LAST && j == 6;  // the row setup of chunk c+2's group
+    const TileRes& TW = nw ? nxt : cur;
+    const TileRes& TX = nx ? nxt : cur;
+    // the next tile's chunks j + 4 - 8, j + 5 - 8 (offsets stay non-negative), pair 0, group 0
+    constexpr int jw = nw ? j - 8 : j;
+    const int cb = nw ? 0 : c8 * (PKC * 2);
+    const int pd = nx ? 0 : (c8 >> 1) + (j >> 1) + 1;
+    const int gn = nw ? 0 : (c8 >> 2) + (j >> 2) + 1;
+    const uint8_t* ec = es + eo0;
+    const uint8_t* en = es + eo1;
+    uint8_t* eq = es + eo2;
+    const uint8_t* sa = sr_addr(srq, k + 2);
+    const uint8_t* xwlo = xclo + xwave;
+    const uint8_t* xwhi = xchi + xwave;
+    const uint8_t* xnw = xnlo + xwave;
+    auto xa = [&](int t) { return (t < 2 ? xwlo : xwhi) + (t & 1) * 32 * XROW; };
+    const int xo0 = xfoff(k & 1, 0), xo1 = xfoff(k & 1, 1), xn0 = xfoff((k + 1) & 1, 0);
+    if (k == 2) {
+      PC = PN;
+      q0 = row_setup(nq ? nxt : cur, PC, 0);
+      q1 = row_setup(nq ? nxt : cur, PC, 1);
+    }
+    bf16x8 a1[4], b1[4];
+    float4 sv[4];
+    float e[16];
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait(std::integral_constant<int, even ? 0 : 12>{});
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      const int r = (g >> 2) & 3, cc = g & 3;
+      if (g < 16)
+        acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[r], b0[cc], FIRST ? zero16 : acc[r][cc], 0, 0, 0);
+      else
+        acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[r], b1[cc], acc[r][cc], 0, 0, 0);
+      if (FIRST && g == 1) {
+        // the previous tile's wave sum, the same value from every lane
+        double* dst = partial + 4 * pend_slot + wave;
+        *dst = pend;
+      }
+      if (g < 2) a0[2 + g] = frag(xa(2 + g), xo0);
+      if (g == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
+      }
+      if (g < 8) {
+        if (g & 1)
+          b1[g >> 1] = frag(ec + (g >> 1) * 32 * PROW, efoff1);
+        else
+          a1[g >> 1] = frag(xa(g >> 1), xo1);
+      }
+      const int el = g >= 3 && g <= 25 && (g - 3) % 3 != 2 ? 2 * ((g - 3) / 3) + (g - 3) % 3 : -1;
+      if (el >= 0) {
+        e[el] = el < 8 ? elem(Q, sv, q0, 0, el) : elem(Q, sv, q1, 1, el - 8);
+        asm volatile("" : "+v"(e[el]));
+      }
+      if (g == 14) store_piece(eq, eslot0, e);
+      if (g == 26) store_piece(eq, eslot1, e + 8);
+      if (g == 15) __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x1 << 8) | (0x3 << 14));
+      if (g >= 16 && g < 24 && (g & 1)) b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * PROW, efoff0);
+      // as in the pipelined kernel; a first step counts its store as well
+      if (g == 24) vm_wait(std::integral_constant<int, even ? (FIRST ? 11 : 10) : 8>{});
+      if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * XROW, xn0);
+      if (even) {
+        if (g == 0) load_w(TW, F4, 0, cb, jw + 4);
+        if (g == 1) load_w(TW, F5, 0, cb, jw + 5);
+        if (g == 2) load_w(TW, F4, 1, cb, jw + 4);
+        if (g == 3) load_w(TW, F5, 1, cb, jw + 5);
+        if (k == 0 && g == 4) PN = load_p(TW, gn);
+        if (k == 0 && g == 5) dma_sr(TW, srn, gn);
+        if (g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(TX, xdlo, (g - 6) / 3, pd);
+      } else {
+        if (g <= 14 && (g & 1) == 0) dma_x_one(TX, xdhi, 8 + g / 2, pd);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k == 1) vm_wait(std::integral_constant<int, 16>{});
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int et = eo0;
+    eo0 = eo1;
+    eo1 = eo2;
+    eo2 = et;
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto body = [&](int c, auto firstc, auto lastc, int& eo0, int& eo1, int& eo2) {
+    step(c, I0{}, firstc, lastc, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, F_{}, lastc, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, F_{}, lastc, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, F_{}, lastc, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I4{}, F_{}, lastc, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I5{}, F_{}, lastc, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I6{}, F_{}, lastc, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I7{}, F_{}, lastc, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
+  };
+  int eo0 = 0, eo1 = ESTAGE, eo2 = 2 * ESTAGE;
+  for (int64_t L = L0;; L += PX) {
+    const bool more = L + PX < lend;
+    if (more)
+      make_res(L + PX, nxt);
+    else
+      nxt = cur;  // nothing follows: the look-ahead re-reads this tile's first chunks, unused
+    body(0, T_{}, F_{}, eo0, eo1, eo2);
+    for (int c = 8; c + 8 < nchunks; c += 8) body(c, F_{}, F_{}, eo0, eo1, eo2);
+    body(nchunks - 8, F_{}, T_{}, eo0, eo1, eo2);
+    // this tile's squares: fp32 per 32x32 tile, fp64 across tiles and lanes
+    double ss = 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t = fmaf(acc[r][c][i], acc[r][c][i], t);
+        ss += (double)t;
+      }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    pend = ss;
+    pend_slot = cur.slot;
+    if (!more) break;
+    cur = nxt;
+  }
+  partial[4 * pend_slot + wave] = pend;
+  __builtin_amdgcn_s_waitcnt(0);  // every copy (the last ones read ahead past the end) has landed
+}
+
 }  // namespace
+
+namespace {
+// compute units of the current device, queried once per device (the persistent grid's size)
+int64_t device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int v = dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (v <= 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+    v = cus;
+    if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+// blocks of the persistent kernel (one per CU, a multiple of 8), or 0 when the pipelined kernel
+// runs instead: bf16 operands, K / 32 a multiple of 8 and at least 16, and at least two tiles
+// per block
+int64_t persistent_blocks(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid) {
+  const int64_t nchunks = K / PKC, total = plan.tiles * n_grid;
+  if (xf32 || wf32 || nchunks % 8 != 0 || nchunks < 16 || total >= (int64_t)INT32_MAX) return 0;
+  const int64_t P = device_cus() / 8 * 8;
+  return P >= 8 && total >= 2 * P ? P : 0;
+}
+}  // namespace
+
+int search_partials_per_tile(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid) {
+  return persistent_blocks(xf32, wf32, K, plan, n_grid) > 0 ? 4 : 1;
+}
 
 SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
   SearchPlan p;
@@ -744,6 +1137,13 @@ hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx,
   search_fused_kernel<XF, WF><<<grid, THREADS, 0, st>>>(X, M, ldx, W, K, s_tab, rs_tab, params, \
                                                         n_grid, plan.nt, plan.tiles, per_xcd,   \
                                                         partial)
+  const int64_t pb = persistent_blocks(xf32, wf32, K, plan, n_grid);
+  if (pb > 0) {
+    search_persistent_kernel<<<(unsigned)pb, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K,
+                                                               sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd,
+                                                               partial);
+    return hipGetLastError();
+  }
   if (!xf32 && !wf32) {
     search_pipelined_kernel<<<grid, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K, sr_tab,
                                                       params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
