@@ -120,7 +120,12 @@ AWQ_API int awq_stats(const void* X, int x_dtype, int64_t M, int64_t K, int64_t 
  *   group, n_grid  128 and 1..64 (20 in the method)
  *   losses_out     fp64 [n_grid];  best_out int32 [1];  s_best_out fp32 [K] = s of the winner
  *   s_table_out    fp32 [n_grid, K] or NULL: the whole scale table
- *   ws             workspace of at least awq_search_workspace_bytes(...) bytes (device)
+ *   ws             workspace of at least awq_search_workspace_bytes(...) bytes (device).
+ *                  When K is a multiple of 256 and at least 512, that size ends with room for
+ *                  a copy of X in matrix-core operand order, xcopy = round_up(2 * round_up(M, 32)
+ *                  * K, 256) bytes, which the fastest kernel (bf16 X and W) reads X from.  A
+ *                  workspace at least xcopy bytes short of the full size still works: it runs
+ *                  a kernel that stages X itself, with bit-identical results.
  *   flags          AWQ_FLAG_SCALE_RANGE, AWQ_FLAG_NONFINITE_LOSS
  * ------------------------------------------------------------------------------------- */
 AWQ_API size_t awq_search_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
@@ -149,10 +154,12 @@ AWQ_API int awq_search_timed(const void* X, int x_dtype, int64_t M, int64_t K, i
  * is a static device array of AWQ_STATIC_SCRATCH_BYTES (128 MiB) inside the library, one
  * copy on each GPU the library runs on, held until the process ends.  The current device
  * must be the device of `stream`.
- *   Limit: a call whose workspace (awq_search_workspace_bytes) exceeds
- *          AWQ_STATIC_SCRATCH_BYTES returns AWQ_ERR_SCRATCH before any HIP call (for n_grid =
- *          20 the workspace is about 1.25 N K bytes: K = N = 4096 needs 21 MB, K = 14336 with
- *          N = 4096 needs 74 MB; N = 28672 with K = 4096 does not fit).
+ *   Limit: a call whose workspace less the copy of X (awq_search_workspace_bytes minus
+ *          xcopy, see awq_search) exceeds AWQ_STATIC_SCRATCH_BYTES returns AWQ_ERR_SCRATCH
+ *          before any HIP call (for n_grid = 20 that part is about 1.25 N K bytes: K = N =
+ *          4096 needs 21 MB, K = 14336 with N = 4096 needs 74 MB; N = 28672 with K = 4096
+ *          does not fit).  The copy of X is used when the whole workspace fits (K = N = M =
+ *          4096: 55 MB), else the kernel that stages X itself runs.
  *   Sharing: every call on one GPU uses that GPU's single copy and leaves its contents
  *          behind; nothing in it has to start at zero.  Calls that overlap on one GPU (two
  *          streams, or two host threads) race on it and must be serialised by the caller.

@@ -65,6 +65,22 @@ bool search_layout(int64_t M, int64_t K, int64_t N, int n_grid, SearchLayout* ou
   return true;
 }
 
+// Bytes of the fragment-ordered copy of X that the persistent search kernel reads (bf16
+// [round_up(M, 32), K]), or 0 when K does not take that kernel, -1 on overflow.
+int64_t xfrag_bytes(int64_t M, int64_t K) {
+  if (!awq::persistent_k(K)) return 0;
+  if (M > INT64_MAX - 31) return -1;
+  return mul_ok(mul_ok((M + 31) / 32 * 32, K), 2);
+}
+
+// A search workspace of `total` bytes plus room for the copy of X where K takes it (0 on
+// overflow).
+size_t with_xfrag(size_t total, int64_t M, int64_t K) {
+  const int64_t xb = xfrag_bytes(M, K);
+  if (xb < 0) return 0;
+  return total + align_up((size_t)xb);
+}
+
 // Checks of an elementwise operand [rows, cols] with row stride ld (no group constraint).
 int check_elems(const void* p, int dtype, int64_t rows, int64_t cols, int64_t ld) {
   if (p == nullptr) return AWQ_ERR_INVALID_ARG;
@@ -188,7 +204,7 @@ AWQ_API size_t awq_search_workspace_bytes(int64_t M, int64_t K, int64_t N, int32
     return 0;
   SearchLayout L;
   if (!search_layout(M, K, N, n_grid, &L)) return 0;
-  return L.total;
+  return with_xfrag(L.total, M, K);
 }
 
 }  // extern "C"
@@ -260,6 +276,13 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   if (ws == nullptr || ws_bytes < total) return AWQ_ERR_WORKSPACE;
   if (!aligned16(ws) || !aligned16(a)) return AWQ_ERR_INVALID_ARG;
   if (s_table_out != nullptr && !aligned16(s_table_out)) return AWQ_ERR_INVALID_ARG;
+  const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
+  const awq::SearchPlan plan = awq::search_plan(rows, K, NP, n_grid);
+  // The persistent kernel reads X from a fragment-ordered copy placed after the rest of the
+  // workspace; without room for it the pipelined kernel runs (the same losses bit for bit).
+  const int64_t xfb = gram ? 0 : xfrag_bytes(M, K);
+  const bool persistent = xfb > 0 && ws_bytes >= total + (size_t)xfb &&
+                          awq::search_persistent(xf32, wf32, K, plan, n_grid);
 
   char* base = static_cast<char*>(ws);
   float* s_tab = s_table_out != nullptr ? s_table_out : reinterpret_cast<float*>(base + L.s_tab);
@@ -267,9 +290,8 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   float2* sr_tab = reinterpret_cast<float2*>(base + L.sr_tab);
   float2* params = reinterpret_cast<float2*>(base + L.params);
   double* partial = reinterpret_cast<double*>(base + L.partial);
-  const bool xf32 = x_dtype == AWQ_DTYPE_F32, wf32 = w_dtype == AWQ_DTYPE_F32;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const awq::SearchPlan plan = awq::search_plan(rows, K, NP, n_grid);
+  uint16_t* Xf = persistent ? reinterpret_cast<uint16_t*>(base + total) : nullptr;  // total: 256-aligned
   uint16_t* Tp = gram ? reinterpret_cast<uint16_t*>(base + gs_off) : nullptr;  // [K, 2K] bf16
   float* gpart = gram ? reinterpret_cast<float*>(base + gp_off) : nullptr;
 
@@ -278,19 +300,21 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   for (int i = 0; i < n_weights && e == hipSuccess; ++i)
     e = awq::launch_group_range(Ws[i], wf32, Ns[i], K, ldws[i], s_tab, n_grid, params, segs.tile0[i] * 128,
                                 NP, flags, s);
+  if (e == hipSuccess && persistent)
+    e = awq::launch_xfrag(static_cast<const uint16_t*>(X), M, K, ldx, Xf, s);
   if (e == hipSuccess && fused_begin != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
   if (e == hipSuccess && gram)
     e = awq::launch_search_gram(Tp, K, segs, sr_tab, params, n_grid, plan, partial, s);
   else if (e == hipSuccess)
-    e = awq::launch_search_fused(X, xf32, M, ldx, segs, wf32, K, s_tab, rs_tab, sr_tab, params, n_grid, plan,
-                                 partial, s);
+    e = awq::launch_search_fused(X, Xf, xf32, M, ldx, segs, wf32, K, s_tab, rs_tab, sr_tab, params, n_grid,
+                                 plan, partial, s);
   if (e == hipSuccess && fused_end != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_end), s);
   if (e == hipSuccess)
     e = awq::launch_select(partial, plan.tiles, n_grid, M, n_total, K, s_tab, losses_out, best_out,
                            s_best_out, flags, s,
-                           gram ? 1 : awq::search_partials_per_tile(xf32, wf32, K, plan, n_grid));
+                           persistent ? 4 : 1);
   return map_hip(e);
 }
 
@@ -361,7 +385,7 @@ AWQ_API size_t awq_search_multi_workspace_bytes(int64_t M, int64_t K, const int6
   }
   SearchLayout L;
   if (!search_layout(M, K, NP, n_grid, &L)) return 0;
-  return L.total;
+  return with_xfrag(L.total, M, K);
 }
 
 AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx,

@@ -126,13 +126,21 @@ hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_ta
 hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, int64_t ldw,
                               const float* s_tab, int n_grid, float2* params, int64_t row_base,
                               int64_t NP, uint32_t* flags, hipStream_t st);
-// fp64 sums per (candidate, tile) that launch_search_fused writes: 4 (one per wave) when it runs
-// the persistent kernel, else 1; the workspace holds 4 for every tile
-int search_partials_per_tile(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid);
-hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
-                               bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
-                               const float2* sr_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st);
+// The persistent search kernel (one block per CU carrying its pipeline across tiles) takes bf16
+// X and W, K a multiple of 256 and at least 512 (persistent_k), and at least two tiles per CU.
+// It reads X from a copy in fragment order (launch_xfrag): bf16 [round_up(M, 32), K], the
+// 16 bytes of lane l of the MFMA operand for rows 32 rb.. and channels 16 kb.. at
+// ((rb K/16 + kb) 64 + l) 16 bytes, rows past M zero.  It writes 4 fp64 sums per (candidate,
+// tile), one per wave; the other kernels write 1 (the workspace holds 4 for every tile).
+inline bool persistent_k(int64_t K) { return K % 256 == 0 && K >= 512; }
+bool search_persistent(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid);
+hipError_t launch_xfrag(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Xf, hipStream_t st);
+// Xf: the fragment-ordered copy of X when search_persistent(...) holds (the persistent kernel
+// runs), else null (the pipelined kernel for bf16 operands, the plain fused kernel otherwise)
+hipError_t launch_search_fused(const void* X, const uint16_t* Xf, bool xf32, int64_t M, int64_t ldx,
+                               const WSegs& W, bool wf32, int64_t K, const float* s_tab,
+                               const float* rs_tab, const float2* sr_tab, const float2* params,
+                               int n_grid, const SearchPlan& plan, double* partial, hipStream_t st);
 // Gram form: Tp bf16 [K, 2K], row k' = chunks of 32 columns of G_hi and G_lo interleaved
 // (bf16(G) and bf16(G - bf16(G)), G = X^T X for bf16 X [M, K]); when gram_triangular(K), G there
 // stands for T = diag(X^T X) + 2 triu(X^T X, 1) (zero below the diagonal), and each candidate
@@ -146,7 +154,7 @@ hipError_t launch_gram(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uin
 hipError_t launch_search_gram(const uint16_t* Tp, int64_t K, const WSegs& W, const float2* sr_tab,
                               const float2* params, int n_grid, const SearchPlan& plan, double* partial,
                               hipStream_t st);
-// partial: per_tile fp64 sums per (candidate, tile) (search_partials_per_tile)
+// partial: per_tile fp64 sums per (candidate, tile): 4 after the persistent kernel, else 1
 hipError_t launch_select(const double* partial, int64_t tiles, int n_grid, int64_t M, int64_t N,
                          int64_t K, const float* s_tab, double* losses, int32_t* best,
                          float* s_best, uint32_t* flags, hipStream_t st, int per_tile = 1);

@@ -23,6 +23,12 @@
 // Block order is XCD-aware: the hardware places workgroup b on XCD b % 8, so logical index
 // L = (b % 8) * ceil(G/8) + b / 8 gives every XCD a contiguous run of L.  L runs candidate-
 // fastest, so the ~32 blocks resident on one XCD share the same X rows and W rows in its L2.
+//
+// Three kernels share this tile and arithmetic: search_fused_kernel (above description; any
+// dtype), search_pipelined_kernel (bf16: a software pipeline with X staged through LDS by the
+// buffer-to-LDS DMA) and search_persistent_kernel (bf16, the production path: one block per CU
+// carrying that pipeline across tiles, with X read straight into registers from a copy of X in
+// matrix-core operand order that xfrag_kernel writes first).
 #include <atomic>
 #include <type_traits>
 
@@ -724,17 +730,26 @@ __global__ __launch_bounds__(THREADS, 1) void search_pipelined_kernel(
 
 // ---- persistent variant of the pipelined kernel -------------------------------------------
 // One block per CU walks its tiles (those of its XCD's run of logical indices, every PX-th, PX
-// = blocks per XCD) and carries the pipeline across tiles: in the last eight steps of a tile the
-// look-ahead loads (W of chunks c+4, c+5, the next group's ranges and scale table, the next X
-// pair) and the quantization of chunks c+2 past the end read the next tile's data, so the next
-// tile starts with its first X pair, W sets and two E chunks already in place and no prologue.
+// = blocks per XCD) and carries the pipeline across tiles.
+// X never passes through LDS here.  The kernel reads it from a copy in fragment order
+// (xfrag_kernel), where the 16 bytes that lane l holds of the MFMA A operand for rows
+// 32 rb .. 32 rb + 31 and channels 16 kb .. 16 kb + 15 sit together, so each A fragment is one
+// coalesced 1 KiB load straight into registers.  Per step and CU, LDS then carries the 8 KiB of
+// E written and 32 KiB of B fragments read, against 104 KiB when X is staged there (the X
+// copies into LDS were the largest cost of a step).
+// Step c loads the A fragments of chunk c+1, each right after the last product of chunk c that
+// reads the same registers, about one step before its first use; the compiler's counters wait
+// for them.  The rest of the look-ahead is the pipelined kernel's: W of chunks c+4, c+5 on even
+// steps, the next group's ranges and (s, 1/s) table when c % 4 = 0.  In the last steps of a
+// tile these read the next tile's data, so the next tile starts with its first A fragments,
+// W sets and two E chunks in place and no prologue.
 // At a tile boundary each wave squares its accumulators and reduces them across its lanes; the
 // first step of the next tile starts the products from zero and stores that wave's sum (one per
-// wave: partial[4 (al tiles + tile) + wave]), after its own wait, so nothing waits for the store.
+// wave: partial[4 (al tiles + tile) + wave]), so nothing waits for the store.
 // Needs K / 32 to be a multiple of 8 (K / 128 even) and at least 16 (the first and the last
 // eight steps of a tile are distinct).
 struct TileRes {
-  __amdgpu_buffer_rsrc_t x, w, sr, p;  // X rows m0.., W rows n0w.., the candidate's (s, 1/s), ranges
+  __amdgpu_buffer_rsrc_t x, w, sr, p;  // Xf from row m0, W rows n0w.., the candidate's (s, 1/s), ranges
   uint32_t woff0, woff1;               // this lane's W rows r0, r1
   int poff;                            // this lane's range slots
   bool live0, live1;                   // rows r0, r1 inside the weight
@@ -742,13 +757,9 @@ struct TileRes {
 };
 
 __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
-    const uint16_t* __restrict__ X, int64_t M, int64_t ldx, const WSegs segs, int64_t K,
+    const uint16_t* __restrict__ Xf, int64_t Mp, const WSegs segs, int64_t K,
     const float2* __restrict__ sr_tab, const float2* __restrict__ params, int n_grid,
     int64_t nt_count, int64_t tiles, int64_t per_xcd, double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[XPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[XPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[XPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[XPSTAGE / 2];
   __shared__ __attribute__((aligned(1024))) uint8_t es[NES * ESTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * SRG];
   __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * SRG];
@@ -762,7 +773,6 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
   if (L0 >= lend) return;
   const int G = (int)(K / kGroup);
   const int64_t NP = nt_count * BN;
-  const int nchunks = (int)(K / PKC);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -783,7 +793,9 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
     const WSel sel = select_wseg(segs, nt);
     const uint16_t* W = static_cast<const uint16_t*>(sel.w);
     const int64_t N = sel.n, ldw = sel.ldw, n0w = sel.n0;
-    T.x = rsrc(X + m0 * ldx, (M - m0) * ldx * 2);
+    // row blocks past Mp (a tile's rows past M) read as zero; 512 rows of Xf span less than
+    // 2^31 bytes (host-checked)
+    T.x = rsrc(Xf + m0 * K, (Mp - m0) * K * 2);
     T.w = rsrc(W + n0w * ldw, (N - n0w) * ldw * 2);
     T.sr = rsrc(sr_tab + (int64_t)al * K, K * 8);
     T.p = rsrc(params + (int64_t)al * G * NP, (int64_t)G * NP * 8);
@@ -795,25 +807,18 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
     T.slot = (int64_t)al * tiles + tile;
   };
 
-  uint32_t xoff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = wave * WAVE_ROWS + 8 * i + (lane >> 3);
-    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 7) ^ xswz(row)) * 16));
-  }
-  const uint32_t xrow16 = (uint32_t)(16 * ldx * 2);
   const int eslot0 = r0 * PROW + ((q4 ^ swz(r0)) * 16);
   const int eslot1 = r1 * PROW + ((q4 ^ swz(r1)) * 16);
   const int fr = lane & 31, fh = lane >> 5;
   const int efoff0 = fr * PROW + (((0 + fh) ^ swz(fr)) * 16);
   const int efoff1 = fr * PROW + (((2 + fh) ^ swz(fr)) * 16);
-  auto xfoff = [&](int half, int h) { return fr * XROW + (((4 * half + 2 * h + fh) ^ xswz(fr)) * 16); };
-  const int xwave = wave * (WAVE_ROWS / 2) * XROW;
 
-  auto dma_x_one = [&](const TileRes& T, uint8_t* xh, int i, int p) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(T.x, (AWQ_LDS void*)(xh + xwave + (i & 7) * 1024), 16,
-                                             (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * XROW),
-                                             0, 0);
+  // A fragment (row block r of this wave's 128 rows, chunk ch, K-half h): 1 KiB of Xf, this
+  // lane's 16 bytes at 16 lane; a row block is 64 K bytes
+  const uint32_t avoff = (uint32_t)(lane * 16) + (uint32_t)(wave * 4) * (uint32_t)(K * 64);
+  auto load_a = [&](const TileRes& T, int ch, int h, int r) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                          T.x, (int)avoff, (int)(r * K * 64 + (2 * ch + h) * 1024), 0));
   };
   auto load_w = [&](const TileRes& T, WSet& S, int i, int cb, int j) {
     S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -890,21 +895,22 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
   WSet S0, S1, S2, S3;
   float4 PC, PN;
   RowQ q0, q1;
-  // prologue of the first tile, as in the pipelined kernel
+  bf16x8 a0[4], a1[4], b0[4];
+  // prologue of the first tile: its table, ranges, W of chunks 0-3 and A fragments of chunk 0
   dma_sr(cur, srs0, 0);
   PC = load_p(cur, 0);
   load_w(cur, S0, 0, 0, 0);
   load_w(cur, S1, 0, 0, 1);
   load_w(cur, S0, 1, 0, 0);
   load_w(cur, S1, 1, 0, 1);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dma_x_one(cur, i < 8 ? xp0lo : xp0hi, i, 0);
-  __builtin_amdgcn_sched_barrier(0);
   load_w(cur, S2, 0, 0, 2);
   load_w(cur, S3, 0, 0, 3);
   load_w(cur, S2, 1, 0, 2);
   load_w(cur, S3, 1, 0, 3);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) a0[r] = load_a(cur, 0, 0, r);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) a1[r] = load_a(cur, 0, 1, r);
   __builtin_amdgcn_sched_barrier(0);
   vm_wait(std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
@@ -912,32 +918,22 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
   quantize_all(cur, S1, PC, 1, es + 1 * ESTAGE);
   q0 = row_setup(cur, PC, 0);
   q1 = row_setup(cur, PC, 1);
-  bf16x8 a0[4], b0[4];
   {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) a0[t] = frag(xp0lo + xwave + t * 32 * XROW, xfoff(0, 0));
-#pragma unroll
     for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * PROW, efoff0);
-    auto consume = [](const WSet& S) {
-      asm volatile("" ::"v"(S.w[0].x), "v"(S.w[0].y), "v"(S.w[0].z), "v"(S.w[0].w), "v"(S.w[1].x),
-                   "v"(S.w[1].y), "v"(S.w[1].z), "v"(S.w[1].w));
-    };
-    consume(S2);
-    consume(S3);
   }
-  double pend = 0.0;          // the sum of the wave's squares of the previous tile
+  double pend = 0.0;             // the sum of the wave's squares of the previous tile
   int64_t pend_slot = cur.slot;  // its slot (the first tile's own slot, overwritten by its sum)
 
-  // Step c of the pipelined kernel.  FIRST: the tile's first step (products start from zero;
-  // the previous tile's wave sum is stored in group 1, after the step's own wait).  LAST: the
-  // tile's last eight steps, whose look-ahead past the tile's end uses the next tile (N: its
-  // resources; chunk, pair and group indices relative to its start).
-  auto step = [&](int c8, auto jc, auto firstc, auto lastc, const uint8_t* xclo, const uint8_t* xchi,
-                  const uint8_t* xnlo, uint8_t* xdlo, uint8_t* xdhi, const WSet& Q, WSet& F4, WSet& F5,
+  // Step c.  FIRST: the tile's first step (products start from zero; the previous tile's wave
+  // sum is stored in group 1).  LAST: the tile's last eight steps, whose look-ahead past the
+  // tile's end uses the next tile (nxt: its resources; chunk and group indices relative to its
+  // start).
+  auto step = [&](int c8, auto jc, auto firstc, auto lastc, const WSet& Q, WSet& F4, WSet& F5,
                   const uint8_t* srq, uint8_t* srn, int& eo0, int& eo1, int& eo2) {
     constexpr int j = decltype(jc)::value;
     constexpr bool FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value;
@@ -945,34 +941,31 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
     constexpr bool even = (k & 1) == 0;
     // which look-ahead of this step falls past the tile's end (last eight steps only)
     constexpr bool nw = LAST && j >= 4;  // W of chunks c+4, c+5 and the next group's ranges / table
-    constexpr bool nx = LAST && j >= 6;  // the X pair after this one
+    constexpr bool na = LAST && j == 7;  // the A fragments of chunk c+1
     constexpr bool nq = LAST && j == 6;  // the row setup of chunk c+2's group
     const TileRes& TW = nw ? nxt : cur;
-    const TileRes& TX = nx ? nxt : cur;
-    // the next tile's chunks j + 4 - 8, j + 5 - 8 (offsets stay non-negative), pair 0, group 0
+    const TileRes& TA = na ? nxt : cur;
+    // the next tile's chunks j + 4 - 8, j + 5 - 8 (offsets stay non-negative) and 0, group 0
     constexpr int jw = nw ? j - 8 : j;
     const int cb = nw ? 0 : c8 * (PKC * 2);
-    const int pd = nx ? 0 : (c8 >> 1) + (j >> 1) + 1;
+    const int ca = na ? 0 : c8 + j + 1;
     const int gn = nw ? 0 : (c8 >> 2) + (j >> 2) + 1;
     const uint8_t* ec = es + eo0;
     const uint8_t* en = es + eo1;
     uint8_t* eq = es + eo2;
     const uint8_t* sa = sr_addr(srq, k + 2);
-    const uint8_t* xwlo = xclo + xwave;
-    const uint8_t* xwhi = xchi + xwave;
-    const uint8_t* xnw = xnlo + xwave;
-    auto xa = [&](int t) { return (t < 2 ? xwlo : xwhi) + (t & 1) * 32 * XROW; };
-    const int xo0 = xfoff(k & 1, 0), xo1 = xfoff(k & 1, 1), xn0 = xfoff((k + 1) & 1, 0);
     if (k == 2) {
       PC = PN;
       q0 = row_setup(nq ? nxt : cur, PC, 0);
       q1 = row_setup(nq ? nxt : cur, PC, 1);
     }
-    bf16x8 a1[4], b1[4];
+    bf16x8 b1[4];
     float4 sv[4];
     float e[16];
     __builtin_amdgcn_sched_barrier(0);
-    vm_wait(std::integral_constant<int, even ? 0 : 12>{});
+    // k == 2 reads the (s, 1/s) table copied into LDS two steps earlier (group 5 of step k = 0):
+    // 7 A loads of that step and 8 of the next were issued after it
+    if (k == 2) vm_wait(std::integral_constant<int, 15>{});
 #pragma unroll
     for (int g = 0; g < 32; ++g) {
       const int r = (g >> 2) & 3, cc = g & 3;
@@ -985,17 +978,15 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
         double* dst = partial + 4 * pend_slot + wave;
         *dst = pend;
       }
-      if (g < 2) a0[2 + g] = frag(xa(2 + g), xo0);
+      // chunk c+1's A fragments, each after the last product that reads chunk c's in its place
+      if (g >= 4 && g <= 16 && (g & 3) == 0) a0[(g >> 2) - 1] = load_a(TA, ca, 0, (g >> 2) - 1);
+      if (g >= 20 && g <= 28 && (g & 3) == 0) a1[(g >> 2) - 5] = load_a(TA, ca, 1, (g >> 2) - 5);
+      if (g == 31) a1[3] = load_a(TA, ca, 1, 3);
       if (g == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) sv[t] = *reinterpret_cast<const float4*>(sa + 16 * t);
       }
-      if (g < 8) {
-        if (g & 1)
-          b1[g >> 1] = frag(ec + (g >> 1) * 32 * PROW, efoff1);
-        else
-          a1[g >> 1] = frag(xa(g >> 1), xo1);
-      }
+      if (g < 8 && (g & 1)) b1[g >> 1] = frag(ec + (g >> 1) * 32 * PROW, efoff1);
       const int el = g >= 3 && g <= 25 && (g - 3) % 3 != 2 ? 2 * ((g - 3) / 3) + (g - 3) % 3 : -1;
       if (el >= 0) {
         e[el] = el < 8 ? elem(Q, sv, q0, 0, el) : elem(Q, sv, q1, 1, el - 8);
@@ -1005,9 +996,6 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
       if (g == 26) store_piece(eq, eslot1, e + 8);
       if (g == 15) __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x1 << 8) | (0x3 << 14));
       if (g >= 16 && g < 24 && (g & 1)) b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * PROW, efoff0);
-      // as in the pipelined kernel; a first step counts its store as well
-      if (g == 24) vm_wait(std::integral_constant<int, even ? (FIRST ? 11 : 10) : 8>{});
-      if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * XROW, xn0);
       if (even) {
         if (g == 0) load_w(TW, F4, 0, cb, jw + 4);
         if (g == 1) load_w(TW, F5, 0, cb, jw + 5);
@@ -1015,13 +1003,9 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
         if (g == 3) load_w(TW, F5, 1, cb, jw + 5);
         if (k == 0 && g == 4) PN = load_p(TW, gn);
         if (k == 0 && g == 5) dma_sr(TW, srn, gn);
-        if (g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(TX, xdlo, (g - 6) / 3, pd);
-      } else {
-        if (g <= 14 && (g & 1) == 0) dma_x_one(TX, xdhi, 8 + g / 2, pd);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (k == 1) vm_wait(std::integral_constant<int, 16>{});
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -1041,16 +1025,19 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
   using I7 = std::integral_constant<int, 7>;
   using T_ = std::true_type;
   using F_ = std::false_type;
+  // eight steps: step j quantizes chunk c+j+2 from the W set loaded four steps before (Q) and,
+  // when even, loads chunks c+j+4, c+j+5 into F4, F5; the (s, 1/s) tables alternate by group
   auto body = [&](int c, auto firstc, auto lastc, int& eo0, int& eo1, int& eo2) {
-    step(c, I0{}, firstc, lastc, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I1{}, F_{}, lastc, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I2{}, F_{}, lastc, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I3{}, F_{}, lastc, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I4{}, F_{}, lastc, xp0lo, xp0hi, xp0lo, xp1lo, xp1hi, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
-    step(c, I5{}, F_{}, lastc, xp0lo, xp0hi, xp1lo, xp1lo, xp1hi, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
-    step(c, I6{}, F_{}, lastc, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
-    step(c, I7{}, F_{}, lastc, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I0{}, firstc, lastc, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, F_{}, lastc, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, F_{}, lastc, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, F_{}, lastc, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I4{}, F_{}, lastc, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I5{}, F_{}, lastc, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I6{}, F_{}, lastc, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I7{}, F_{}, lastc, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
   };
+  const int nchunks = (int)(K / PKC);
   int eo0 = 0, eo1 = ESTAGE, eo2 = 2 * ESTAGE;
   for (int64_t L = L0;; L += PX) {
     const bool more = L + PX < lend;
@@ -1080,7 +1067,27 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
     cur = nxt;
   }
   partial[4 * pend_slot + wave] = pend;
-  __builtin_amdgcn_s_waitcnt(0);  // every copy (the last ones read ahead past the end) has landed
+  __builtin_amdgcn_s_waitcnt(0);  // every load (the last ones read ahead past the end) has landed
+}
+
+// X bf16 [M, K] (row stride ldx) into the fragment order of the persistent kernel: the 16-byte
+// piece of row 32 rb + l % 32, channels 16 kb + 8 (l / 32) .. + 7 goes to byte
+// ((rb K/16 + kb) 64 + l) 16 of Xf; rows M .. Mp - 1 are zero.  Block b covers rows
+// 32 rb .. + 31 and channels 64 cb .. + 63 (four fragments, 4 KiB); thread t reads 16 bytes
+// (t % 8) of row 32 rb + t / 8, so eight lanes read one 128-byte run of a row.
+__global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                   int64_t ldx, uint16_t* __restrict__ Xf) {
+  const int64_t kc = K / 64;
+  const int64_t b = blockIdx.x;
+  const int64_t rb = b / kc, cb = b - rb * kc;
+  const int t = threadIdx.x;
+  const int rl = t >> 3, piece = t & 7;
+  const int64_t row = rb * 32 + rl;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < M) v = *reinterpret_cast<const uint4*>(X + row * ldx + cb * 64 + piece * 8);
+  const int64_t frag_index = rb * (K / 16) + cb * 4 + (piece >> 1);
+  const int l = rl + 32 * (piece & 1);
+  *reinterpret_cast<uint4*>(Xf + (frag_index * 64 + l) * 8) = v;
 }
 
 }  // namespace
@@ -1105,15 +1112,24 @@ int64_t device_cus() {
 // runs instead: bf16 operands, K / 32 a multiple of 8 and at least 16, and at least two tiles
 // per block
 int64_t persistent_blocks(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid) {
-  const int64_t nchunks = K / PKC, total = plan.tiles * n_grid;
-  if (xf32 || wf32 || nchunks % 8 != 0 || nchunks < 16 || total >= (int64_t)INT32_MAX) return 0;
+  const int64_t total = plan.tiles * n_grid;
+  static_assert(PKC * 8 == 256, "persistent_k: K / 32 a multiple of 8 and at least 16");
+  if (xf32 || wf32 || !persistent_k(K) || total >= (int64_t)INT32_MAX) return 0;
   const int64_t P = device_cus() / 8 * 8;
   return P >= 8 && total >= 2 * P ? P : 0;
 }
 }  // namespace
 
-int search_partials_per_tile(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid) {
-  return persistent_blocks(xf32, wf32, K, plan, n_grid) > 0 ? 4 : 1;
+bool search_persistent(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid) {
+  return persistent_blocks(xf32, wf32, K, plan, n_grid) > 0;
+}
+
+hipError_t launch_xfrag(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Xf, hipStream_t st) {
+  if (K % 64 != 0) return hipErrorInvalidValue;
+  const int64_t blocks = (M + 31) / 32 * (K / 64);
+  if (blocks <= 0 || blocks >= (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  xfrag_kernel<<<(unsigned)blocks, 256, 0, st>>>(X, M, K, ldx, Xf);
+  return hipGetLastError();
 }
 
 SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
@@ -1127,21 +1143,21 @@ SearchPlan search_plan(int64_t M, int64_t K, int64_t N, int n_grid) {
   return p;
 }
 
-hipError_t launch_search_fused(const void* X, bool xf32, int64_t M, int64_t ldx, const WSegs& W,
-                               bool wf32, int64_t K, const float* s_tab, const float* rs_tab,
-                               const float2* sr_tab, const float2* params, int n_grid,
-                               const SearchPlan& plan, double* partial, hipStream_t st) {
+hipError_t launch_search_fused(const void* X, const uint16_t* Xf, bool xf32, int64_t M, int64_t ldx,
+                               const WSegs& W, bool wf32, int64_t K, const float* s_tab,
+                               const float* rs_tab, const float2* sr_tab, const float2* params,
+                               int n_grid, const SearchPlan& plan, double* partial, hipStream_t st) {
   const int64_t per_xcd = plan.blocks / 8;
   const dim3 grid((unsigned)plan.blocks);
 #define AWQ_LAUNCH(XF, WF)                                                                  \
   search_fused_kernel<XF, WF><<<grid, THREADS, 0, st>>>(X, M, ldx, W, K, s_tab, rs_tab, params, \
                                                         n_grid, plan.nt, plan.tiles, per_xcd,   \
                                                         partial)
-  const int64_t pb = persistent_blocks(xf32, wf32, K, plan, n_grid);
-  if (pb > 0) {
-    search_persistent_kernel<<<(unsigned)pb, THREADS, 0, st>>>(static_cast<const uint16_t*>(X), M, ldx, W, K,
-                                                               sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd,
-                                                               partial);
+  if (Xf != nullptr) {
+    const int64_t pb = persistent_blocks(xf32, wf32, K, plan, n_grid);
+    if (pb <= 0) return hipErrorInvalidValue;  // the caller checks search_persistent first
+    search_persistent_kernel<<<(unsigned)pb, THREADS, 0, st>>>(Xf, (M + 31) / 32 * 32, W, K, sr_tab, params,
+                                                               n_grid, plan.nt, plan.tiles, per_xcd, partial);
     return hipGetLastError();
   }
   if (!xf32 && !wf32) {

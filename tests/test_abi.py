@@ -135,12 +135,37 @@ def test_search_static_argument_errors(L, kw, status):
     assert search_static(L, **kw) == status
 
 
+def xcopy_bytes(M, K):
+    """The fragment-ordered copy of X at the end of a search workspace (header formula)."""
+    if K % 256 or K < 512:
+        return 0
+    return -(-2 * (-(-M // 32) * 32) * K // 256) * 256
+
+
 def test_search_static_limit_matches_the_workspace_size(L):
     from post_weight_quantization_mean_amd import awq
     assert awq.STATIC_SCRATCH_BYTES == 128 * 1024 * 1024
+    ws = lambda M, K, N: L.awq_search_workspace_bytes(M, K, N, 128, 20) - xcopy_bytes(M, K)
     # the decoder block's down projection (K = 14336, N = 4096) fits, its fused gate+up does not
-    assert L.awq_search_workspace_bytes(16384, 14336, 4096, 128, 20) <= awq.STATIC_SCRATCH_BYTES
-    assert L.awq_search_workspace_bytes(16384, 4096, 28672, 128, 20) > awq.STATIC_SCRATCH_BYTES
+    assert ws(16384, 14336, 4096) <= awq.STATIC_SCRATCH_BYTES
+    assert ws(16384, 4096, 28672) > awq.STATIC_SCRATCH_BYTES
+    assert search_static(L, M=16384, K=4096, ldx=4096, ldw=4096, N=28672) == SCRATCH
+
+
+@pytest.mark.parametrize("M,M2,K", [(4096, 3585, 4096), (1000, 513, 512), (16384, 15873, 14336), (64, 1, 256),
+                                     (4096, 3585, 384), (33, 1, 1024)])
+def test_search_workspace_ends_with_the_copy_of_x(L, M, M2, K):
+    """Between two token counts with the same number of 512-row tiles (the same partial sums),
+    the workspace differs by the copy of X exactly where K takes the persistent kernel (a
+    multiple of 256, at least 512), for one weight and for several."""
+    assert -(-M // 512) == -(-M2 // 512)
+    one = lambda m: L.awq_search_workspace_bytes(m, K, 4096, 128, 20)
+    assert one(M) - one(M2) == xcopy_bytes(M, K) - xcopy_bytes(M2, K)
+    ns = (ctypes.c_int64 * 2)(2048, 2048)
+    multi = lambda m: L.awq_search_multi_workspace_bytes(m, K, ns, 2, 128, 20)
+    assert multi(M) - multi(M2) == xcopy_bytes(M, K) - xcopy_bytes(M2, K)
+    if xcopy_bytes(M, K):
+        assert xcopy_bytes(M, K) > xcopy_bytes(M2, K)
 
 
 def search_multi(L, X=P, xt=BF16, M=64, K=256, ldx=256, Ws=(P, P + 4096), wt=BF16, Ns=(128, 64), ldws=(256, 256),
@@ -195,19 +220,19 @@ def test_search_gram_argument_errors(L, kw, status):
 
 
 def test_search_gram_workspace(L):
-    # the search workspace for K rows of the left operand (T as K x 2K: hi and lo interleaved)
-    # plus that K x 2K bf16 matrix
+    # the search workspace for K rows of the left operand (T as K x 2K: hi and lo interleaved;
+    # no copy of X) plus that K x 2K bf16 matrix
     K, N = 4096, 4096
-    assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= \
-        L.awq_search_workspace_bytes(K, K, N, 128, 20) + 2 * K * K * 2
+    direct = lambda k: L.awq_search_workspace_bytes(k, k, N, 128, 20) - xcopy_bytes(k, k)
+    assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= direct(K) + 2 * K * K * 2
     assert L.awq_search_gram_workspace_bytes(16384, 4000, N, 128, 20) == 0
     assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 65) == 0
     # plus the fp32 sums of the G tiles split along the tokens: at K = 4096, 528 upper-triangle
     # tiles of 128 x 128, the 16 past the first 512 split into 16 slices of 1024 tokens
-    base = L.awq_search_workspace_bytes(K, K, N, 128, 20) + 2 * K * K * 2
+    base = direct(K) + 2 * K * K * 2
     assert L.awq_search_gram_workspace_bytes(16384, K, N, 128, 20) >= base + 16 * 16 * 128 * 128 * 4
     # K = 5120: 820 tiles; the 308 past the first 512 would get one slice each, so none is split
-    base = L.awq_search_workspace_bytes(5120, 5120, N, 128, 20) + 2 * 5120 * 5120 * 2
+    base = direct(5120) + 2 * 5120 * 5120 * 2
     assert base <= L.awq_search_gram_workspace_bytes(16384, 5120, N, 128, 20) < base + 4096
 
 
