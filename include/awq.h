@@ -209,8 +209,9 @@ AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, i
  *   X, W   AWQ_DTYPE_BF16 only (AWQ_ERR_UNSUPPORTED otherwise); 512 x 2K bf16 must span less
  *          than 2^31 bytes (K < 2^20)
  *   ws     workspace of at least awq_search_gram_workspace_bytes(...) bytes: the search
- *          workspace for K rows, the K x 2K bf16 matrix, and fp32 sums of the G tiles that are
- *          split along the tokens to fill the last round of blocks (at most 64 MiB)
+ *          workspace for K rows (without a copy of X), the K x 2K bf16 matrix (stored in
+ *          matrix-core operand order), and fp32 sums of the G tiles that are split along the
+ *          tokens to fill the last round of blocks (at most 64 MiB)
  * Other arguments, results and errors as awq_search. */
 AWQ_API size_t awq_search_gram_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group,
                                                int32_t n_grid);

@@ -7,9 +7,10 @@
 // gram_dma_kernel forms G on the bf16 matrix cores and stores it as two bf16 matrices,
 // G_hi = bf16(G) and G_lo = bf16(G - G_hi), so G_hi + G_lo keeps 16 significand bits of G (a
 // single bf16 G would lose the cancellation that the quadratic form depends on).  They are
-// interleaved in one [K x 2K] matrix Tp: row k' holds, for every 32-column chunk c, chunk c of
-// row k' of G_hi and then of G_lo.  gram_search_kernel multiplies both with E^T into the same
-// accumulators and dots each output (k', n) with E[n, k'].
+// interleaved in one [K x 2K] matrix: row k' holds, for every 32-column chunk c, chunk c of row
+// k' of G_hi and then of G_lo; Tp stores that matrix in matrix-core operand order (tp_at).
+// gram_search_kernel multiplies both with E^T into the same accumulators and dots each output
+// (k', n) with E[n, k'].
 //
 // Triangular form (K > 512).  G is symmetric, so e G e^T = sum_k G[k,k] e_k^2 +
 // 2 sum_{k < k'} G[k,k'] e_k e_k': the same quadratic form with T = diag(G) + 2 triu(G, 1) in
@@ -58,24 +59,33 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int gd_swz(int row) { return 2 * (row & 3); }
 
-// Element (k1, k2) of G, g, from a tile with k1b <= k2b: its hi and lo parts go to row k1 of Tp
-// [K x 2K], columns 64 (k2 / 32) + k2 % 32 and 32 more.  Off the tile diagonal (off_diag:
+// Element (row, col) of part `part` (0: hi, 1: lo) in Tp.  The parts are interleaved by
+// 32-column chunks into a [K x 2K] matrix (column pc = 64 (col / 32) + 32 part + col % 32), and
+// that matrix is stored in matrix-core operand order: fragments of 32 rows x 16 columns, 1 KiB
+// each, row block after row block (K / 8 fragments per block of 32 rows); lane l of a fragment
+// holds row l % 32, columns 8 (l / 32) .. + 7 as 16 contiguous bytes, the 16 bytes that lane l
+// of a v_mfma_f32_32x32x16_bf16 A operand takes.  The candidate kernel thus loads each of its A
+// fragments with one coalesced 1 KiB load straight into registers.
+__device__ __forceinline__ int64_t tp_at(int64_t K, int64_t row, int64_t col, int part) {
+  const int64_t pc = 64 * (col >> 5) + 32 * part + (col & 31);
+  const int64_t frag = (row >> 5) * (K >> 3) + (pc >> 4);
+  const int64_t l = (row & 31) + 32 * ((pc >> 3) & 1);
+  return (frag * 64 + l) * 8 + (pc & 7);
+}
+// Element (k1, k2) of G, g, from a tile with k1b <= k2b.  Off the tile diagonal (off_diag:
 // k1b < k2b) the transposed element (k2, k1) is written too.  Triangular form: T[k1, k2] = 2 g
 // above the diagonal, g on it, and 0 below it (so the transposed element of an off-diagonal
 // tile is 0).
-__device__ __forceinline__ int64_t tp_at(int64_t K, int64_t row, int64_t col) {
-  return row * 2 * K + 64 * (col >> 5) + (col & 31);
-}
 __device__ __forceinline__ void store_g(uint16_t* __restrict__ Tp, int64_t K, int64_t k1, int64_t k2, bool off_diag,
                                         bool tri, float g) {
   const float t = !tri || k1 == k2 ? g : (k1 < k2 ? 2.0f * g : 0.0f);
   const uint16_t hi = bf16_bits(t);
   const uint16_t lo = bf16_bits(t - __uint_as_float((uint32_t)hi << 16));
-  Tp[tp_at(K, k1, k2)] = hi;
-  Tp[tp_at(K, k1, k2) + 32] = lo;
+  Tp[tp_at(K, k1, k2, 0)] = hi;
+  Tp[tp_at(K, k1, k2, 1)] = lo;
   if (off_diag) {
-    Tp[tp_at(K, k2, k1)] = tri ? (uint16_t)0 : hi;
-    Tp[tp_at(K, k2, k1) + 32] = tri ? (uint16_t)0 : lo;
+    Tp[tp_at(K, k2, k1, 0)] = tri ? (uint16_t)0 : hi;
+    Tp[tp_at(K, k2, k1, 1)] = tri ? (uint16_t)0 : lo;
   }
 }
 
@@ -318,20 +328,19 @@ GramPlan gram_plan(int64_t M, int64_t K) {
 }
 
 // ---- the candidate kernel of the Gram form ------------------------------------------------
-// The stack is stored as Tp [K, 2K] (see store_g): row k' of T_hi and row k' of T_lo
-// interleaved by 32-column chunks, so that one 128-byte line of a row holds chunk c of both.
-// Since (T_hi + T_lo) e^T = T_hi e^T + T_lo e^T, both parts accumulate into the same outputs:
+// The stack is stored as Tp (see tp_at): row k' of T_hi and row k' of T_lo interleaved by
+// 32-column chunks, in matrix-core operand order.  Since (T_hi + T_lo) e^T = T_hi e^T + T_lo e^T, both parts accumulate into the same outputs:
 // a block is a tile of 512 rows k' x 128 outputs n for one candidate, and its step c multiplies
 // the hi and the lo part of chunk c with the same E chunk, 64 v_mfma_f32_32x32x16_bf16 per wave.
 // Per matrix instruction that halves, against a [2K x K] stack of separate hi and lo rows, the
 // quantization, the E stores and reads and the barriers, and the blocks' fixed prologue and
 // epilogue; the bytes of T per instruction stay the same.
 // The pipeline is the direct search kernel's (search.hip), with these differences:
-//   * X (here T) comes as one pair per step, DMA'd one step ahead into the other pair stage:
-//     instruction i (rows 8 i .. 8 i + 7 of the wave's 128) in group 1 + 3 i;
-//   * the 64 matrix instructions of a step run K-half by K-half; within one, row block r of
-//     the wave, hi then lo: group g = 32 h + 8 r + 4 part + cc.  Each A fragment is read two
-//     blocks of four before its first use (the first two of a step in the previous step);
+//   * T never passes through LDS: the 64 matrix instructions of a step run K-half by K-half;
+//     within one, row block r of the wave, hi then lo: group g = 32 h + 8 r + 4 part + cc, and
+//     block blk = g / 4 of chunk c+1's A fragments (1 KiB of Tp each) is loaded straight into
+//     registers right after the last product of chunk c that reads block blk, one step before
+//     its use (the compiler's counters wait for it);
 //   * the B fragments of the second K-half are read in groups 1-7 and the next chunk's first
 //     K-half in groups 33-39, after the last use of the current ones;
 //   * the quantization of chunk c+2 places element el in group 3 + 3 el, its two stores after
@@ -339,15 +348,12 @@ GramPlan gram_plan(int64_t M, int64_t K) {
 // Triangular form: the block's K loop starts at its first row, chunk m0 / 32 (a multiple of 16).
 constexpr int GS_BM = 512, GS_BN = 128, GS_KC = 32;
 constexpr int GS_PROW = GS_KC * 2;            // bytes of an E row (one chunk)
-constexpr int GS_XROW = 2 * GS_PROW;          // bytes of a T pair row (hi and lo chunk)
-constexpr int GS_XPSTAGE = GS_BM * GS_XROW;   // 64 KiB
 constexpr int GS_ESTAGE = GS_BN * GS_PROW;    // 8 KiB
 constexpr int GS_NES = 3;
 constexpr int GS_SRG = kGroup * 8;            // one group's (s, 1/s) pairs: 1 KiB
 #define AWQ_LDS_G __attribute__((address_space(3)))
 
 __device__ __forceinline__ int gs_swz(int row) { return (row >> 2) & 3; }   // E rows
-__device__ __forceinline__ int gs_xswz(int row) { return (row >> 1) & 7; }  // T pair rows
 __device__ __forceinline__ float gs_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float gs_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ uint32_t gs_pack(float a, float b) {
@@ -371,10 +377,6 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
     const uint16_t* __restrict__ Tp, int64_t K, const WSegs segs, const float2* __restrict__ sr_tab,
     const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles, bool tri,
     double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[GS_XPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[GS_XPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[GS_XPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[GS_XPSTAGE / 2];
   __shared__ __attribute__((aligned(1024))) uint8_t es[GS_NES * GS_ESTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * GS_SRG];
   __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * GS_SRG];
@@ -415,16 +417,14 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   const __amdgpu_buffer_rsrc_t wrsrc = rsrc(W + n0w * ldw, (N - n0w) * ldw * 2);
   const __amdgpu_buffer_rsrc_t srsrc = rsrc(sr_tab + (int64_t)al * K, K * 8);
   const __amdgpu_buffer_rsrc_t prsrc = rsrc(params + (int64_t)al * G * NP, (int64_t)G * NP * 8);
-  // T copy instruction i (0..15) of wave w fills pair rows 128 w + 8 i + lane / 8, slot lane % 8,
-  // with the global 16-byte piece slot ^ gs_xswz(row)
-  uint32_t xoff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = wave * 128 + 8 * i + (lane >> 3);
-    xoff[i] = (uint32_t)(row * ldx * 2 + (((lane & 7) ^ gs_xswz(row)) * 16));
-  }
-  const uint32_t xrow16 = (uint32_t)(16 * ldx * 2);
-  const int xwave = wave * 64 * GS_XROW;  // this wave's 64 rows in a half stage
+  // A fragment blk = 8 h + 2 r + part of chunk ch: row block 4 wave + r of the tile (K / 8
+  // fragments of 1 KiB each), column block 4 ch + 2 part + h; this lane's 16 bytes at 16 lane
+  const uint32_t avoff = (uint32_t)(lane * 16) + (uint32_t)(wave * 4) * (uint32_t)(K * 128);
+  auto load_a = [&](int ch, int blk) {
+    const int h = blk >> 3, r = (blk >> 1) & 3, part = blk & 1;
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                          xrsrc, (int)avoff, (int)(r * K * 128 + (4 * ch + 2 * part + h) * 1024), 0));
+  };
   // quantization: rows r0, r1 of the E tile, channel piece q4 of each chunk
   const int q4 = lane & 3;
   const int r0 = wave * 32 + (lane >> 2), r1 = r0 + 16;
@@ -434,18 +434,10 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   const int eslot1 = r1 * GS_PROW + ((q4 ^ gs_swz(r1)) * 16);
   const bool live0 = n0w + r0 < N, live1 = n0w + r1 < N;
   const int poff = (int)((n0 + 32 * wave + 2 * (lane >> 2)) * 8);
-  // fragment reads: lane reads row (32 t + fr), 16-byte piece 2 h + fh of K-half h; in a pair
-  // row the hi chunk is pieces 0-3, the lo chunk pieces 4-7
+  // E fragment reads: lane reads row (32 t + fr), 16-byte piece 2 h + fh of K-half h
   const int fr = lane & 31, fh = lane >> 5;
   const int efoff0 = fr * GS_PROW + (((0 + fh) ^ gs_swz(fr)) * 16);
   const int efoff1 = fr * GS_PROW + (((2 + fh) ^ gs_swz(fr)) * 16);
-  auto xfoff = [&](int part, int h) { return fr * GS_XROW + (((4 * part + 2 * h + fh) ^ gs_xswz(fr)) * 16); };
-
-  auto dma_x_one = [&](uint8_t* xh, int i, int p) {  // instruction i of pair p into half stage xh
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS_G void*)(xh + xwave + (i & 7) * 1024), 16,
-                                             (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * GS_XROW),
-                                             0, 0);
-  };
   auto load_w = [&](GsWSet& S, int i, int cb, int j) {
     S.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            wrsrc, (int)(i == 0 ? woff0 : woff1) + j * (GS_KC * 2), cb, 0));
@@ -519,8 +511,8 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   GsWSet S0, S1, S2, S3;  // W words of chunk c live in set c % 4
   float4 PC, PN;          // ranges of the group being quantized, of the next group
   GsRowQ q0, q1;
-  // Prologue: group c0 / 4's scale table and ranges, W of chunks c0 .. c0 + 3, pair c0 of T;
-  // chunks c0 and c0 + 1 are quantized.
+  // Prologue: group c0 / 4's scale table and ranges, W of chunks c0 .. c0 + 3, the A fragments
+  // of chunk c0; chunks c0 and c0 + 1 are quantized.
   dma_sr(srs0, c0 >> 2);
   PC = load_p(c0 >> 2);
   load_w(S0, 0, c0 * (GS_KC * 2), 0);
@@ -528,8 +520,9 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   load_w(S0, 1, c0 * (GS_KC * 2), 0);
   load_w(S1, 1, c0 * (GS_KC * 2), 1);
   __builtin_amdgcn_sched_barrier(0);
+  bf16x8 a[16];  // A fragments of the step's chunk, block by block replaced by the next chunk's
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, c0);
+  for (int i = 0; i < 16; ++i) a[i] = load_a(c0, i);
   __builtin_amdgcn_sched_barrier(0);
   load_w(S2, 0, c0 * (GS_KC * 2), 2);
   load_w(S3, 0, c0 * (GS_KC * 2), 3);
@@ -542,7 +535,7 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   quantize_all(S1, PC, 1, es + 1 * GS_ESTAGE);
   q0 = row_setup(PC, 0);
   q1 = row_setup(PC, 1);
-  bf16x8 b0[4], an0, an1;  // B fragments of K-half 0 of chunk c; A fragments of blocks 0, 1 of step c
+  bf16x8 b0[4];  // B fragments of K-half 0 of chunk c
   {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -550,26 +543,18 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * GS_PROW, efoff0);
-    an0 = frag(xp0lo + xwave, xfoff(0, 0));
-    an1 = frag(xp0lo + xwave, xfoff(1, 0));
     asm volatile("" ::"v"(S2.w[0].x), "v"(S2.w[0].y), "v"(S2.w[0].z), "v"(S2.w[0].w), "v"(S2.w[1].x),
                  "v"(S2.w[1].y), "v"(S2.w[1].z), "v"(S2.w[1].w));
     asm volatile("" ::"v"(S3.w[0].x), "v"(S3.w[0].y), "v"(S3.w[0].z), "v"(S3.w[0].w), "v"(S3.w[1].x),
                  "v"(S3.w[1].y), "v"(S3.w[1].z), "v"(S3.w[1].w));
   }
 
-  // Step c (k = c % 4 known at compile time): xc is pair c's stage, xd pair c+1's.
-  // vmcnt accounting (even steps: 4 W loads in groups 0-3, 2 more in groups 4, 5 when k = 0, and
-  // 16 T copies in groups 1, 4, ..., 46; odd steps: the 16 copies):
-  //   * group 8: pair c's rows 64-127 (copied in the previous step) landed before their first read;
-  //     what may be outstanding is this step's loads before group 8 (even: 4 W, 2 when k = 0,
-  //     3 copies; odd: 3 copies);
-  //   * group 56: pair c+1's rows 0-63 (this step's copies 0-7) landed before the next step's
-  //     first fragments are read: only copies 8-15 may be outstanding.  Every earlier load,
-  //     including the scale table DMA of a k = 0 step, has landed then.
-  auto step = [&](int c8, auto jc, const uint8_t* xclo, const uint8_t* xchi, uint8_t* xdlo, uint8_t* xdhi,
-                  const GsWSet& Q, GsWSet& F4, GsWSet& F5, const uint8_t* srq, uint8_t* srn, int& eo0, int& eo1,
-                  int& eo2) {
+  // Step c (k = c % 4 known at compile time).  Loads: even steps 4 W in groups 0-3, when k = 0
+  // the next group's ranges (group 4) and scale table DMA (group 5); every step 16 A fragments
+  // in groups 4, 8, ..., 60 and 63.  The scale table DMA'd in a k = 0 step is read from the
+  // k = 2 step on: 15 A loads of its own step and 16 of the next were issued after it.
+  auto step = [&](int c8, auto jc, const GsWSet& Q, GsWSet& F4, GsWSet& F5, const uint8_t* srq, uint8_t* srn,
+                  int& eo0, int& eo1, int& eo2) {
     constexpr int j = decltype(jc)::value;
     constexpr int k = j & 3;
     constexpr bool even = (k & 1) == 0;
@@ -580,33 +565,19 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
     const uint8_t* en = es + eo1;
     uint8_t* eq = es + eo2;
     const uint8_t* sa = sr_addr(srq, k + 2);
-    // A fragment of row block r of pair stage (lo, hi), part p, K-half h
-    auto xa = [&](const uint8_t* lo, const uint8_t* hi, int r, int p, int h) {
-      return frag((r < 2 ? lo : hi) + xwave + (r & 1) * 32 * GS_XROW, xfoff(p, h));
-    };
     if (k == 2) {  // chunks c+2 .. c+5 of this quad after the first two: next group
       PC = PN;
       q0 = row_setup(PC, 0);
       q1 = row_setup(PC, 1);
     }
-    bf16x8 a[16], b1[4];
-    a[0] = an0;
-    a[1] = an1;
+    bf16x8 b1[4];
     float4 sv[4];
     float e[16];
     __builtin_amdgcn_sched_barrier(0);
+    if (k == 2) vm_wait(std::integral_constant<int, 31>{});
     gs_each([&](auto gc) {
       constexpr int g = decltype(gc)::value;
       constexpr int blk = g >> 2, h = blk >> 3, r = (blk >> 1) & 3, cc = g & 3;
-      if (g == 8) vm_wait(std::integral_constant<int, even ? (k == 0 ? 9 : 7) : 3>{});
-      // the A fragment of block blk + 2, two blocks ahead (blocks 0, 1 of the next step: groups 56, 60)
-      if ((g & 3) == 0 && blk + 2 < 16) {
-        constexpr int nb = blk + 2 < 16 ? blk + 2 : 15;
-        a[nb] = xa(xclo, xchi, (nb >> 1) & 3, nb & 1, nb >> 3);
-      }
-      if (g == 56) vm_wait(std::integral_constant<int, 8>{});
-      if (g == 56) an0 = xa(xdlo, xdhi, 0, 0, 0);
-      if (g == 60) an1 = xa(xdlo, xdhi, 0, 1, 0);
       acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[blk], h == 0 ? b0[cc] : b1[cc], acc[r][cc], 0, 0, 0);
       if (g == 0) {
 #pragma unroll
@@ -630,7 +601,10 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
         if (k == 0 && g == 4) PN = load_p(gn);
         if (k == 0 && g == 5) dma_sr(srn, gn);
       }
-      if (g <= 46 && (g - 1) % 3 == 0) dma_x_one((g - 1) / 3 < 8 ? xdlo : xdhi, (g - 1) / 3, c + 1);
+      // chunk c+1's A fragment of block blk - 1 (block 15: after the last product, group 63);
+      // past the last chunk these read other rows of the tile or, past its end, zeros (unused)
+      if (g >= 4 && (g & 3) == 0) a[(g >> 2) - 1] = load_a(c + 1, (g >> 2) - 1);
+      if (g == 63) a[15] = load_a(c + 1, 15);
       __builtin_amdgcn_sched_barrier(0);
     }, std::make_integer_sequence<int, 64>{});
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // E stores of chunk c+2, fragment reads
@@ -642,8 +616,8 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
     eo2 = et;
   };
 
-  // The body covers two groups (8 steps) so that each scale table has a static role; the pair
-  // stages alternate every step.  nchunks - c0 is a multiple of 4 (c0 a multiple of 16).
+  // The body covers two groups (8 steps) so that each scale table has a static role.  nchunks -
+  // c0 is a multiple of 4 (c0 a multiple of 16).
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -655,22 +629,22 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   int eo0 = 0, eo1 = GS_ESTAGE, eo2 = 2 * GS_ESTAGE;
   int c = c0;
   for (; c + 8 <= nchunks; c += 8) {
-    step(c, I0{}, xp0lo, xp0hi, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I1{}, xp1lo, xp1hi, xp0lo, xp0hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I2{}, xp0lo, xp0hi, xp1lo, xp1hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I4{}, xp0lo, xp0hi, xp1lo, xp1hi, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
-    step(c, I5{}, xp1lo, xp1hi, xp0lo, xp0hi, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
-    step(c, I6{}, xp0lo, xp0hi, xp1lo, xp1hi, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
-    step(c, I7{}, xp1lo, xp1hi, xp0lo, xp0hi, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I0{}, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I4{}, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I5{}, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
+    step(c, I6{}, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I7{}, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
   }
   if (c < nchunks) {  // K / 128 odd: one more group
-    step(c, I0{}, xp0lo, xp0hi, xp1lo, xp1hi, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I1{}, xp1lo, xp1hi, xp0lo, xp0hi, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I2{}, xp0lo, xp0hi, xp1lo, xp1hi, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0hi, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I0{}, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I1{}, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
+    step(c, I2{}, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I3{}, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no copy (the last ones read past the end) outlives the block
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no load (the last ones read past the end) outlives the block
 
   // This wave's 128 rows are rows kb .. kb + 127 of T: one whole group gq of K (rows past K hold
   // zeros and are skipped).  Lane l's outputs sit at k' = kb + 32 r + 8 (i / 4) + 4 (l / 32) + i % 4
