@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define AWQ_ABI_VERSION 7
+#define AWQ_ABI_VERSION 8
 
 #if defined(__GNUC__)
 #define AWQ_API __attribute__((visibility("default")))
@@ -321,6 +321,20 @@ AWQ_API int awq_scaled_act(const void* X, void* Y, int dtype, int64_t M, int64_t
 AWQ_API int awq_w4a16(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
                       const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
                       int64_t ldy, awq_stream_t stream);
+
+/* The same product with a workspace.  The prefill (bf16 X, more than 8 tokens) then first
+ * copies X into matrix-core operand order in the workspace (the layout of awq_search's copy of
+ * X) and reads its matrix operand from there straight into registers, instead of staging X
+ * through on-chip memory: the same products in the same order, so Y is identical bit for bit.
+ *   awq_w4a16_workspace_bytes: the bytes that copy needs, 2 * round_up(M, 32) * K for bf16 X
+ *              with more than 8 tokens, else 0 (no workspace used; 0 also for invalid sizes)
+ *   ws         device memory of at least that size, 16-byte aligned, or NULL; a smaller
+ *              workspace (or NULL) runs the product as awq_w4a16 does
+ * Other arguments, results and errors as awq_w4a16. */
+AWQ_API size_t awq_w4a16_workspace_bytes(int64_t M, int64_t K, int x_dtype);
+AWQ_API int awq_w4a16_ws(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                         const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
+                         int64_t ldy, void* ws, size_t ws_bytes, awq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -100,7 +100,11 @@ def lib() -> ctypes.CDLL:
         L.awq_scaled_act.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, vp, vp, vp]
         L.awq_w4a16.restype = ctypes.c_int
         L.awq_w4a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i32, vp, i64, vp]
-        if L.awq_abi_version() != 7:
+        L.awq_w4a16_workspace_bytes.restype = sz
+        L.awq_w4a16_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+        L.awq_w4a16_ws.restype = ctypes.c_int
+        L.awq_w4a16_ws.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i32, vp, i64, vp, sz, vp]
+        if L.awq_abi_version() != 8:
             raise ImportError("libawq ABI version mismatch")
         _lib = L
     return _lib
@@ -475,10 +479,19 @@ def scaled_act(X: torch.Tensor, s: torch.Tensor, act: str = "gelu", *, out: Opti
     return Y
 
 
+def w4a16_workspace_bytes(M: int, K: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    """Bytes of the prefill's copy of X in matrix-core operand order (0 when none is used)."""
+    return int(lib().awq_w4a16_workspace_bytes(M, K, 0 if dtype == torch.float32 else 1))
+
+
 def w4a16(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-          group_size: int = GROUP, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+          group_size: int = GROUP, *, out: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None, staged: bool = False) -> torch.Tensor:
     """Y = X' W_hat^T (fp32 [M, N]) for activations X' [M, K] that already carry S^-1 and the
-    artefact (qweight int32 [N, K/8], scales and zeros fp16 [N, K/128]) of ``pack``."""
+    artefact (qweight int32 [N, K/8], scales and zeros fp16 [N, K/128]) of ``pack``.
+    The prefill (bf16 X, more than 8 tokens) reads X from a copy in matrix-core operand order
+    in ``workspace`` (allocated here when not given; ``w4a16_workspace_bytes``); ``staged``
+    runs it without the copy (X staged on chip), with the same result bit for bit."""
     M, K, ldx = _matrix(X, "X")
     N = qweight.shape[0]
     if qweight.shape != (N, K // 8) or qweight.dtype != torch.int32 or not qweight.is_contiguous():
@@ -492,7 +505,14 @@ def w4a16(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: t
     if Y.shape != (M, N) or Y.dtype != torch.float32 or Y.stride(1) != 1:
         raise ValueError("out must be fp32 [M, N] with unit stride along N")
     _same_device(Y, X.device, "out")
-    _check(lib().awq_w4a16(X.data_ptr(), _dtype_code(X), M, K, ldx, qweight.data_ptr(), scales.data_ptr(),
-                           zeros.data_ptr(), N, group_size, Y.data_ptr(), Y.stride(0), _stream(X.device)),
-           "awq_w4a16")
+    need = 0 if staged else w4a16_workspace_bytes(M, K, X.dtype)
+    if need > 0:
+        ws, ws_bytes = _workspace(workspace, need, X.device)
+        ws_ptr = ws.data_ptr()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    _check(lib().awq_w4a16_ws(X.data_ptr(), _dtype_code(X), M, K, ldx, qweight.data_ptr(), scales.data_ptr(),
+                              zeros.data_ptr(), N, group_size, Y.data_ptr(), Y.stride(0), ws_ptr, ws_bytes,
+                              _stream(X.device)),
+           "awq_w4a16_ws")
     return Y

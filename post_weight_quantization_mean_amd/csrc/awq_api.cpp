@@ -474,9 +474,14 @@ AWQ_API int awq_scaled_act(const void* X, void* Y, int dtype, int64_t M, int64_t
   return scale_op(2, X, Y, dtype, M, K, ld, s, act, flags, stream);
 }
 
-AWQ_API int awq_w4a16(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
-                      const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
-                      int64_t ldy, awq_stream_t stream) {
+AWQ_API size_t awq_w4a16_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
+  if (M <= 0 || K <= 0 || K % kGroup != 0 || !valid_dtype(x_dtype) || M > INT64_MAX / 2 / K) return 0;
+  return awq::w4a16_xcopy_bytes(x_dtype == AWQ_DTYPE_F32, M, K);
+}
+
+AWQ_API int awq_w4a16_ws(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                         const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
+                         int64_t ldy, void* ws, size_t ws_bytes, awq_stream_t stream) {
   int st = check_matrix(X, x_dtype, M, K, ldx);
   if (st != AWQ_OK) return st;
   if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
@@ -486,10 +491,20 @@ AWQ_API int awq_w4a16(const void* X, int x_dtype, int64_t M, int64_t K, int64_t 
       (reinterpret_cast<uintptr_t>(zeros) & 1u) != 0 || (reinterpret_cast<uintptr_t>(Y) & 3u) != 0)
     return AWQ_ERR_INVALID_ARG;
   if (mul_ok(mul_ok(M, ldy), 4) < 0 || mul_ok(N, K) < 0) return AWQ_ERR_SHAPE;
-  // prefill tiles use 32-bit offsets within 512 rows of X
+  // prefill tiles use 32-bit offsets within 512 rows of X (and of its copy, K <= ldx)
   if (mul_ok(mul_ok(awq::kW4a16BM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  if (ws != nullptr && !aligned16(ws)) return AWQ_ERR_INVALID_ARG;
+  // the copy of X when the workspace holds it; otherwise the prefill stages X itself
+  const size_t xb = awq::w4a16_xcopy_bytes(x_dtype == AWQ_DTYPE_F32, M, K);
+  uint16_t* xcopy = xb > 0 && ws != nullptr && ws_bytes >= xb ? static_cast<uint16_t*>(ws) : nullptr;
   return map_hip(awq::launch_w4a16(X, x_dtype == AWQ_DTYPE_F32, M, K, ldx, qweight, scales, zeros, N, Y, ldy,
-                                   reinterpret_cast<hipStream_t>(stream)));
+                                   xcopy, reinterpret_cast<hipStream_t>(stream)));
+}
+
+AWQ_API int awq_w4a16(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
+                      const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group, float* Y,
+                      int64_t ldy, awq_stream_t stream) {
+  return awq_w4a16_ws(X, x_dtype, M, K, ldx, qweight, scales, zeros, N, group, Y, ldy, nullptr, 0, stream);
 }
 
 }  // extern "C"

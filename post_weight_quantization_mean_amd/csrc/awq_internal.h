@@ -176,9 +176,13 @@ hipError_t launch_scale_op(int op, const void* X, void* Y, bool bf16, int64_t ro
 // ---- W4A16 products over the artefact -----------------------------------------------------
 constexpr int64_t kW4a16GemvMax = 8;  // tokens per decode launch; bf16 X above this runs on MFMA
 constexpr int kW4a16BM = 512;         // tokens per prefill tile
+// bytes of the operand-order copy of X that the prefill reads X from (bf16 X, more than
+// kW4a16GemvMax tokens; the xfrag layout of the search), else 0
+size_t w4a16_xcopy_bytes(bool xf32, int64_t M, int64_t K);
+// xcopy: w4a16_xcopy_bytes of device memory for that copy, or null (the prefill stages X itself)
 hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, float* Y, int64_t ldy,
-                        hipStream_t st);
+                        uint16_t* xcopy, hipStream_t st);
 
 // ---- clipping search --------------------------------------------------------------------
 constexpr int kClipBM = 512;  // tokens per product tile

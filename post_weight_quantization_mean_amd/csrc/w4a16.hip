@@ -623,6 +623,11 @@ __device__ __forceinline__ uint32_t bf16x2_of(float a, float b) {
 // pair rows by (row >> 1) & 7, W rows by (row >> 2) & 3) so that the 32-row fragment reads are
 // free of bank conflicts.  Rows past M or N read as zero through the buffer resources (a zero
 // scale decodes to zero weights) and their outputs are not stored.
+// XF: X is read instead from a copy in matrix-core operand order (xfrag_kernel of the search:
+// the 16 bytes that lane l of an A operand takes for rows 32 rb.. and channels 16 kb.. are
+// contiguous, 1 KiB per fragment), each A fragment with one load straight into registers, right
+// after the last product of chunk c that reads its registers for chunk c+1; X then needs no LDS
+// and no copies, as in the persistent search kernel.
 constexpr int QXROW = 128;            // bytes of an X pair row (two chunks)
 constexpr int QXPSTAGE = PBM * QXROW;  // 64 KiB
 constexpr int QEROW = PKC * 2;        // bytes of a decoded W row of one chunk
@@ -642,14 +647,18 @@ struct RowDq {
   float d, nzd;  // Delta and -z Delta of one row's group
 };
 
+// X: row-major X [M, ldx] (XF false) or the operand-order copy (XF true, ldx ignored, rows
+// padded to a multiple of 32 with zeros).
+template <bool XF>
 __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t ldx, int64_t K, const int32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int64_t N,
     float* __restrict__ Y, int64_t ldy, int64_t ntiles, int64_t tiles, int64_t per_xcd) {
-  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[QXPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[QXPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[QXPSTAGE / 2];
-  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[QXPSTAGE / 2];
+  constexpr int XST = XF ? 16 : QXPSTAGE / 2;  // the X stages are unused with the copy
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0lo[XST];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0hi[XST];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1lo[XST];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1hi[XST];
   __shared__ __attribute__((aligned(1024))) uint8_t es[QNES * QESTAGE];
   // XCD x (= block % 8) takes the tiles x per_xcd .. (x + 1) per_xcd - 1 in order (token-tile
   // major), so its resident blocks share token tiles in its L2
@@ -666,7 +675,11 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                              (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t xrsrc = rsrc(X + m0 * ldx, (M - m0) * ldx * 2);
+  // the copy: rows m0.. are 64 K bytes per block of 32 rows; blocks past round_up(M, 32) read as
+  // zero (512 rows of the copy span less than 2^31 bytes: host-checked for X)
+  const int64_t Mp = (M + 31) / 32 * 32;
+  const __amdgpu_buffer_rsrc_t xrsrc =
+      XF ? rsrc(X + m0 * K, (Mp - m0) * K * 2) : rsrc(X + m0 * ldx, (M - m0) * ldx * 2);
   const __amdgpu_buffer_rsrc_t crsrc = rsrc(qweight + n0 * words, (N - n0) * words * 4);
   const __amdgpu_buffer_rsrc_t srsrc = rsrc(scales + n0 * G, (N - n0) * G * 2);
   const __amdgpu_buffer_rsrc_t zrsrc = rsrc(zeros + n0 * G, (N - n0) * G * 2);
@@ -684,6 +697,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (AWQ_LDS void*)(xh + xwave + (i & 7) * 1024), 16,
                                              (int)xoff[i & 1], (int)((uint32_t)(i >> 1) * xrow16 + (uint32_t)p * QXROW),
                                              0, 0);
+  };
+  // A fragment (row block r of this wave's 128 rows, chunk ch, K-half h) of the copy
+  const uint32_t avoff = (uint32_t)(lane * 16) + (uint32_t)(wave * 4) * (uint32_t)(K * 64);
+  auto load_a = [&](int ch, int h, int r) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                          xrsrc, (int)avoff, (int)(r * K * 64 + (2 * ch + h) * 1024), 0));
   };
   // decode: rows r0, r1 of the W tile, code word q4 of each chunk (channels 8 q4 .. 8 q4 + 7)
   const int q4 = lane & 3;
@@ -754,16 +773,24 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
   CodeSet S0, S1, S2, S3;  // code words of chunk c live in set c % 4
   ScaleZero PC, PN;        // scales and zeros of the group being decoded, of the next group
   RowDq q0, q1;            // row_setup of PC (rows r0, r1)
-  // Prologue: group 0's scales and zeros, codes of chunks 0-3, the X pair of chunks 0 and 1;
-  // then chunks 0 and 1 are decoded.
+  // Prologue: group 0's scales and zeros, codes of chunks 0-3, the X pair of chunks 0 and 1 (XF:
+  // chunk 0's A fragments); then chunks 0 and 1 are decoded.
+  bf16x8 a0[4], a1[4], b0[4];
   load_sz(PC, 0);
   load_c(S0, 0, 0, 0);
   load_c(S1, 0, 0, 1);
   load_c(S0, 1, 0, 0);
   load_c(S1, 1, 0, 1);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XF) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, 0);
+    for (int r = 0; r < 4; ++r) a0[r] = load_a(0, 0, r);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a1[r] = load_a(0, 1, r);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dma_x_one(i < 8 ? xp0lo : xp0hi, i, 0);
+  }
   __builtin_amdgcn_sched_barrier(0);
   load_c(S2, 0, 0, 2);
   load_c(S3, 0, 0, 3);
@@ -776,14 +803,15 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
   q1 = row_setup(PC.d1, PC.z1);
   decode_all(S0, q0, q1, es + 0 * QESTAGE);
   decode_all(S1, q0, q1, es + 1 * QESTAGE);
-  bf16x8 a0[4], b0[4];
   {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!XF) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) a0[t] = frag(xp0lo + xwave + t * 32 * QXROW, xfoff(0, 0));
+      for (int t = 0; t < 2; ++t) a0[t] = frag(xp0lo + xwave + t * 32 * QXROW, xfoff(0, 0));
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) b0[t] = frag(es + t * 32 * QEROW, efoff0);
     // use the code words of chunks 2 and 3 here, so that their loads are not sunk to the loop
@@ -810,6 +838,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
   //   * group 24 of an odd step: chunk c+1's rows 0-63 (copied by step c-1) landed, with this
   //     step's 8 copies after them; of an even step: nothing is awaited (those rows came from
   //     step c-2), the count is this step's loads before group 24.
+  // XF: no copies and no explicit waits; the A fragments of chunk c+1 are loaded in groups 4, 8,
+  // 12, 16 (K-half 0) and 20, 24, 28, 31 (K-half 1), and the compiler's counters wait for them
+  // and for the code words, scales and zeros (all loaded into registers).
   auto step = [&](int c8, auto jc, const uint8_t* xclo, const uint8_t* xchi, const uint8_t* xnlo, uint8_t* xdlo,
                   uint8_t* xdhi, const CodeSet& Q, CodeSet& F4, CodeSet& F5, int& eo0, int& eo1, int& eo2) {
     constexpr int j = decltype(jc)::value;
@@ -831,10 +862,11 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
       q0 = row_setup(PC.d0, PC.z0);
       q1 = row_setup(PC.d1, PC.z1);
     }
-    bf16x8 a1[4], b1[4];
+    bf16x8 b1[4];
     float e[16];
+    const int ca = c8 + j + 1;  // XF: the chunk whose A fragments this step loads
     __builtin_amdgcn_sched_barrier(0);
-    vm_wait(std::integral_constant<int, even ? 0 : 12>{});
+    if constexpr (!XF) vm_wait(std::integral_constant<int, even ? 0 : 12>{});
 #pragma unroll
     for (int g = 0; g < 32; ++g) {
       const int r = (g >> 2) & 3, cc = g & 3;
@@ -842,12 +874,20 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
         acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[r], b0[cc], acc[r][cc], 0, 0, 0);
       else
         acc[r][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[r], b1[cc], acc[r][cc], 0, 0, 0);
-      if (g < 2) a0[2 + g] = frag(xa(2 + g), xo0);
-      if (g < 8) {
-        if (g & 1)
-          b1[g >> 1] = frag(ec + (g >> 1) * 32 * QEROW, efoff1);
-        else
-          a1[g >> 1] = frag(xa(g >> 1), xo1);
+      if constexpr (XF) {
+        // past the last chunk these read other rows of the tile or zeros (unused)
+        if (g >= 4 && g <= 16 && (g & 3) == 0) a0[(g >> 2) - 1] = load_a(ca, 0, (g >> 2) - 1);
+        if (g >= 20 && g <= 28 && (g & 3) == 0) a1[(g >> 2) - 5] = load_a(ca, 1, (g >> 2) - 5);
+        if (g == 31) a1[3] = load_a(ca, 1, 3);
+        if (g < 8 && (g & 1)) b1[g >> 1] = frag(ec + (g >> 1) * 32 * QEROW, efoff1);
+      } else {
+        if (g < 2) a0[2 + g] = frag(xa(2 + g), xo0);
+        if (g < 8) {
+          if (g & 1)
+            b1[g >> 1] = frag(ec + (g >> 1) * 32 * QEROW, efoff1);
+          else
+            a1[g >> 1] = frag(xa(g >> 1), xo1);
+        }
       }
       // weight el in group 3 + 3 (el / 2) + el % 2: groups 3-13 for row r0, 15-25 for r1
       const int el = g >= 3 && g <= 25 && (g - 3) % 3 != 2 ? 2 * ((g - 3) / 3) + (g - 3) % 3 : -1;
@@ -861,8 +901,10 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
       // flight
       if (g == 15) __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x1 << 8) | (0x3 << 14));
       if (g >= 16 && g < 24 && (g & 1)) b0[(g - 16) >> 1] = frag(en + ((g - 16) >> 1) * 32 * QEROW, efoff0);
-      if (g == 24) vm_wait(std::integral_constant<int, even ? (k == 0 ? 14 : 10) : 8>{});
-      if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * QXROW, xn0);
+      if constexpr (!XF) {
+        if (g == 24) vm_wait(std::integral_constant<int, even ? (k == 0 ? 14 : 10) : 8>{});
+        if (g == 24 || g == 25) a0[g - 24] = frag(xnw + (g - 24) * 32 * QXROW, xn0);
+      }
       if (even) {
         if (g == 0) load_c(F4, 0, cb, j + 4);
         if (g == 1) load_c(F5, 0, cb, j + 5);
@@ -876,9 +918,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
           PN.z0 = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, (int)soff0, gn * 2, 0);
           PN.z1 = __builtin_amdgcn_raw_buffer_load_b16(zrsrc, (int)soff1, gn * 2, 0);
         }
-        if (g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(xdlo, (g - 6) / 3, pd);
+        if (!XF && g >= 6 && g <= 27 && (g - 6) % 3 == 0) dma_x_one(xdlo, (g - 6) / 3, pd);
       } else {
-        if (g <= 14 && (g & 1) == 0) dma_x_one(xdhi, 8 + g / 2, pd);
+        if (!XF && g <= 14 && (g & 1) == 0) dma_x_one(xdhi, 8 + g / 2, pd);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -921,7 +963,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
     step(c, I2{}, xp1lo, xp1hi, xp1lo, xp0lo, xp0hi, S0, S2, S3, eo0, eo1, eo2);
     step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, eo0, eo1, eo2);
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no copy outlives the block
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no copy or load outlives the block
   // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -987,14 +1029,26 @@ int64_t w4a16_mfma_kc(int64_t M, int64_t K) {
   return kc;
 }
 
+size_t w4a16_xcopy_bytes(bool xf32, int64_t M, int64_t K) {
+  if (xf32 || M <= kW4a16GemvMax || K % 64 != 0) return 0;
+  return (size_t)((M + 31) / 32 * 32) * (size_t)K * 2;
+}
+
 hipError_t launch_w4a16(const void* X, bool xf32, int64_t M, int64_t K, int64_t ldx, const int32_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, float* Y, int64_t ldy,
-                        hipStream_t st) {
+                        uint16_t* xcopy, hipStream_t st) {
   if (!xf32 && M > kW4a16GemvMax) {
     const int64_t mtiles = (M + PBM - 1) / PBM, ntiles = (N + PBN - 1) / PBN;
     const int64_t tiles = mtiles * ntiles, per_xcd = (tiles + 7) / 8;
-    w4a16_gemm_pipe_kernel<<<(unsigned)(8 * per_xcd), 256, 0, st>>>(
-        static_cast<const uint16_t*>(X), M, ldx, K, qweight, scales, zeros, N, Y, ldy, ntiles, tiles, per_xcd);
+    if (xcopy != nullptr) {
+      hipError_t e = launch_xfrag(static_cast<const uint16_t*>(X), M, K, ldx, xcopy, st);
+      if (e != hipSuccess) return e;
+      w4a16_gemm_pipe_kernel<true><<<(unsigned)(8 * per_xcd), 256, 0, st>>>(
+          xcopy, M, K, K, qweight, scales, zeros, N, Y, ldy, ntiles, tiles, per_xcd);
+    } else {
+      w4a16_gemm_pipe_kernel<false><<<(unsigned)(8 * per_xcd), 256, 0, st>>>(
+          static_cast<const uint16_t*>(X), M, ldx, K, qweight, scales, zeros, N, Y, ldy, ntiles, tiles, per_xcd);
+    }
     return hipGetLastError();
   }
   // decode path, up to 8 tokens per launch (fp32 X always takes it).  bf16 X with two or more

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                           "awq_search_multi_workspace_bytes", "awq_search_multi",
                           "awq_search_gram_workspace_bytes", "awq_search_gram",
                           "awq_pack_clipped", "awq_clip_workspace_bytes", "awq_clip", "awq_fold_rows",
-                          "awq_scale_cols", "awq_scaled_act", "awq_w4a16", "awq_search_static"}
+                          "awq_scale_cols", "awq_scaled_act", "awq_w4a16", "awq_search_static",
+                          "awq_w4a16_workspace_bytes", "awq_w4a16_ws"}
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.awq_abi_version() == 7
+    assert L.awq_abi_version() == 8
     for st in range(7):
         assert L.awq_status_string(st)
     assert L.awq_status_string(99) == b"unknown status"
@@ -319,6 +320,14 @@ def test_w4a16_argument_errors(L, kw, status):
     a.update(kw)
     assert L.awq_w4a16(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["q"], a["sc"], a["z"], a["N"], a["group"],
                        a["Y"], a["ldy"], None) == status
+    # the workspace form checks the same arguments first (prefill-sized M: it would use the copy)
+    a["M"] = 64 if a["M"] == 4 else a["M"]
+    assert L.awq_w4a16_ws(a["X"], a["xt"], a["M"], a["K"], a["ldx"], a["q"], a["sc"], a["z"], a["N"],
+                          a["group"], a["Y"], a["ldy"], P, 1 << 30, None) == status
+
+
+def test_w4a16_ws_rejects_a_misaligned_workspace(L):
+    assert L.awq_w4a16_ws(P, BF16, 64, 256, 256, P, P, P, 128, 128, P, 128, P + 8, 1 << 20, None) == INVALID
 
 
 @pytest.mark.parametrize("name,skipped", [
@@ -334,3 +343,13 @@ def test_clip_skips_query_and_key_modules(name, skipped):
     ("AWQ：为什么 4-bit 权重量化要先观察 Activation", §5); every other projection is clipped."""
     from post_weight_quantization_mean_amd import awq
     assert awq.clip_skipped(name) is skipped
+
+
+@pytest.mark.parametrize("M,K,dt,want", [
+    (4096, 4096, BF16, 2 * 4096 * 4096), (1000, 4096, BF16, 2 * 1024 * 4096), (9, 128, BF16, 2 * 32 * 128),
+    (8, 4096, BF16, 0), (1, 4096, BF16, 0), (4096, 4096, 0, 0), (0, 4096, BF16, 0), (64, 100, BF16, 0),
+    (64, 4096, 7, 0)])
+def test_w4a16_workspace_bytes(L, M, K, dt, want):
+    """The prefill's copy of X: bf16 X with more than 8 tokens, 2 round_up(M, 32) K bytes; no
+    workspace for the decode, fp32 X or invalid sizes."""
+    assert L.awq_w4a16_workspace_bytes(M, K, dt) == want

@@ -248,3 +248,27 @@ def test_prefill_unaligned_scales_odd_groups(awq):
     X = torch.from_numpy(np.random.default_rng(41).standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
     Y = awq.w4a16(X.to(DEV), q, sc, zz).cpu().numpy().astype(np.float64)
     check(Y, X.float().numpy().astype(np.float64), art, prefill=True, biased=False)
+
+
+@pytest.mark.parametrize("M,K,N,stride", [(9, 512, 128, 0), (600, 4096, 200, 0), (1000, 1152, 130, 0),
+                                          (4096, 4096, 1024, 0), (700, 1024, 256, 72)])
+def test_prefill_copy_of_x_matches_staged(awq, M, K, N, stride):
+    """The prefill reading X from its copy in matrix-core operand order (the default, with a
+    workspace) against the same kernel staging X through LDS (no workspace): the same products
+    in the same order, so Y must agree bit for bit, on ragged M (rows past M zero in the copy),
+    K / 128 odd, ragged N and X with row stride K + 72; and a reused, larger workspace gives
+    the same Y again."""
+    banner(f"w4a16 prefill copy vs staged M={M} K={K} N={N} stride+{stride}")
+    art = artefact(N, K, 13)
+    q = torch.from_numpy(art["qweight"]).to(DEV)
+    sc = torch.from_numpy(art["scales"].view(np.float16)).to(DEV)
+    zz = torch.from_numpy(art["zeros"].view(np.float16)).to(DEV)
+    full = torch.from_numpy(np.random.default_rng(14).standard_normal((M, K + stride)).astype(np.float32))
+    Xd = full.to(torch.bfloat16).to(DEV)[:, :K]
+    need = awq.w4a16_workspace_bytes(M, K)
+    assert need == 2 * (-(-M // 32) * 32) * K
+    Y_copy = awq.w4a16(Xd, q, sc, zz)
+    Y_staged = awq.w4a16(Xd, q, sc, zz, staged=True)
+    assert torch.equal(Y_copy, Y_staged)
+    ws = torch.full((need + 4096,), 0x7f, dtype=torch.uint8, device=DEV)  # stale bytes in the workspace
+    assert torch.equal(awq.w4a16(Xd, q, sc, zz, workspace=ws), Y_staged)
