@@ -756,6 +756,9 @@ struct TileRes {
   int64_t slot;                        // al * tiles + tile
 };
 
+// MULTI: the tiles come from several weights (the segment table is scanned per tile); otherwise
+// every tile is one of segs' first weight, whose fields alone are read.
+template <bool MULTI>
 __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
     const uint16_t* __restrict__ Xf, int64_t Mp, const WSegs segs, int64_t K,
     const float2* __restrict__ sr_tab, const float2* __restrict__ params, int n_grid,
@@ -790,7 +793,7 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
     const int al = (int)((uint32_t)L - tile * ng);
     const uint32_t mt = tile / ntc, nt = tile - mt * ntc;
     const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
-    const WSel sel = select_wseg(segs, nt);
+    const WSel sel = MULTI ? select_wseg(segs, nt) : WSel{segs.w[0], segs.ldw[0], segs.n[0], (int64_t)nt * BN};
     const uint16_t* W = static_cast<const uint16_t*>(sel.w);
     const int64_t N = sel.n, ldw = sel.ldw, n0w = sel.n0;
     // row blocks past Mp (a tile's rows past M) read as zero; 512 rows of Xf span less than
@@ -1156,8 +1159,12 @@ hipError_t launch_search_fused(const void* X, const uint16_t* Xf, bool xf32, int
   if (Xf != nullptr) {
     const int64_t pb = persistent_blocks(xf32, wf32, K, plan, n_grid);
     if (pb <= 0) return hipErrorInvalidValue;  // the caller checks search_persistent first
-    search_persistent_kernel<<<(unsigned)pb, THREADS, 0, st>>>(Xf, (M + 31) / 32 * 32, W, K, sr_tab, params,
-                                                               n_grid, plan.nt, plan.tiles, per_xcd, partial);
+    if (W.count == 1)
+      search_persistent_kernel<false><<<(unsigned)pb, THREADS, 0, st>>>(
+          Xf, (M + 31) / 32 * 32, W, K, sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
+    else
+      search_persistent_kernel<true><<<(unsigned)pb, THREADS, 0, st>>>(
+          Xf, (M + 31) / 32 * 32, W, K, sr_tab, params, n_grid, plan.nt, plan.tiles, per_xcd, partial);
     return hipGetLastError();
   }
   if (!xf32 && !wf32) {
