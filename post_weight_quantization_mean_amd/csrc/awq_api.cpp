@@ -295,13 +295,14 @@ int search_impl(const void* X, int x_dtype, int64_t M, int64_t K, int64_t ldx, c
   uint16_t* Tp = gram ? reinterpret_cast<uint16_t*>(base + gs_off) : nullptr;  // [K, 2K] bf16
   float* gpart = gram ? reinterpret_cast<float*>(base + gp_off) : nullptr;
 
-  hipError_t e = awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
+  // the copy of X shares the scale table's launch (both only read X and a)
+  hipError_t e = persistent ? awq::launch_scale_table_xfrag(a, K, n_grid, s_tab, rs_tab, sr_tab, flags,
+                                                             static_cast<const uint16_t*>(X), M, ldx, Xf, s)
+                            : awq::launch_scale_table(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, s);
   if (e == hipSuccess && gram) e = awq::launch_gram(static_cast<const uint16_t*>(X), M, K, ldx, Tp, gpart, s);
   for (int i = 0; i < n_weights && e == hipSuccess; ++i)
     e = awq::launch_group_range(Ws[i], wf32, Ns[i], K, ldws[i], s_tab, n_grid, params, segs.tile0[i] * 128,
                                 NP, flags, s);
-  if (e == hipSuccess && persistent)
-    e = awq::launch_xfrag(static_cast<const uint16_t*>(X), M, K, ldx, Xf, s);
   if (e == hipSuccess && fused_begin != nullptr)
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(fused_begin), s);
   if (e == hipSuccess && gram)

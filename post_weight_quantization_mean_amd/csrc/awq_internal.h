@@ -135,6 +135,28 @@ hipError_t launch_group_range(const void* W, bool wf32, int64_t N, int64_t K, in
 inline bool persistent_k(int64_t K) { return K % 256 == 0 && K >= 512; }
 bool search_persistent(bool xf32, bool wf32, int64_t K, const SearchPlan& plan, int n_grid);
 hipError_t launch_xfrag(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, uint16_t* Xf, hipStream_t st);
+// One block (256 threads) of that copy: rows 32 rb .. + 31 and channels 64 cb .. + 63 of X (four
+// fragments, 4 KiB), with rb, cb from block index b; thread t reads 16 bytes (t % 8) of row
+// 32 rb + t / 8, so eight lanes read one 128-byte run of a row.  The 16-byte piece of row
+// 32 rb + l % 32, channels 16 kb + 8 (l / 32) .. + 7 goes to byte ((rb K/16 + kb) 64 + l) 16 of
+// Xf; rows M .. Mp - 1 are zero.
+__device__ __forceinline__ void xfrag_block(const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
+                                            uint16_t* __restrict__ Xf, int64_t b, int t) {
+  const int64_t kc = K / 64;
+  const int64_t rb = b / kc, cb = b - rb * kc;
+  const int rl = t >> 3, piece = t & 7;
+  const int64_t row = rb * 32 + rl;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < M) v = *reinterpret_cast<const uint4*>(X + row * ldx + cb * 64 + piece * 8);
+  const int64_t frag_index = rb * (K / 16) + cb * 4 + (piece >> 1);
+  const int l = rl + 32 * (piece & 1);
+  *reinterpret_cast<uint4*>(Xf + (frag_index * 64 + l) * 8) = v;
+}
+// The scale table and that copy in one launch (they are independent): the scale table's few,
+// latency-bound blocks first, then the copy's blocks, which run beside them.
+hipError_t launch_scale_table_xfrag(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
+                                    float2* sr_tab, uint32_t* flags, const uint16_t* X, int64_t M,
+                                    int64_t ldx, uint16_t* Xf, hipStream_t st);
 // Xf: the fragment-ordered copy of X when search_persistent(...) holds (the persistent kernel
 // runs), else null (the pipelined kernel for bf16 operands, the plain fused kernel otherwise)
 hipError_t launch_search_fused(const void* X, const uint16_t* Xf, bool xf32, int64_t M, int64_t ldx,

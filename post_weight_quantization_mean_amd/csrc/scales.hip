@@ -20,15 +20,13 @@ constexpr int kScaleThreads = 256;
 constexpr int kScalePerThread = 4;
 constexpr int kScaleCols = kScaleThreads * kScalePerThread;
 
-__global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float* __restrict__ a,
-                                                                   int64_t K, int n_grid,
-                                                                   float* __restrict__ s_tab,
-                                                                   float* __restrict__ rs_tab,
-                                                                   float2* __restrict__ sr_tab,
-                                                                   uint32_t* __restrict__ flags) {
+// column block bx of candidate i
+__device__ __forceinline__ void scale_table_block(const float* __restrict__ a, int64_t K, int n_grid,
+                                                  float* __restrict__ s_tab, float* __restrict__ rs_tab,
+                                                  float2* __restrict__ sr_tab, uint32_t* __restrict__ flags,
+                                                  int bx, int i) {
   __shared__ double smax[kScaleThreads / 64];
   __shared__ double smin[kScaleThreads / 64];
-  const int i = blockIdx.y;
   const double alpha = (double)i / (double)n_grid;
   double lmax = 0.0, lmin = INFINITY;
   bool bad = false;  // a_j negative, NaN or infinite
@@ -57,7 +55,7 @@ __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float*
   bool bad_s = false;
 #pragma unroll
   for (int t = 0; t < kScalePerThread; ++t) {
-    const int64_t j = (int64_t)blockIdx.x * kScaleCols + t * kScaleThreads + threadIdx.x;
+    const int64_t j = (int64_t)bx * kScaleCols + t * kScaleThreads + threadIdx.x;
     if (j < K) {
       const double r = fmax(pow((double)a[j], alpha), 1e-4);
       const float sv = (float)(r / norm);
@@ -69,7 +67,29 @@ __global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float*
     }
   }
   // every block sees all of a; the ones of column block 0 report a bad statistic
-  if (bad_s || (bad && blockIdx.x == 0)) atomicOr(flags, kFlagScaleRange);
+  if (bad_s || (bad && bx == 0)) atomicOr(flags, kFlagScaleRange);
+}
+
+__global__ __launch_bounds__(kScaleThreads) void scale_table_kernel(const float* __restrict__ a, int64_t K,
+                                                                   int n_grid, float* __restrict__ s_tab,
+                                                                   float* __restrict__ rs_tab,
+                                                                   float2* __restrict__ sr_tab,
+                                                                   uint32_t* __restrict__ flags) {
+  scale_table_block(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, blockIdx.x, blockIdx.y);
+}
+
+// blocks 0 .. n_scale - 1: the scale table (column block b % cols of candidate b / cols); the
+// rest: the copy of X in operand order (xfrag_block)
+__global__ __launch_bounds__(kScaleThreads) void scale_table_xfrag_kernel(
+    const float* __restrict__ a, int64_t K, int n_grid, float* __restrict__ s_tab, float* __restrict__ rs_tab,
+    float2* __restrict__ sr_tab, uint32_t* __restrict__ flags, int cols, const uint16_t* __restrict__ X,
+    int64_t M, int64_t ldx, uint16_t* __restrict__ Xf) {
+  const int64_t n_scale = (int64_t)cols * n_grid;
+  const int64_t b = blockIdx.x;
+  if (b < n_scale)
+    scale_table_block(a, K, n_grid, s_tab, rs_tab, sr_tab, flags, (int)(b % cols), (int)(b / cols));
+  else
+    xfrag_block(X, M, K, ldx, Xf, b - n_scale, threadIdx.x);
 }
 
 // ---- group ranges: Delta and z of every (candidate, output channel, group) ---------------
@@ -233,6 +253,18 @@ hipError_t launch_scale_table(const float* a, int64_t K, int n_grid, float* s_ta
                               float2* sr_tab, uint32_t* flags, hipStream_t st) {
   const dim3 grid((unsigned)((K + kScaleCols - 1) / kScaleCols), (unsigned)n_grid);
   scale_table_kernel<<<grid, kScaleThreads, 0, st>>>(a, K, n_grid, s_tab, rs_tab, sr_tab, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_table_xfrag(const float* a, int64_t K, int n_grid, float* s_tab, float* rs_tab,
+                                    float2* sr_tab, uint32_t* flags, const uint16_t* X, int64_t M,
+                                    int64_t ldx, uint16_t* Xf, hipStream_t st) {
+  if (K % 64 != 0) return hipErrorInvalidValue;
+  const int64_t cols = (K + kScaleCols - 1) / kScaleCols;
+  const int64_t blocks = cols * n_grid + (M + 31) / 32 * (K / 64);
+  if (blocks <= 0 || blocks >= (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  scale_table_xfrag_kernel<<<(unsigned)blocks, kScaleThreads, 0, st>>>(a, K, n_grid, s_tab, rs_tab, sr_tab, flags,
+                                                                      (int)cols, X, M, ldx, Xf);
   return hipGetLastError();
 }
 

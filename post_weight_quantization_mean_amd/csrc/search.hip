@@ -1073,24 +1073,11 @@ __global__ __launch_bounds__(THREADS, 1) void search_persistent_kernel(
   __builtin_amdgcn_s_waitcnt(0);  // every load (the last ones read ahead past the end) has landed
 }
 
-// X bf16 [M, K] (row stride ldx) into the fragment order of the persistent kernel: the 16-byte
-// piece of row 32 rb + l % 32, channels 16 kb + 8 (l / 32) .. + 7 goes to byte
-// ((rb K/16 + kb) 64 + l) 16 of Xf; rows M .. Mp - 1 are zero.  Block b covers rows
-// 32 rb .. + 31 and channels 64 cb .. + 63 (four fragments, 4 KiB); thread t reads 16 bytes
-// (t % 8) of row 32 rb + t / 8, so eight lanes read one 128-byte run of a row.
+// X bf16 [M, K] (row stride ldx) into the fragment order of the persistent kernel, one
+// xfrag_block per block.
 __global__ __launch_bounds__(256) void xfrag_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                    int64_t ldx, uint16_t* __restrict__ Xf) {
-  const int64_t kc = K / 64;
-  const int64_t b = blockIdx.x;
-  const int64_t rb = b / kc, cb = b - rb * kc;
-  const int t = threadIdx.x;
-  const int rl = t >> 3, piece = t & 7;
-  const int64_t row = rb * 32 + rl;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (row < M) v = *reinterpret_cast<const uint4*>(X + row * ldx + cb * 64 + piece * 8);
-  const int64_t frag_index = rb * (K / 16) + cb * 4 + (piece >> 1);
-  const int l = rl + 32 * (piece & 1);
-  *reinterpret_cast<uint4*>(Xf + (frag_index * 64 + l) * 8) = v;
+  xfrag_block(X, M, K, ldx, Xf, blockIdx.x, threadIdx.x);
 }
 
 }  // namespace
