@@ -55,7 +55,7 @@ typedef enum {
   AWQ_ERR_SHAPE = 2,       /* K not a multiple of the group size, 64-bit size overflow,
                               awq_search / awq_clip: 512 rows of X or 128 rows of W span 2^31
                               bytes or more; awq_search: one candidate's group ranges
-                              (8 N K / 128 bytes) do */
+                              (8 N K / 128 bytes) do; awq_w4a16: 512 rows of X or of Y do */
   AWQ_ERR_UNSUPPORTED = 3, /* dtype other than F32/BF16, group other than 128 */
   AWQ_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than the size function says */
   AWQ_ERR_HIP = 5,         /* a HIP launch or runtime call failed */

@@ -492,8 +492,9 @@ AWQ_API int awq_w4a16_ws(const void* X, int x_dtype, int64_t M, int64_t K, int64
       (reinterpret_cast<uintptr_t>(zeros) & 1u) != 0 || (reinterpret_cast<uintptr_t>(Y) & 3u) != 0)
     return AWQ_ERR_INVALID_ARG;
   if (mul_ok(mul_ok(M, ldy), 4) < 0 || mul_ok(N, K) < 0) return AWQ_ERR_SHAPE;
-  // prefill tiles use 32-bit offsets within 512 rows of X (and of its copy, K <= ldx)
+  // prefill tiles use 32-bit offsets within 512 rows of X (and of its copy, K <= ldx) and of Y
   if (mul_ok(mul_ok(awq::kW4a16BM, ldx), dsize(x_dtype)) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
+  if (mul_ok(mul_ok(awq::kW4a16BM, ldy), 4) >= (int64_t)INT32_MAX) return AWQ_ERR_SHAPE;
   if (ws != nullptr && !aligned16(ws)) return AWQ_ERR_INVALID_ARG;
   // the copy of X when the workspace holds it; otherwise the prefill stages X itself
   const size_t xb = awq::w4a16_xcopy_bytes(x_dtype == AWQ_DTYPE_F32, M, K);

@@ -964,17 +964,40 @@ __global__ __launch_bounds__(256, 1) void w4a16_gemm_pipe_kernel(
     step(c, I3{}, xp1lo, xp1hi, xp0lo, xp0lo, xp0hi, S1, S2, S3, eo0, eo1, eo2);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no copy or load outlives the block
-  // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4
+  // 32x32 result layout: lane l holds column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4.
+  if (m0 + PBM <= M) {
+    // a whole token tile: stores through a buffer resource based at Y[m0, n0], with no branch
+    // per store: the lane's offset is a VGPR, each store's row a scalar (512 rows of Y span
+    // less than 2^31 bytes: host-checked), and columns past N are one lane mask per 32-column
+    // block.  Every row addressed here is below M.
+    const __amdgpu_buffer_rsrc_t yrsrc = rsrc(Y + m0 * ldy + n0, (PBM * ldy - n0) * 4);
+    const uint32_t ldy4 = (uint32_t)ldy * 4u;
+    const int yv = (int)((uint32_t)(wave * 128 + 4 * (lane / 32)) * ldy4 + (uint32_t)(lane % 32) * 4u);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+    for (int cc = 0; cc < 4; ++cc) {
+      if (n0 + cc * 32 + (lane % 32) < N) {
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t m = m0 + wave * 128 + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
-        const int64_t n = n0 + cc * 32 + (lane % 32);
-        if (m < M && n < N) Y[m * ldy + n] = acc[r][cc][i];
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t so = (uint32_t)(r * 32 + 8 * (i / 4) + (i % 4)) * ldy4 + (uint32_t)(cc * 128);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r][cc][i]), yrsrc, yv, (int)so, 0);
+          }
       }
+    }
+  } else {
+    // the last, partial token tile: each store checks its row and column
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t m = m0 + wave * 128 + r * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+          const int64_t n = n0 + cc * 32 + (lane % 32);
+          if (m < M && n < N) Y[m * ldy + n] = acc[r][cc][i];
+        }
+  }
 }
 
 }  // namespace

@@ -314,6 +314,7 @@ def test_scaled_act_argument_errors(L, kw, status):
     (dict(Y=None), INVALID), (dict(N=0), INVALID), (dict(ldy=127), INVALID), (dict(q=P + 4), INVALID),
     (dict(sc=P + 1), INVALID), (dict(Y=P + 2), INVALID), (dict(group=64), UNSUP), (dict(xt=4), UNSUP),
     (dict(K=200, ldx=200), SHAPE), (dict(ldx=1 << 21), SHAPE),
+    (dict(ldy=1 << 20), SHAPE),  # 512 rows of Y span 2^31 bytes (32-bit offsets in a prefill tile)
 ])
 def test_w4a16_argument_errors(L, kw, status):
     a = dict(X=P, xt=BF16, M=4, K=256, ldx=256, q=P, sc=P, z=P, N=128, group=128, Y=P, ldy=128)
