@@ -198,7 +198,8 @@ AWQ_API int awq_search_multi(const void* X, int x_dtype, int64_t M, int64_t K, i
  * with G formed once on the matrix cores (fp32 sums per 1024 tokens, then across blocks) and
  * kept as G_hi + G_lo, two bf16 matrices (16 significand bits of G) interleaved in one
  * [K, 2K] matrix.  Every candidate then multiplies both with E^T into the same outputs
- * (2 * 2 K^2 N flop instead of 2 M K N) and dots each output with E[n, k'].  For K > 512 the
+ * (2 * 2 K^2 N flop instead of 2 M K N) and dots each output with E[n, k'], both E rounded to
+ * bf16 as the direct form's product operand is.  For K > 512 the
  * matrix holds T = diag(G) + 2 triu(G, 1) instead (the same quadratic form, zero below the
  * diagonal), and each 512-row block of the product skips the columns left of its first row:
  * about 2 K (K + 512) N flop per candidate, less work than the direct form when

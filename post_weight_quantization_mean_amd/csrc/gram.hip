@@ -9,8 +9,9 @@
 // single bf16 G would lose the cancellation that the quadratic form depends on).  They are
 // interleaved in one [K x 2K] matrix: row k' holds, for every 32-column chunk c, chunk c of row
 // k' of G_hi and then of G_lo; Tp stores that matrix in matrix-core operand order (tp_at).
-// gram_search_kernel multiplies both with E^T into the same accumulators and dots each output
-// (k', n) with E[n, k'].
+// gram_search_kernel multiplies both with E~^T (E rounded to bf16, the direct form's operand)
+// into the same accumulators and dots each output (k', n) with E~[n, k'], read back from the E
+// stages of the block's first 16 chunks, which hold exactly its rows k'.
 //
 // Triangular form (K > 512).  G is symmetric, so e G e^T = sum_k G[k,k] e_k^2 +
 // 2 sum_{k < k'} G[k,k'] e_k e_k': the same quadratic form with T = diag(G) + 2 triu(G, 1) in
@@ -344,12 +345,17 @@ GramPlan gram_plan(int64_t M, int64_t K) {
 //   * the B fragments of the second K-half are read in groups 1-7 and the next chunk's first
 //     K-half in groups 33-39, after the last use of the current ones;
 //   * the quantization of chunk c+2 places element el in group 3 + 3 el, its two stores after
-//     elements 7 and 15.
+//     elements 7 and 15;
+//   * the E stage of chunk c0 + j is slot j for j < 16 (kept to the end), later chunks rotate
+//     through three more slots; the block's rows k' are its first 16 chunks, so the epilogue
+//     reads the E~ it dots the outputs with from the kept slots (one 8-byte LDS read per four
+//     outputs, against recomputing each e from W, s and the group's range).
 // Triangular form: the block's K loop starts at its first row, chunk m0 / 32 (a multiple of 16).
 constexpr int GS_BM = 512, GS_BN = 128, GS_KC = 32;
 constexpr int GS_PROW = GS_KC * 2;            // bytes of an E row (one chunk)
 constexpr int GS_ESTAGE = GS_BN * GS_PROW;    // 8 KiB
 constexpr int GS_NES = 3;
+constexpr int GS_KEEP = GS_BM / GS_KC;         // E stages kept for the epilogue: the block's first 16 chunks
 constexpr int GS_SRG = kGroup * 8;            // one group's (s, 1/s) pairs: 1 KiB
 #define AWQ_LDS_G __attribute__((address_space(3)))
 
@@ -377,7 +383,9 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
     const uint16_t* __restrict__ Tp, int64_t K, const WSegs segs, const float2* __restrict__ sr_tab,
     const float2* __restrict__ params, int n_grid, int64_t nt_count, int64_t tiles, bool tri,
     double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(1024))) uint8_t es[GS_NES * GS_ESTAGE];
+  // E stages: slot j < 16 holds chunk c0 + j for good (the epilogue reads them back), later
+  // chunks rotate through slots 16 .. 18; 152 KiB, with the scale tables the whole 160 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t es[(GS_KEEP + GS_NES) * GS_ESTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t srs0[4 * GS_SRG];
   __shared__ __attribute__((aligned(1024))) uint8_t srs1[4 * GS_SRG];
 
@@ -402,6 +410,11 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   const int nchunks = (int)(K / GS_KC);
   const int c0 = tri ? (int)(m0 / GS_KC) : 0;
   const int64_t ldx = 2 * K;
+  // the E stage of chunk q (see es)
+  auto eoff = [&](int q) {
+    const int j = q - c0;
+    return j < GS_KEEP ? j * GS_ESTAGE : (GS_KEEP + (j - GS_KEEP) % GS_NES) * GS_ESTAGE;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -553,17 +566,16 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   // the next group's ranges (group 4) and scale table DMA (group 5); every step 16 A fragments
   // in groups 4, 8, ..., 60 and 63.  The scale table DMA'd in a k = 0 step is read from the
   // k = 2 step on: 15 A loads of its own step and 16 of the next were issued after it.
-  auto step = [&](int c8, auto jc, const GsWSet& Q, GsWSet& F4, GsWSet& F5, const uint8_t* srq, uint8_t* srn,
-                  int& eo0, int& eo1, int& eo2) {
+  auto step = [&](int c8, auto jc, const GsWSet& Q, GsWSet& F4, GsWSet& F5, const uint8_t* srq, uint8_t* srn) {
     constexpr int j = decltype(jc)::value;
     constexpr int k = j & 3;
     constexpr bool even = (k & 1) == 0;
     const int c = c8 + j;
     const int cb = c8 * (GS_KC * 2);
     const int gn = (c8 >> 2) + (j >> 2) + 1;  // next group (k = 0 steps)
-    const uint8_t* ec = es + eo0;
-    const uint8_t* en = es + eo1;
-    uint8_t* eq = es + eo2;
+    const uint8_t* ec = es + eoff(c);
+    const uint8_t* en = es + eoff(c + 1);
+    uint8_t* eq = es + eoff(c + 2);
     const uint8_t* sa = sr_addr(srq, k + 2);
     if (k == 2) {  // chunks c+2 .. c+5 of this quad after the first two: next group
       PC = PN;
@@ -610,10 +622,6 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // E stores of chunk c+2, fragment reads
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int et = eo0;
-    eo0 = eo1;
-    eo1 = eo2;
-    eo2 = et;
   };
 
   // The body covers two groups (8 steps) so that each scale table has a static role.  nchunks -
@@ -626,77 +634,49 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   using I5 = std::integral_constant<int, 5>;
   using I6 = std::integral_constant<int, 6>;
   using I7 = std::integral_constant<int, 7>;
-  int eo0 = 0, eo1 = GS_ESTAGE, eo2 = 2 * GS_ESTAGE;
   int c = c0;
   for (; c + 8 <= nchunks; c += 8) {
-    step(c, I0{}, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I1{}, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I2{}, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I3{}, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I4{}, S2, S0, S1, srs1, srs0, eo0, eo1, eo2);
-    step(c, I5{}, S3, S0, S1, srs1, srs0, eo0, eo1, eo2);
-    step(c, I6{}, S0, S2, S3, srs0, srs0, eo0, eo1, eo2);
-    step(c, I7{}, S1, S2, S3, srs0, srs0, eo0, eo1, eo2);
+    step(c, I0{}, S2, S0, S1, srs0, srs1);
+    step(c, I1{}, S3, S0, S1, srs0, srs1);
+    step(c, I2{}, S0, S2, S3, srs1, srs1);
+    step(c, I3{}, S1, S2, S3, srs1, srs1);
+    step(c, I4{}, S2, S0, S1, srs1, srs0);
+    step(c, I5{}, S3, S0, S1, srs1, srs0);
+    step(c, I6{}, S0, S2, S3, srs0, srs0);
+    step(c, I7{}, S1, S2, S3, srs0, srs0);
   }
   if (c < nchunks) {  // K / 128 odd: one more group
-    step(c, I0{}, S2, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I1{}, S3, S0, S1, srs0, srs1, eo0, eo1, eo2);
-    step(c, I2{}, S0, S2, S3, srs1, srs1, eo0, eo1, eo2);
-    step(c, I3{}, S1, S2, S3, srs1, srs1, eo0, eo1, eo2);
+    step(c, I0{}, S2, S0, S1, srs0, srs1);
+    step(c, I1{}, S3, S0, S1, srs0, srs1);
+    step(c, I2{}, S0, S2, S3, srs1, srs1);
+    step(c, I3{}, S1, S2, S3, srs1, srs1);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt 0: no load (the last ones read past the end) outlives the block
 
-  // This wave's 128 rows are rows kb .. kb + 127 of T: one whole group gq of K (rows past K hold
-  // zeros and are skipped).  Lane l's outputs sit at k' = kb + 32 r + 8 (i / 4) + 4 (l / 32) + i % 4
-  // and n = n0 + 32 cc + l % 32, where it recomputes e = E[n, k'] exactly as the K loop formed it
-  // (before the bf16 rounding) and adds acc e.
+  // This wave's 128 rows are rows kb .. kb + 127 of T: chunks c0 + 4 wave .. + 3 of K, whose E
+  // stages are slots 4 wave .. + 3 (rows past K hold zeros and are skipped).  Lane l's outputs sit
+  // at k' = kb + 32 r + 8 (i / 4) + 4 (l / 32) + i % 4 and n = n0 + 32 cc + l % 32; the lane reads
+  // E~[n, k'] (E rounded to bf16, the operand the products used: rows past N hold zeros) four
+  // channels at a time from slot 4 wave + r, and adds acc E~.
   double ss = 0.0;
   const int64_t kb = m0 + 128 * wave;
   if (kb < K) {
-    const int gq = (int)(kb / kGroup);
-    GsRowQ rq[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int nl = 32 * cc + (lane & 31);
-      const float2 P = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                      prsrc, (int)(((int64_t)gq * NP + range_slot(n0 + nl)) * 8), 0, 0));
-      const bool live = n0w + nl < N;
-      rq[cc].delta = live ? P.x : 1.0f;  // rows past N: Delta 1, z 0, w 0 (read as zero): e = 0
-      const float z = live ? P.y : 0.0f;
-      rq[cc].inv = __builtin_amdgcn_rcpf(rq[cc].delta);
-      rq[cc].lo = -z;
-      rq[cc].hi = 15.0f - z;
-    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4 sv[4][2];  // (s, 1/s) of the four consecutive channels of each i / 4
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int kk = (int)kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          sv[i4][hh] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, kk * 8 + 16 * hh, 0, 0));
-      }
+      const uint8_t* slot = es + (4 * wave + r) * GS_ESTAGE;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const int nl = 32 * cc + (lane & 31);
         float t = 0.0f;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int kk = (int)kb + 32 * r + 8 * i4 + 4 * (lane >> 5);
-          const uint2 w4 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                         wrsrc, (int)(nl * ldw * 2 + kk * 2), 0, 0));
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t u = jj < 2 ? w4.x : w4.y;
-            const float w = (jj & 1) ? gs_hi(u) : gs_lo(u);
-            const float4& sp = sv[i4][jj >> 1];
-            const float s = (jj & 1) ? sp.z : sp.x, rs = (jj & 1) ? sp.w : sp.y;
-            const float v = w * s;
-            const float q = __builtin_amdgcn_fmed3f(rintf(v * rq[cc].inv), rq[cc].lo, rq[cc].hi);
-            const float e = fmaf(-(q * rq[cc].delta), rs, w);
-            t = fmaf(acc[r][cc][4 * i4 + jj], e, t);
-          }
+          // channels 8 i4 + 4 (l / 32) .. + 3 of row nl: piece i4, bytes 8 (l / 32) .. + 7
+          const uint2 e4 = *reinterpret_cast<const uint2*>(slot + nl * GS_PROW + ((i4 ^ gs_swz(nl)) * 16) +
+                                                           8 * (lane >> 5));
+          t = fmaf(acc[r][cc][4 * i4 + 0], gs_lo(e4.x), t);
+          t = fmaf(acc[r][cc][4 * i4 + 1], gs_hi(e4.x), t);
+          t = fmaf(acc[r][cc][4 * i4 + 2], gs_lo(e4.y), t);
+          t = fmaf(acc[r][cc][4 * i4 + 3], gs_hi(e4.y), t);
         }
         ss += (double)t;
       }
@@ -704,9 +684,9 @@ __global__ __launch_bounds__(256, 1) void gram_search_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  // every wave is past its last LDS access (the barrier ending the last step), so the first E
-  // stage can hold the four wave sums
-  double* red = reinterpret_cast<double*>(es);
+  // the rotating E stages are past their last access (the barrier ending the last step) and the
+  // epilogue reads only the kept ones, so the first rotating stage can hold the four wave sums
+  double* red = reinterpret_cast<double*>(es + GS_KEEP * GS_ESTAGE);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   if (tid == 0) partial[(int64_t)al * tiles + tile] = ((red[0] + red[1]) + red[2]) + red[3];

@@ -2,11 +2,12 @@
 Activation", §1, the exact output error through X^T X) against the oracle's exact losses.
 
 Tolerance, from the arithmetic.  The kernel forms Y' = G~ E~^T with E~ = E rounded to bf16
-and G~ = G_hi + G_lo, then sums Y'[k', n] e[n, k'] with the unrounded e (for K > 512, G~ is the
+and G~ = G_hi + G_lo, then sums Y'[k', n] E~[n, k'] with the same rounded E~, so that it
+evaluates the quadratic form of the operand the direct form multiplies (for K > 512, G~ is the
 triangular T = diag(G) + 2 triu(G, 1), whose quadratic form is G's; only the K <= 512 cases,
 where G~ is G itself, can fall under the small-layer bound below):
-  * bf16 E: sum_n e G (E~ - E)^T = sum_{m,n} y (X dE^T), at most 2^-8 sum |y| (|X| |E|^T): the
-    first-order term of the direct form with coefficient 1 instead of 2;
+  * bf16 E: E~ G E~^T - E G E^T = 2 sum_{m,n} y (X dE^T) + |X dE^T|^2, at most
+    2^-7 sum |y| (|X| |E|^T) + 2^-16 sum (|X| |E|^T)^2: the direct form's terms;
   * G: 2^-16 relative per entry (G_lo's rounding) plus fp32 sums over 1024-token blocks and
     across the M / 1024 blocks, each bounded by its count times 2^-24 of |X|^T |X|;
   * fp32 accumulation over the K products of the matrix cores and the epilogue's 16-term sums.
@@ -55,7 +56,7 @@ def gram_tolerance(X64, W32, s_table, ref_losses):
         E = W32.astype(np.float64) - o.effective_weight(q, z, d, s, 128)
         Y = X64 @ E.T
         A = absX @ np.abs(E).T
-        bound = (2.0 ** -8 * np.sum(np.abs(Y) * A) + cG * np.sum(A * A)) / (M * N)
+        bound = (2.0 ** -7 * np.sum(np.abs(Y) * A) + (2.0 ** -16 + cG) * np.sum(A * A)) / (M * N)
         tol[i] = max(1e-3 * ref_losses[i], bound + 1e-5 * ref_losses[i])
     return tol
 
